@@ -1,0 +1,123 @@
+"""Seeded cache images, raw token streams and queries for the workloads.
+
+Everything here is random data laid out in the cache's plane layout; no step
+of the method (pooling, quantization, scoring, attention) is performed.
+Cache images are random codes:
+  * nope: random e4m3fn bytes (NaN codes moved to +-448), per-64 fp32 scales
+    uniform in [2/448, 3/448], slot 7 of each scale row 0;
+  * rope: bf16 of N(0,1);
+  * indexer keys: random e2m1 nibbles with E8M0 block exponents 2^-3..2^0;
+  * ring: the last min(len, R) raw tokens (bf16 N(0,1) KV, N(0,1) gates and
+    indexer streams) at slot position % R.
+Needle blocks (retrieval stand-ins) get indexer codes equal to the sign
+pattern of sum_h w_h q_h at the largest e2m1 magnitude with block exponent
+2^1, and KV codes with the sign pattern of sum_h q_h at a large e4m3
+magnitude, so that they outrank random blocks for the query they target.
+Every tensor comes from its own stream (seed, name, row), so one row can be
+regenerated alone.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (abs_normal_f32, bf16_normal, distinct_choice, e2m1_code_image,
+               e4m3_code_image, e8m0_image, fp8_scale_image, normal_f32)
+
+KV, NOPE, ROPE, IDX = 512, 448, 64, 64
+
+
+def empty_layer(batch, ratio, window, ring, has_indexer, max_blocks):
+    B, MB, R = batch, max_blocks, ring
+    L = dict(batch=B, ratio=ratio, window=window, ring=R, has_indexer=int(has_indexer),
+             max_blocks=MB,
+             seq_len=np.zeros(B, np.int32),
+             nope=np.zeros((B, MB, NOPE), np.uint8),
+             rope=np.zeros((B, MB, ROPE), np.uint16),
+             kv_scale=np.zeros((B, MB, 8), np.float32),
+             idx_code=np.zeros((B, MB if has_indexer else 0, 32), np.uint8),
+             idx_scale=np.zeros((B, MB if has_indexer else 0, 2), np.uint8),
+             ring_kv=np.zeros((B, R, KV), np.uint16),
+             ring_gate=np.zeros((B, R, KV), np.float32),
+             ring_ikey=np.zeros((B, R if has_indexer else 0, IDX), np.float32),
+             ring_igate=np.zeros((B, R if has_indexer else 0, IDX), np.float32))
+    return L
+
+
+def pos_bias(seed, tag, ratio, has_indexer):
+    pb = normal_f32(seed, "pos_bias", (ratio, KV), tag)
+    ipb = normal_f32(seed, "ipos_bias", (ratio, IDX), tag) if has_indexer else None
+    return pb, ipb
+
+
+def fill_row_image(L, seed, tag, row, length):
+    """Random cache image for row `row` holding `length` tokens."""
+    m, R, MB = L["ratio"], L["ring"], L["max_blocks"]
+    nb = length // m
+    if nb > MB:
+        raise ValueError("cache capacity exceeded")
+    L["seq_len"][row] = length
+    if nb:
+        L["nope"][row, :nb] = e4m3_code_image(seed, "nope", nb * NOPE, tag, row).reshape(nb, NOPE)
+        L["rope"][row, :nb] = bf16_normal(seed, "rope", (nb, ROPE), tag, row)
+        sc = fp8_scale_image(seed, "kv_scale", nb * 7, tag, row).reshape(nb, 7)
+        L["kv_scale"][row, :nb, :7] = sc
+        L["kv_scale"][row, :nb, 7] = 0.0
+        if L["has_indexer"]:
+            L["idx_code"][row, :nb] = e2m1_code_image(seed, "idx_code", nb * 32, tag, row).reshape(nb, 32)
+            L["idx_scale"][row, :nb] = e8m0_image(seed, "idx_scale", nb * 2, tag, row).reshape(nb, 2)
+    nr = min(length, R)
+    if nr:
+        pos = np.arange(length - nr, length)
+        slots = pos % R
+        L["ring_kv"][row, slots] = bf16_normal(seed, "ring_kv", (nr, KV), tag, row)
+        L["ring_gate"][row, slots] = normal_f32(seed, "ring_gate", (nr, KV), tag, row)
+        if L["has_indexer"]:
+            L["ring_ikey"][row, slots] = normal_f32(seed, "ring_ikey", (nr, IDX), tag, row)
+            L["ring_igate"][row, slots] = normal_f32(seed, "ring_igate", (nr, IDX), tag, row)
+
+
+def make_layer(seed, tag, batch, ratio, window, ring, has_indexer, max_blocks, lengths):
+    L = empty_layer(batch, ratio, window, ring, has_indexer, max_blocks)
+    L["pos_bias"], L["ipos_bias"] = pos_bias(seed, tag, ratio, has_indexer)
+    for b in range(batch):
+        fill_row_image(L, seed, tag, b, int(lengths[b]))
+    return L
+
+
+def tokens(seed, tag, batch, n, has_indexer, step=0):
+    """Raw tokens for one append of n tokens per row."""
+    t = dict(kv=bf16_normal(seed, "tok_kv", (batch, n, KV), tag, step),
+             gate=normal_f32(seed, "tok_gate", (batch, n, KV), tag, step))
+    if has_indexer:
+        t["ikey"] = normal_f32(seed, "tok_ikey", (batch, n, IDX), tag, step)
+        t["igate"] = normal_f32(seed, "tok_igate", (batch, n, IDX), tag, step)
+    return t
+
+
+def queries(seed, tag, batch, n_q, H, H_I=0, step=0):
+    q = dict(q=bf16_normal(seed, "q", (batch, n_q, H, KV), tag, step))
+    if H_I:
+        q["iq"] = normal_f32(seed, "iq", (batch, n_q, H_I, IDX), tag, step)
+        q["iw"] = abs_normal_f32(seed, "iw", (batch, n_q, H_I), tag, step)
+    return q
+
+
+def plant_needles(L, seed, tag, row, count, iq_row, iw_row, q_row):
+    """Plant `count` needle blocks in `row`, targeted at one query (its fp32
+    indexer query [H_I][64], weights [H_I] and bf16-bit attention query
+    [H][512]).  Returns the needle block indices.  Needles lie outside the
+    query's window: blocks 0 .. n_vis - 1 - ceil(W/m)."""
+    m, W = L["ratio"], L["window"]
+    n_vis = int(L["seq_len"][row]) // m
+    hi = n_vis - 1 - (W + m - 1) // m
+    blocks = distinct_choice(seed, "needles", count, 0, hi, tag, row)
+    u = (iw_row[:, None].astype(np.float64) * iq_row.astype(np.float64)).sum(0)
+    nib = np.where(u < 0, 0xF, 0x7).astype(np.uint8)          # +-6
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    qsum = (q_row.astype(np.uint32) << 16).view(np.float32).astype(np.float64).sum(0)
+    kv_code = np.where(qsum[:NOPE] < 0, 0xEE, 0x6E).astype(np.uint8)  # +-112
+    for b in blocks:
+        L["idx_code"][row, b] = packed
+        L["idx_scale"][row, b] = 128
+        L["nope"][row, b] = kv_code
+    return blocks
