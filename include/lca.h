@@ -1,0 +1,224 @@
+/*
+ * lca.h -- C ABI of the MI355X (gfx950) compressed long-context attention
+ * library (liblca.so).
+ *
+ * The library implements the decode/prefill hot path of interleaved
+ * compressed attention as described on these pages (cited by title and
+ * section):
+ *   [AGENT]  vibecoco.ai "DeepSeek V4 agent architecture" page, section
+ *            "混合注意力" (hybrid attention): KV compressed 4x along the
+ *            sequence by softmax-gated pooling with a learned position bias;
+ *            an FP4 lightning indexer (ReLU-scored multi-head dot products)
+ *            keeps the top-k compressed blocks; recent tokens stay raw in a
+ *            sliding-window branch; HCA compresses 128x and attends densely
+ *            to every compressed block; KV is stored in FP8 except the RoPE
+ *            dims (BF16); the indexer runs in FP4.
+ *   [REPORT] agents-report.net "DeepSeek-V4：交錯壓縮注意力與低位元 KV 儲存"
+ *            page, section "核心技術" (CSA: 4x compressor + lightning indexer
+ *            top-k; HCA: 128x, dense).
+ *   [ARCH]   pnsm.cn "DeepSeek V4 架构深度解析" page, section 2.1 (window KV
+ *            overwritten cyclically; the compressor updates the compressed
+ *            cache, the index keeps the top-k; one attention over both) and
+ *            section 2.2 (HCA, 128:1, layers alternate CSA and HCA).
+ *
+ * Conventions
+ *   - Every entry point returns LCA_OK (0) or a negative LCA_E* code.  On an
+ *     error nothing has been enqueued and lca_last_error() returns a message
+ *     (thread-local, valid until the next call on the same thread).
+ *   - Pointers inside lca_layer and all array arguments are device pointers
+ *     owned by the caller, 16-byte aligned, row-major.  The library never
+ *     allocates, frees or keeps them after the call returns.
+ *   - Work is enqueued on the hipStream_t argument and the call returns
+ *     without waiting.  Buffers must stay alive until the stream has executed
+ *     the work.  Device faults surface at the caller's next synchronisation.
+ *   - Calls on different layers may run concurrently.  Calls that touch the
+ *     same layer or the same workspace must be ordered by the caller (same
+ *     stream, or events).
+ *
+ * Fixed dimensions: a KV entry has 512 dims (448 FP8 + 64 BF16 RoPE); an
+ * indexer key has 64 dims.
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCA_ABI_VERSION 1
+
+enum {
+  LCA_OK = 0,
+  LCA_EINVAL = -1,        /* null/misaligned pointer, bad size or argument    */
+  LCA_EUNSUPPORTED = -2,  /* valid but outside the supported shape range      */
+  LCA_ECAPACITY = -3,     /* cache or ring too small for the request          */
+  LCA_EWORKSPACE = -4,    /* workspace missing or smaller than required       */
+  LCA_EHIP = -5           /* a HIP runtime call failed                        */
+};
+
+#define LCA_KV_DIM 512
+#define LCA_NOPE_DIM 448
+#define LCA_ROPE_DIM 64
+#define LCA_IDX_DIM 64
+#define LCA_SCALE_STRIDE 8
+
+/*
+ * One attention layer's cache.  Caller-filled; the library reads the sizes
+ * and pointers and updates len_min / len_max (host mirrors) in
+ * lca_compress_append.
+ *
+ * Planes (B = batch rows, MB = max_blocks, R = ring, m = ratio):
+ *   seq_len    int32   [B]            tokens appended so far, per row (device)
+ *   sync       uint32  [1]            zero when created; the library keeps it 0
+ *                                     between calls (a completion counter)
+ *   nope       uint8   [B][MB][448]   e4m3fn codes of entry dims 0..447
+ *   rope       uint16  [B][MB][64]    bf16 entry dims 448..511
+ *   kv_scale   float   [B][MB][8]     fp32 scale of each 64-dim FP8 group
+ *                                     (slot 7 unused, written 0)
+ *   idx_code   uint8   [B][MB][32]    e2m1 indexer key codes, element 2j in
+ *                                     the low nibble of byte j   (CSA only)
+ *   idx_scale  uint8   [B][MB][2]     E8M0 exponent of each 32-element half
+ *                                     (CSA only)
+ *   ring_kv    uint16  [B][R][512]    raw bf16 KV of the last R tokens at slot
+ *                                     position % R (window + pooling source)
+ *   ring_gate  float   [B][R][512]    their gate logits
+ *   ring_ikey  float   [B][R][64]     their indexer-key stream (CSA only)
+ *   ring_igate float   [B][R][64]     its gate logits (CSA only)
+ *   pos_bias   float   [m][512]       learned in-block position bias
+ *   ipos_bias  float   [m][64]        its indexer counterpart (CSA only)
+ * Compressed entry b of a row pools tokens b*m .. b*m+m-1.  A query at
+ * position p sees entries b < floor((p+1)/m) and the raw tokens
+ * max(0, p-W+1) .. p.  Rows may hold different lengths; every call appends
+ * the same number of tokens to every row.
+ */
+typedef struct lca_layer {
+  int32_t batch;        /* B >= 1                                              */
+  int32_t ratio;        /* m: power of two, 1..128                             */
+  int32_t window;       /* W >= 1                                              */
+  int32_t ring;         /* R >= W                                              */
+  int32_t has_indexer;  /* 1: CSA layer (indexer planes present); 0: HCA       */
+  int32_t reserved;     /* 0                                                   */
+  int64_t max_blocks;   /* MB >= 1                                             */
+  int64_t len_min;      /* host mirror: min over rows of seq_len               */
+  int64_t len_max;      /* host mirror: max over rows of seq_len               */
+  int32_t *seq_len;
+  uint32_t *sync;
+  uint8_t *nope;
+  uint16_t *rope;
+  float *kv_scale;
+  uint8_t *idx_code;
+  uint8_t *idx_scale;
+  uint16_t *ring_kv;
+  float *ring_gate;
+  float *ring_ikey;
+  float *ring_igate;
+  const float *pos_bias;
+  const float *ipos_bias;
+} lca_layer;
+
+/*
+ * lca_compress_append -- [AGENT] hybrid-attention section (softmax-gated
+ * pooling with a learned position bias, FP8 entries with BF16 RoPE dims, FP4
+ * indexer keys); [ARCH] 2.1 (the compressor updates the compressed cache; the
+ * window store overwrites cyclically).
+ *
+ * Appends n tokens to every row at positions seq_len .. seq_len+n-1, then
+ * writes every entry that these tokens complete (blocks b with
+ * seq_len < (b+1)*m <= seq_len+n):
+ *   a_i = gate[i][c] + pos_bias[i][c];  w_i = softmax_i(a) per channel c;
+ *   y_c = sum_i w_i * x_i[c]  (x from bf16 kv; fp32 arithmetic)
+ *   dims 0..447 -> e4m3fn codes with a per-64 fp32 scale amax/448;
+ *   dims 448..511 -> bf16 (round to nearest even);
+ *   CSA: the 64-d indexer stream (ikey, igate, ipos_bias) is pooled the same
+ *   way and stored as two MXFP4 blocks (e2m1 codes, E8M0 = floor(log2 amax)-2).
+ * Then seq_len += n (on the device) and len_min/len_max += n (on the host).
+ *   kv    uint16 [B][n][512] bf16      gate  float [B][n][512]
+ *   ikey  float  [B][n][64]            igate float [B][n][64]  (CSA; NULL for HCA)
+ * Needs ring >= n + max(window, ratio) - 1 and max_blocks*ratio >= len_max+n.
+ * n == 0 is a no-op.  Errors: EINVAL, EUNSUPPORTED, ECAPACITY, EHIP.
+ */
+int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
+                        const float *ikey, const float *igate, int32_t n,
+                        hipStream_t stream);
+
+/*
+ * lca_indexer_topk -- [AGENT] hybrid-attention section (FP4 lightning indexer:
+ * ReLU-scored multi-head dot products, top-k compressed blocks kept);
+ * [REPORT] 核心技術 (the indexer picks top-k compressed blocks).
+ *
+ * For each row and each of the last n_q appended tokens (query position
+ * p = seq_len - n_q + i), over the visible blocks b < floor((p+1)/m):
+ *   q_h = MXFP4(iq[h]) (quantized in the call, same rule as the keys);
+ *   dot_h = exact dot of the dequantized q_h and key b, rounded once to fp32;
+ *   score = +0; for h = 0..H_I-1: score = fmaf(iw[h], max(dot_h, 0), score);
+ *   topk = the min(k, visible) largest (score desc, block asc), written in
+ *          ascending block order, padded with -1.
+ *   iq    float [B][n_q][H_I][64]     iw    float [B][n_q][H_I]
+ *   topk  int32 [B][n_q][k]           (output)
+ * Needs a CSA layer, 1 <= H_I <= 32, 1 <= k <= 2048, n_q <= len_min and
+ * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes.
+ */
+size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k);
+int lca_indexer_topk(const lca_layer *layer, const float *iq, const float *iw, int32_t n_q,
+                     int32_t H_I, int32_t k, int32_t *topk, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * lca_csa_attend -- [ARCH] 2.1 (one attention over the sliding-window KV and
+ * the top-k selected compressed KV); [AGENT] hybrid-attention section (recent
+ * tokens at raw precision).
+ *
+ * For each row, query i (position p = seq_len - n_q + i) and head h: one
+ * softmax attention, logit = scale * (q . k), over the keys
+ *   { entry b : b listed in topk[row][i][0..k), 0 <= b < floor((p+1)/m) }
+ *   then the raw window tokens max(0, p-W+1) .. p,
+ * where an entry's vector is e4m3(code)*scale of its 64-group for dims
+ * 0..447 and the bf16 RoPE dims 448..511, a window token's vector is its raw
+ * bf16 KV, and every key is also its value.  Entries outside the visible
+ * range and -1 are skipped; listed indices must be distinct.
+ *   q     uint16 [B][n_q][H][512] bf16     out float [B][n_q][H][512]
+ * Needs 1 <= H <= 128, 1 <= k <= 2048, n_q <= len_min and
+ * n_q + window - 1 <= ring.  ws must hold lca_attend_workspace(...) bytes.
+ */
+size_t lca_attend_workspace(const lca_layer *layer, int32_t n_q, int32_t H, int32_t k);
+int lca_csa_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32_t H,
+                   const int32_t *topk, int32_t k, float scale, float *out, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lca_hca_attend -- [AGENT] hybrid-attention section and [REPORT] 核心技術
+ * (HCA: 128x compression, no sparse selection, every query attends densely to
+ * all compressed blocks), plus the raw window branch.
+ *
+ * Same as lca_csa_attend with the key set = every visible entry
+ * b < floor((p+1)/m), then the window tokens.  Pass k = 0 to
+ * lca_attend_workspace for this call.
+ */
+int lca_hca_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32_t H,
+                   float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Library version and last error (thread-local, never NULL). */
+int lca_abi_version(void);
+const char *lca_last_error(void);
+
+/*
+ * Kernel timing.  Between lca_timing_begin(kernel) and lca_timing_end(), every
+ * launch of the named kernel is bracketed by HIP events on its stream;
+ * lca_timing_end synchronizes on them and returns the summed duration (ms)
+ * and the number of launches.  Kernel names: "indexer_score", "topk_select",
+ * "attend", "attend_combine", "compress".  At most 4096 launches are
+ * recorded per session.  Errors: EINVAL (unknown name or nested session),
+ * EHIP.
+ */
+int lca_timing_begin(const char *kernel);
+int lca_timing_end(double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,321 @@
+"""Python binding of liblca.so (MI355X / gfx950 compressed long-context attention).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+liblca.so, called through its C ABI (include/lca.h) with plain device
+pointers and the current HIP stream.  PyTorch provides device memory and
+streams.  There is no CPU fallback: if the library is missing or the GPU is
+absent, the calls raise.
+
+    import long_context_compressed_append_amd as lca
+    layer = lca.Layer(batch=32, ratio=4, window=128, ring=256, has_indexer=True,
+                      max_blocks=33000)
+    lca.compress_append(layer, kv, gate, ikey, igate)   # appends n tokens per row
+    topk = lca.indexer_topk(layer, iq, iw, k=512)
+    out = lca.csa_attend(layer, q, topk)
+    out = lca.hca_attend(hca_layer, q)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblca.so")
+
+KV, NOPE, ROPE, IDX = 512, 448, 64, 64
+ERRORS = {0: "LCA_OK", -1: "LCA_EINVAL", -2: "LCA_EUNSUPPORTED", -3: "LCA_ECAPACITY",
+          -4: "LCA_EWORKSPACE", -5: "LCA_EHIP"}
+
+
+class LcaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+P = C.c_void_p
+
+
+class LcaLayerStruct(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("ratio", C.c_int32), ("window", C.c_int32),
+                ("ring", C.c_int32), ("has_indexer", C.c_int32), ("reserved", C.c_int32),
+                ("max_blocks", C.c_int64), ("len_min", C.c_int64), ("len_max", C.c_int64),
+                ("seq_len", P), ("sync", P), ("nope", P), ("rope", P), ("kv_scale", P),
+                ("idx_code", P), ("idx_scale", P), ("ring_kv", P), ("ring_gate", P),
+                ("ring_ikey", P), ("ring_igate", P), ("pos_bias", P), ("ipos_bias", P)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liblca.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "or python long_context_compressed_append_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        LP = C.POINTER(LcaLayerStruct)
+        L.lca_abi_version.restype = C.c_int
+        L.lca_last_error.restype = C.c_char_p
+        L.lca_compress_append.argtypes = [LP, P, P, P, P, C.c_int32, P]
+        L.lca_indexer_workspace.restype = C.c_size_t
+        L.lca_indexer_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
+        L.lca_indexer_topk.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_size_t, P]
+        L.lca_attend_workspace.restype = C.c_size_t
+        L.lca_attend_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
+        L.lca_csa_attend.argtypes = [LP, P, C.c_int32, C.c_int32, P, C.c_int32, C.c_float, P, P,
+                                     C.c_size_t, P]
+        L.lca_hca_attend.argtypes = [LP, P, C.c_int32, C.c_int32, C.c_float, P, P, C.c_size_t, P]
+        L.lca_timing_begin.argtypes = [C.c_char_p]
+        L.lca_timing_end.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise LcaError(rc, lib().lca_last_error().decode(errors="replace"))
+
+
+def _stream():
+    return P(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else P(t.data_ptr())
+
+
+def _dev(t, dtype, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+class Layer:
+    """One layer's cache in device memory (plane layout of include/lca.h).
+
+    Planes are torch tensors on `device`; `from_host` uploads numpy planes of
+    the same layout (the dict built by synth.layers)."""
+
+    PLANES = ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
+              "ring_gate", "ring_ikey", "ring_igate")
+
+    def __init__(self, batch, ratio, window, ring, has_indexer, max_blocks, device="cuda",
+                 pos_bias=None, ipos_bias=None, lengths=None):
+        self.batch, self.ratio, self.window, self.ring = int(batch), int(ratio), int(window), int(ring)
+        self.has_indexer, self.max_blocks = int(bool(has_indexer)), int(max_blocks)
+        B, MB, R = self.batch, self.max_blocks, self.ring
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.seq_len = z((B,), torch.int32)
+        self.sync = z((4,), torch.int32)
+        self.nope = z((B, MB, NOPE), torch.uint8)
+        self.rope = z((B, MB, ROPE), torch.int16)
+        self.kv_scale = z((B, MB, 8), torch.float32)
+        hi = self.has_indexer
+        self.idx_code = z((B, MB, 32), torch.uint8) if hi else None
+        self.idx_scale = z((B, MB, 2), torch.uint8) if hi else None
+        self.ring_kv = z((B, R, KV), torch.int16)
+        self.ring_gate = z((B, R, KV), torch.float32)
+        self.ring_ikey = z((B, R, IDX), torch.float32) if hi else None
+        self.ring_igate = z((B, R, IDX), torch.float32) if hi else None
+        self.pos_bias = (torch.as_tensor(pos_bias, dtype=torch.float32).to(device).contiguous()
+                         if pos_bias is not None else z((self.ratio, KV), torch.float32))
+        self.ipos_bias = None
+        if hi:
+            self.ipos_bias = (torch.as_tensor(ipos_bias, dtype=torch.float32).to(device).contiguous()
+                              if ipos_bias is not None else z((self.ratio, IDX), torch.float32))
+        self.len_min = self.len_max = 0
+        if lengths is not None:
+            self.set_lengths(lengths)
+        self._ws = {}
+
+    @classmethod
+    def from_host(cls, L, device="cuda"):
+        """Upload a numpy plane dict (synth.layers layout)."""
+        lay = cls(L["batch"], L["ratio"], L["window"], L["ring"], L["has_indexer"], L["max_blocks"],
+                  device=device, pos_bias=L["pos_bias"], ipos_bias=L.get("ipos_bias"))
+        lay.upload(L)
+        return lay
+
+    def upload(self, L):
+        import numpy as np
+        for f in self.PLANES:
+            t = getattr(self, f)
+            if t is None:
+                continue
+            a = np.ascontiguousarray(L[f])
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            t.copy_(torch.from_numpy(a).to(t.device))
+        self.len_min = int(L["seq_len"].min())
+        self.len_max = int(L["seq_len"].max())
+
+    def download(self):
+        """Planes back to host numpy (uint16 for bf16 planes)."""
+        import numpy as np
+        out = dict(batch=self.batch, ratio=self.ratio, window=self.window, ring=self.ring,
+                   has_indexer=self.has_indexer, max_blocks=self.max_blocks)
+        for f in self.PLANES:
+            t = getattr(self, f)
+            if t is None:
+                continue
+            a = t.cpu().numpy()
+            if a.dtype == np.int16:
+                a = a.view(np.uint16)
+            out[f] = a
+        out["pos_bias"] = self.pos_bias.cpu().numpy()
+        out["ipos_bias"] = self.ipos_bias.cpu().numpy() if self.ipos_bias is not None else None
+        return out
+
+    def set_lengths(self, lengths):
+        lengths = torch.as_tensor(lengths, dtype=torch.int32)
+        self.seq_len.copy_(lengths.to(self.seq_len.device))
+        self.len_min, self.len_max = int(lengths.min()), int(lengths.max())
+
+    def struct(self):
+        s = LcaLayerStruct()
+        s.batch, s.ratio, s.window, s.ring = self.batch, self.ratio, self.window, self.ring
+        s.has_indexer, s.reserved, s.max_blocks = self.has_indexer, 0, self.max_blocks
+        s.len_min, s.len_max = self.len_min, self.len_max
+        for f in ("seq_len", "sync", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
+                  "ring_gate", "ring_ikey", "ring_igate", "pos_bias", "ipos_bias"):
+            t = getattr(self, f)
+            setattr(s, f, t.data_ptr() if t is not None else None)
+        return s
+
+    def workspace(self, nbytes):
+        """A cached device workspace of at least nbytes (per layer object)."""
+        if nbytes == 0:
+            return None
+        dev = self.seq_len.device
+        ws = self._ws.get(dev)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
+            self._ws[dev] = ws
+        return ws
+
+
+def abi_version():
+    return lib().lca_abi_version()
+
+
+def compress_append(layer: Layer, kv, gate, ikey=None, igate=None):
+    """Append n tokens to every row.  kv int16/bf16 bits [B][n][512], gate fp32
+    [B][n][512], ikey/igate fp32 [B][n][64] (indexer layers)."""
+    B = layer.batch
+    if kv.dtype == torch.bfloat16:
+        kv = kv.view(torch.int16)
+    n = kv.shape[1]
+    _dev(kv, torch.int16, (B, n, KV), "kv")
+    _dev(gate, torch.float32, (B, n, KV), "gate")
+    if layer.has_indexer:
+        _dev(ikey, torch.float32, (B, n, IDX), "ikey")
+        _dev(igate, torch.float32, (B, n, IDX), "igate")
+    s = layer.struct()
+    _check(lib().lca_compress_append(C.byref(s), _ptr(kv), _ptr(gate), _ptr(ikey), _ptr(igate), n,
+                                     _stream()))
+    layer.len_min, layer.len_max = s.len_min, s.len_max
+
+
+def indexer_workspace_bytes(layer: Layer, n_q, H_I, k):
+    s = layer.struct()
+    return lib().lca_indexer_workspace(C.byref(s), n_q, H_I, k)
+
+
+def indexer_topk(layer: Layer, iq, iw, k, out=None):
+    """Top-k visible blocks per query.  iq fp32 [B][n_q][H_I][64], iw fp32
+    [B][n_q][H_I] -> int32 [B][n_q][k] (ascending, -1 padded)."""
+    B, n_q, H_I = iw.shape
+    _dev(iq, torch.float32, (B, n_q, H_I, IDX), "iq")
+    _dev(iw, torch.float32, (B, n_q, H_I), "iw")
+    if out is None:
+        out = torch.empty((B, n_q, k), dtype=torch.int32, device=iq.device)
+    _dev(out, torch.int32, (B, n_q, k), "topk")
+    s = layer.struct()
+    nbytes = lib().lca_indexer_workspace(C.byref(s), n_q, H_I, k)
+    ws = layer.workspace(nbytes)
+    _check(lib().lca_indexer_topk(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _ptr(ws),
+                                  nbytes, _stream()))
+    return out
+
+
+def attend_workspace_bytes(layer: Layer, n_q, H, k=0):
+    s = layer.struct()
+    return lib().lca_attend_workspace(C.byref(s), n_q, H, k)
+
+
+def _q(q):
+    if q.dtype == torch.bfloat16:
+        q = q.view(torch.int16)
+    return q
+
+
+def csa_attend(layer: Layer, q, topk, scale=None, out=None):
+    """q bf16 [B][n_q][H][512], topk int32 [B][n_q][k] -> fp32 [B][n_q][H][512]."""
+    q = _q(q)
+    B, n_q, H, _ = q.shape
+    k = topk.shape[-1]
+    _dev(q, torch.int16, (B, n_q, H, KV), "q")
+    _dev(topk, torch.int32, (B, n_q, k), "topk")
+    scale = 1.0 / math.sqrt(KV) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, n_q, H, KV), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, (B, n_q, H, KV), "out")
+    s = layer.struct()
+    nbytes = lib().lca_attend_workspace(C.byref(s), n_q, H, k)
+    ws = layer.workspace(nbytes)
+    _check(lib().lca_csa_attend(C.byref(s), _ptr(q), n_q, H, _ptr(topk), k, scale, _ptr(out),
+                                _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def hca_attend(layer: Layer, q, scale=None, out=None):
+    """q bf16 [B][n_q][H][512] -> fp32 [B][n_q][H][512] over every visible entry + window."""
+    q = _q(q)
+    B, n_q, H, _ = q.shape
+    _dev(q, torch.int16, (B, n_q, H, KV), "q")
+    scale = 1.0 / math.sqrt(KV) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, n_q, H, KV), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, (B, n_q, H, KV), "out")
+    s = layer.struct()
+    nbytes = lib().lca_attend_workspace(C.byref(s), n_q, H, 0)
+    ws = layer.workspace(nbytes)
+    _check(lib().lca_hca_attend(C.byref(s), _ptr(q), n_q, H, scale, _ptr(out), _ptr(ws), nbytes,
+                                _stream()))
+    return out
+
+
+class KernelTimer:
+    """Sum of HIP-event durations of one library kernel over a code region:
+
+        with KernelTimer("indexer_score") as t: ...
+        t.total_ms, t.launches
+    """
+
+    def __init__(self, kernel):
+        self.kernel = kernel
+        self.total_ms, self.launches = 0.0, 0
+
+    def __enter__(self):
+        _check(lib().lca_timing_begin(self.kernel.encode()))
+        return self
+
+    def __exit__(self, *exc):
+        ms, n = C.c_double(0.0), C.c_int64(0)
+        _check(lib().lca_timing_end(C.byref(ms), C.byref(n)))
+        self.total_ms, self.launches = ms.value, n.value
+        return False

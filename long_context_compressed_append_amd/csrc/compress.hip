@@ -1,0 +1,217 @@
+// compress.hip -- ring append + block finalisation (softmax-gated pooling and
+// FP8 / BF16 / MXFP4 quantisation) in one launch.
+//
+// vibecoco.ai "DeepSeek V4 agent architecture" page, section 混合注意力:
+// KV entries are compressed along the sequence by softmax-gated pooling with a
+// learned position bias (4x for CSA, 128x for HCA), stored in FP8 with BF16
+// RoPE dims; the indexer keys are FP4.  pnsm.cn "DeepSeek V4 架构深度解析"
+// page, section 2.1: the window store keeps raw tokens and overwrites
+// cyclically.
+//
+// Work decomposition: every wavefront takes one task.
+//   ring task      (row, token)        copies the raw token into slot pos % R
+//   finalise task  (row, block, group) pools one 64-channel group of one
+//                  newly completed block: lane = channel.  Groups 0..6 are
+//                  the FP8 groups (wave-wide amax), group 7 the BF16 RoPE dims,
+//                  group 8 the indexer stream (two 32-lane MXFP4 blocks).
+// Finalise tasks read the tokens of the current call from the inputs and the
+// older tokens of a straddling block from the ring; ring tasks only write
+// slots of the current call's tokens, which never alias those older tokens
+// while R >= n + m - 1.  The last workgroup to finish advances seq_len.
+#include "lca_device.h"
+#include "lca_internal.h"
+
+namespace lca {
+
+struct CompressArgs {
+  int B, m, R, n, has_idx, groups, nfin;   // nfin: block slots per row
+  int64_t max_blocks;
+  int32_t* seq_len;
+  uint32_t* sync;
+  uint8_t* nope;
+  uint16_t* rope;
+  float* kv_scale;
+  uint8_t* idx_code;
+  uint8_t* idx_scale;
+  uint16_t* ring_kv;
+  float* ring_gate;
+  float* ring_ikey;
+  float* ring_igate;
+  const float* pos_bias;
+  const float* ipos_bias;
+  const uint16_t* kv;
+  const float* gate;
+  const float* ikey;
+  const float* igate;
+  int64_t ring_tasks, total_tasks;
+};
+
+__device__ __forceinline__ void ring_copy(const CompressArgs& a, int row, int j, int lane) {
+  const int L0 = a.seq_len[row];
+  const int64_t slot = (int64_t)row * a.R + (int64_t)((L0 + j) % a.R);
+  const int64_t src = (int64_t)row * a.n + j;
+  // kv: 512 bf16 = 1 KB -> 16 B per lane
+  const uint4* skv = reinterpret_cast<const uint4*>(a.kv + src * kKv);
+  uint4* dkv = reinterpret_cast<uint4*>(a.ring_kv + slot * kKv);
+  dkv[lane] = skv[lane];
+  // gate: 512 fp32 = 2 KB -> 32 B per lane
+  const uint4* sg = reinterpret_cast<const uint4*>(a.gate + src * kKv);
+  uint4* dg = reinterpret_cast<uint4*>(a.ring_gate + slot * kKv);
+  dg[lane] = sg[lane];
+  dg[lane + 64] = sg[lane + 64];
+  if (a.has_idx) {
+    const uint4* sk = reinterpret_cast<const uint4*>(a.ikey + src * kIdx);
+    const uint4* sgi = reinterpret_cast<const uint4*>(a.igate + src * kIdx);
+    uint4* dk = reinterpret_cast<uint4*>(a.ring_ikey + slot * kIdx);
+    uint4* dgi = reinterpret_cast<uint4*>(a.ring_igate + slot * kIdx);
+    if (lane < 16) dk[lane] = sk[lane];
+    else if (lane < 32) dgi[lane - 16] = sgi[lane - 16];
+  }
+}
+
+// Pool channel `c` (of a stream with C channels) over the m tokens of block bk.
+// Token t of the block comes from this call's input when t >= L0, else from
+// the ring.  Same operation order as the definition: logits, max, exp and
+// ascending sum, then the weights times the values in ascending order.
+template <bool kBf16>
+__device__ __forceinline__ float pool_channel(const CompressArgs& a, int row, int64_t bk, int L0,
+                                              int c, int C, const void* in_x, const float* in_z,
+                                              const void* ring_x, const float* ring_z,
+                                              const float* bias) {
+  const int m = a.m;
+  auto xval = [&](int64_t t) -> float {
+    if (t >= L0) {
+      int64_t i = ((int64_t)row * a.n + (t - L0)) * C + c;
+      return kBf16 ? bf16_f32(static_cast<const uint16_t*>(in_x)[i]) : static_cast<const float*>(in_x)[i];
+    }
+    int64_t i = ((int64_t)row * a.R + t % a.R) * C + c;
+    return kBf16 ? bf16_f32(static_cast<const uint16_t*>(ring_x)[i]) : static_cast<const float*>(ring_x)[i];
+  };
+  auto zval = [&](int64_t t) -> float {
+    if (t >= L0) return in_z[((int64_t)row * a.n + (t - L0)) * C + c];
+    return ring_z[((int64_t)row * a.R + t % a.R) * C + c];
+  };
+  const int64_t t0 = bk * m;
+  float M = -INFINITY;
+  for (int i = 0; i < m; i++) {
+    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
+    M = ai > M ? ai : M;
+  }
+  float S = 0.0f;
+  for (int i = 0; i < m; i++) {
+    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
+    S = __fadd_rn(S, expf(__fsub_rn(ai, M)));
+  }
+  float acc = 0.0f;
+  for (int i = 0; i < m; i++) {
+    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
+    float w = __fdiv_rn(expf(__fsub_rn(ai, M)), S);
+    acc = __fadd_rn(acc, __fmul_rn(w, xval(t0 + i)));
+  }
+  return acc;
+}
+
+__global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  if (task < a.ring_tasks) {
+    ring_copy(a, (int)(task / a.n), (int)(task % a.n), lane);
+  } else if (task < a.total_tasks) {
+    int64_t f = task - a.ring_tasks;
+    const int g = (int)(f % a.groups);
+    f /= a.groups;
+    const int s = (int)(f % a.nfin);
+    const int row = (int)(f / a.nfin);
+    const int L0 = a.seq_len[row];
+    const int64_t bk = (int64_t)(L0 / a.m) + s;
+    if ((bk + 1) * a.m <= (int64_t)L0 + a.n) {      // block completes in this call
+      const int64_t e = (int64_t)row * a.max_blocks + bk;
+      if (g < 8) {
+        const int c = g * 64 + lane;
+        float y = pool_channel<true>(a, row, bk, L0, c, kKv, a.kv, a.gate, a.ring_kv, a.ring_gate,
+                                     a.pos_bias);
+        if (g < 7) {
+          float amax = wave_max(fabsf(y));
+          uint32_t code = 0;
+          float scale = 0.0f;
+          if (amax > 0.0f) {
+            float inv = __fdiv_rn(448.0f, amax);
+            scale = __fdiv_rn(amax, 448.0f);
+            code = f32_e4m3(__fmul_rn(y, inv));
+          }
+          a.nope[e * kNope + c] = (uint8_t)code;
+          if (lane == 0) a.kv_scale[e * kScaleStride + g] = scale;
+        } else {
+          a.rope[e * kRope + lane] = f32_bf16(y);
+          if (lane == 0) a.kv_scale[e * kScaleStride + 7] = 0.0f;
+        }
+      } else {
+        float y = pool_channel<false>(a, row, bk, L0, lane, kIdx, a.ikey, a.igate, a.ring_ikey,
+                                      a.ring_igate, a.ipos_bias);
+        float amax = half_wave_max(fabsf(y));
+        uint32_t code = 0, ebyte = 0;
+        if (amax > 0.0f) {
+          int X = floor_log2(amax) - 2;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+          code = f32_e2m1(ldexpf(y, -X));
+          ebyte = (uint32_t)(X + 127);
+        }
+        uint32_t hi = __shfl_xor(code, 1, kWave);
+        if ((lane & 1) == 0) a.idx_code[e * 32 + (lane >> 1)] = (uint8_t)(code | (hi << 4));
+        if ((lane & 31) == 0) a.idx_scale[e * 2 + (lane >> 5)] = (uint8_t)ebyte;
+      }
+    }
+  }
+  // The last workgroup to finish advances every row's length.  All reads of
+  // seq_len by a workgroup happen before its counter increment.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    uint32_t done = atomicAdd(a.sync, 1u);
+    if (done == gridDim.x - 1) {
+      __threadfence();
+      for (int r = 0; r < a.B; r++) a.seq_len[r] += a.n;
+      atomicExch(a.sync, 0u);
+      __threadfence();
+    }
+  }
+}
+
+int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
+                    const float* igate, int n, hipStream_t stream) {
+  CompressArgs a;
+  a.B = L->batch;
+  a.m = L->ratio;
+  a.R = L->ring;
+  a.n = n;
+  a.has_idx = L->has_indexer;
+  a.groups = L->has_indexer ? 9 : 8;
+  a.nfin = (n - 1) / L->ratio + 1;
+  a.max_blocks = L->max_blocks;
+  a.seq_len = L->seq_len;
+  a.sync = L->sync;
+  a.nope = L->nope;
+  a.rope = L->rope;
+  a.kv_scale = L->kv_scale;
+  a.idx_code = L->idx_code;
+  a.idx_scale = L->idx_scale;
+  a.ring_kv = L->ring_kv;
+  a.ring_gate = L->ring_gate;
+  a.ring_ikey = L->ring_ikey;
+  a.ring_igate = L->ring_igate;
+  a.pos_bias = L->pos_bias;
+  a.ipos_bias = L->ipos_bias;
+  a.kv = kv;
+  a.gate = gate;
+  a.ikey = ikey;
+  a.igate = igate;
+  a.ring_tasks = (int64_t)a.B * n;
+  a.total_tasks = a.ring_tasks + (int64_t)a.B * a.nfin * a.groups;
+  int64_t blocks = (a.total_tasks + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return LCA_EUNSUPPORTED;
+  TimedLaunch t(kKernelCompress, stream);
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return t.done();
+}
+
+}  // namespace lca

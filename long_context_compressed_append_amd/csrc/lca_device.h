@@ -1,0 +1,101 @@
+// lca_device.h -- device-side number formats and wave helpers for the gfx950
+// kernels.  Private to liblca.so.
+//
+// Formats (fixed by the workload definitions and the OCP FP8 / MX documents):
+//   bf16     upper half of binary32, round to nearest even;
+//   e4m3fn   1/4/3 bits, bias 7, max 448, no infinities, saturating encode;
+//   e2m1     1/2/1 bits, values 0, .5, 1, 1.5, 2, 3, 4, 6, saturating encode;
+//   E8M0     2^(e-127) block exponent of an MX block of 32 elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lca {
+
+constexpr int kKv = 512;
+constexpr int kNope = 448;
+constexpr int kRope = 64;
+constexpr int kIdx = 64;
+constexpr int kScaleStride = 8;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even (finite inputs; +-inf stay infinite).
+__device__ __forceinline__ uint16_t f32_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// e4m3fn code -> fp32 value (exact).
+__device__ __forceinline__ float e4m3_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// e4m3fn code -> bf16 bits of the same value (exact: 4 significant bits).
+__device__ __forceinline__ uint32_t e4m3_bf16(uint32_t c) {
+  return __float_as_uint(e4m3_f32(c)) >> 16;
+}
+
+// fp32 -> e4m3fn code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                 // below the smallest normal 2^-6
+    code = (uint32_t)rintf(a * 512.0f);       // multiples of 2^-9, ties to even
+  } else {
+    uint32_t ua = __float_as_uint(a);
+    uint32_t e = (ua >> 23) - 127u + 7u;      // 1..15
+    uint32_t mant = ua & 0x7FFFFFu;
+    uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+    uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+    code = (e << 3) + keep + up;              // a carry moves into the exponent
+  }
+  return sign | code;
+}
+
+// fp32 (already divided by the block scale) -> e2m1 code, RNE, saturating.
+__device__ __forceinline__ uint32_t f32_e2m1(float x) {
+  float a = fabsf(x);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return (__float_as_uint(x) >> 28 & 8u) | c;
+}
+
+// floor(log2(a)) for finite a > 0 (normal or subnormal), exact.
+__device__ __forceinline__ int floor_log2(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)(u >> 23);
+  if (e) return e - 127;
+  return (31 - __clz((int)(u & 0x7FFFFFu))) - 149;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// max over the 32-lane half of the wave that the caller is in
+__device__ __forceinline__ float half_wave_max(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t ord_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace lca

@@ -1,0 +1,59 @@
+// lca_internal.h -- host-side glue shared by the translation units of
+// liblca.so: launch entry points, kernel ids for timing, workspace layouts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lca.h"
+
+namespace lca {
+
+enum KernelId {
+  kKernelNone = -1,
+  kKernelIndexerScore = 0,
+  kKernelTopkSelect = 1,
+  kKernelAttend = 2,
+  kKernelAttendCombine = 3,
+  kKernelCompress = 4,
+  kKernelCount = 5
+};
+
+// Records HIP events around one launch when a timing session for `id` is open.
+struct TimedLaunch {
+  TimedLaunch(KernelId id, hipStream_t s);
+  int done();  // records the stop event; returns LCA_OK or LCA_EHIP
+  int slot;
+  hipStream_t stream;
+};
+
+int set_error(int code, const char* fmt, ...);
+
+int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
+                    const float* igate, int n, hipStream_t stream);
+
+// Indexer: scores as order-preserving uint32 keys, [rows][stride], then the
+// selection.  rows = B * n_q.
+struct IndexerPlan {
+  int64_t stride;       // keys per score row (>= visible blocks of any query)
+  int chunks;           // workgroups per score row
+  size_t keys_bytes;
+};
+IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
+int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
+                   int32_t* topk, void* ws, const IndexerPlan& plan, hipStream_t stream);
+
+// Attention: split-K partials (m, l) and unnormalised o per (row, split, head).
+struct AttendPlan {
+  int splits;
+  int head_groups;
+  int64_t max_keys;     // upper bound of keys per query
+  int chunk;            // keys per split (multiple of the tile)
+  size_t ml_bytes, o_bytes;
+};
+AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa);
+int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const int32_t* topk, int k,
+                  float scale, float* out, void* ws, const AttendPlan& plan, hipStream_t stream);
+
+}  // namespace lca

@@ -1,0 +1,112 @@
+"""Shared helpers of the GPU parity tests: comparison rules against the oracle.
+
+Tolerances (stated once, used by every GPU test):
+  * ring planes, seq_len, top-k index sets, indexer scores: bit-exact;
+  * compressed entries: the pooled value is fp32 on both sides but the
+    device and host exp differ by an ulp now and then, so an FP8/FP4/BF16
+    code may differ by one step where the oracle's pre-rounding value lies
+    within 1e-4 (relative) of that rounding midpoint; an FP8 scale may differ
+    by a few ulps when its amax element does;
+  * attention: per (query, head) row, max|o - o_ref| / max|o_ref| <= 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+ATTN_TOL = 2e-3
+
+
+def e4m3_values():
+    return np.array([oracle.e4m3_value(c) for c in range(256)])
+
+
+_E4 = None
+
+
+def _e4():
+    global _E4
+    if _E4 is None:
+        _E4 = e4m3_values()
+    return _E4
+
+
+E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def _near_mid(t, v1, v2, rel=1e-4):
+    mid = (v1 + v2) / 2.0
+    return abs(t - mid) <= rel * max(abs(mid), 1e-30)
+
+
+def compare_entries(gpu, ref_layer, row, blocks, raw_kv, raw_gate, raw_ikey, raw_igate, pos_bias,
+                    ipos_bias, m):
+    """Compare the GPU's entries of `blocks` with the oracle's pooled-and-
+    quantized values, allowing only midpoint flips.  raw_* hold the m tokens
+    of each block ([nb][m][C]).  Returns the number of tolerated flips."""
+    e4 = _e4()
+    flips = 0
+    for bi, b in enumerate(blocks):
+        x = (raw_kv[bi].astype(np.uint32) << 16).view(np.float32)
+        y = oracle.pool(x, raw_gate[bi], pos_bias)
+        nope, rope, sc = oracle.make_entry(y)
+        g_n, g_r, g_s = gpu["nope"][row, b], gpu["rope"][row, b], gpu["kv_scale"][row, b]
+        for g in range(7):
+            s_ref, s_gpu = np.float32(sc[g]), np.float32(g_s[g])
+            if s_ref != s_gpu:
+                assert abs(s_ref - s_gpu) <= 4 * np.spacing(s_ref), (row, b, g, s_ref, s_gpu)
+                flips += 1
+            yg = y[g * 64:(g + 1) * 64]
+            amax = np.float32(np.abs(yg).max())
+            inv = np.float32(448.0) / amax if amax > 0 else np.float32(0)
+            for c in range(64):
+                cr, cg = nope[g * 64 + c], g_n[g * 64 + c]
+                if e4[cr] == e4[cg]:
+                    continue
+                t = float(np.float32(yg[c]) * inv)
+                adjacent = (cr & 0x80) == (cg & 0x80) and abs(int(cr & 0x7F) - int(cg & 0x7F)) == 1
+                assert adjacent and _near_mid(t, e4[cr], e4[cg]), (row, b, g, c, t, e4[cr], e4[cg])
+                flips += 1
+        assert g_s[7] == 0.0
+        for c in range(64):
+            if rope[c] != g_r[c]:
+                assert abs(int(rope[c]) - int(g_r[c])) == 1, (row, b, c)
+                flips += 1
+        if ref_layer["has_indexer"]:
+            yi = oracle.pool(raw_ikey[bi], raw_igate[bi], ipos_bias)
+            code, ex = oracle.make_idx(yi)
+            g_c, g_e = gpu["idx_code"][row, b], gpu["idx_scale"][row, b]
+            for h in range(2):
+                if ex[h] != g_e[h]:
+                    # amax sits on a power of two: accept one step of exponent
+                    assert abs(int(ex[h]) - int(g_e[h])) == 1, (row, b, h)
+                    flips += 1
+                    continue
+                sc2 = 2.0 ** (int(ex[h]) - 127)
+                for j in range(32):
+                    el = h * 32 + j
+                    nr = (code[el // 2] >> (4 * (el & 1))) & 15
+                    ng = (g_c[el // 2] >> (4 * (el & 1))) & 15
+                    if E2M1[nr] == E2M1[ng]:
+                        continue
+                    t = float(yi[el]) / sc2
+                    assert _near_mid(t, E2M1[nr], E2M1[ng]), (row, b, el, t, nr, ng)
+                    flips += 1
+    return flips
+
+
+def attn_rel_err(out, ref):
+    """max over (query, head) rows of max|o - ref| / max|ref|."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(out - ref).max(-1)
+    den = np.abs(ref).max(-1)
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+def decode_keys(keys_u32):
+    """order-preserving uint32 keys back to fp32 scores"""
+    k = keys_u32.astype(np.uint32)
+    bits = np.where(k & 0x80000000, k & 0x7FFFFFFF, ~k).astype(np.uint32)
+    return bits.view(np.float32)

@@ -1,0 +1,104 @@
+"""The C-ABI library loads on the CPU, exports every symbol include/lca.h
+declares, and rejects bad calls before touching the GPU (no compute calls
+are made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "lca.h")
+LIB = os.path.join(ROOT, "long_context_compressed_append_amd", "liblca.so")
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    return C.CDLL(LIB)
+
+
+def declared_symbols():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lca_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib()
+    syms = declared_symbols()
+    assert {"lca_compress_append", "lca_indexer_topk", "lca_csa_attend", "lca_hca_attend"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_abi_version():
+    L = _lib()
+    assert L.lca_abi_version() == 1
+
+
+def _layer(**kw):
+    from long_context_compressed_append_amd import LcaLayerStruct
+    s = LcaLayerStruct()
+    s.batch, s.ratio, s.window, s.ring, s.has_indexer, s.max_blocks = 1, 4, 16, 64, 0, 16
+    fake = 0x10000   # aligned, never dereferenced: validation fails first
+    for f in ("seq_len", "sync", "nope", "rope", "kv_scale", "ring_kv", "ring_gate", "pos_bias"):
+        setattr(s, f, fake)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ratio=3), -2),            # not a power of two
+    (dict(ratio=256), -2),
+    (dict(batch=0), -1),
+    (dict(ring=8), -3),             # ring < window
+    (dict(seq_len=None), -1),
+    (dict(nope=0x10001), -1),       # misaligned
+    (dict(has_indexer=1), -1),      # indexer planes missing
+    (dict(len_min=5, len_max=2), -1),
+])
+def test_layer_validation(kw, code):
+    L = _lib()
+    L.lca_last_error.restype = C.c_char_p
+    s = _layer(**kw)
+    rc = L.lca_compress_append(C.byref(s), C.c_void_p(0x10000), C.c_void_p(0x10000), None, None, 1, None)
+    assert rc == code, L.lca_last_error()
+    assert L.lca_last_error()
+
+
+def test_call_validation():
+    L = _lib()
+    L.lca_last_error.restype = C.c_char_p
+    s = _layer()
+    p = C.c_void_p(0x10000)
+    # ring too small for the append
+    assert L.lca_compress_append(C.byref(s), p, p, None, None, 60, None) == -3
+    # capacity: 16 blocks * 4 = 64 tokens
+    s2 = _layer(ring=200)
+    assert L.lca_compress_append(C.byref(s2), p, p, None, None, 100, None) == -3
+    # indexer on an HCA layer
+    assert L.lca_indexer_topk(C.byref(s), p, p, 1, 4, 8, p, p, C.c_size_t(1 << 20), None) == -1
+    # n_q beyond the shortest row
+    assert L.lca_hca_attend(C.byref(s), p, 1, 16, C.c_float(0.04), p, None, C.c_size_t(0), None) == -1
+    s3 = _layer(len_min=10, len_max=10)
+    # H out of range
+    assert L.lca_hca_attend(C.byref(s3), p, 1, 129, C.c_float(0.04), p, None, C.c_size_t(0), None) == -2
+    # k out of range
+    assert L.lca_csa_attend(C.byref(s3), p, 1, 16, p, 0, C.c_float(0.04), p, None, C.c_size_t(0),
+                            None) == -2
+    # n == 0 is a no-op
+    assert L.lca_compress_append(C.byref(s), p, p, None, None, 0, None) == 0
+
+
+def test_workspace_queries_are_pure():
+    L = _lib()
+    L.lca_attend_workspace.restype = C.c_size_t
+    L.lca_indexer_workspace.restype = C.c_size_t
+    s = _layer(len_min=131072, len_max=131072, max_blocks=33000, has_indexer=1)
+    n = L.lca_indexer_workspace(C.byref(s), 1, 16, 512)
+    assert n >= 4 * 32768
+    a = L.lca_attend_workspace(C.byref(s), 1, 64, 512)
+    assert a % 4 == 0

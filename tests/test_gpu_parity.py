@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Every case prints its name, shape and seed before touching the GPU.  Inputs
+come from synth (seeded); expected values come from the oracle only.
+"""
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+from synth import layers as SL
+
+from gpu_helpers import ATTN_TOL, attn_rel_err, compare_entries, decode_keys
+
+pytestmark = pytest.mark.gpu
+SCALE = np.float32(1.0 / np.sqrt(512.0))
+
+
+def _lca():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import long_context_compressed_append_amd as lca
+    return lca
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+# ------------------------------------------------------------------ compressor
+
+COMPRESS_CASES = [
+    # (name, ratio, has_idx, window, ring, batch, initial lengths, append sizes)
+    ("csa_m4", 4, 1, 16, 64, 3, [0, 5, 11], [37, 1, 1, 1, 1, 9, 3]),
+    ("hca_m128", 128, 0, 16, 300, 2, [0, 100], [130, 1, 1, 60, 70]),
+    ("m1_idx", 1, 1, 8, 40, 2, [0, 3], [20, 1, 7]),
+    ("m8_noidx", 8, 0, 32, 96, 1, [0], [57, 1, 1, 1, 30]),
+]
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=[c[0] for c in COMPRESS_CASES])
+def test_compress_append_parity(case):
+    lca = _lca()
+    name, m, hi, W, R, B, lens0, appends = case
+    seed = 2000 + zlib.crc32(name.encode()) % 1000
+    say("compress", name, "m", m, "idx", hi, "B", B, "appends", appends, "seed", seed)
+    total = max(lens0) + sum(appends)
+    MB = total // m + 2
+    # history of raw tokens per row (positions 0..total-1)
+    hist = SL.tokens(seed, "hist", B, total, hi)
+    ref = SL.empty_layer(B, m, W, R, hi, MB)
+    ref["pos_bias"], ref["ipos_bias"] = SL.pos_bias(seed, name, m, hi)
+    # initial state: row b holds lens0[b] tokens, appended on the oracle side
+    # token by token (rows with fewer tokens get theirs first)
+    for b in range(B):
+        one = SL.empty_layer(1, m, W, R, hi, MB)
+        one["pos_bias"], one["ipos_bias"] = ref["pos_bias"], ref["ipos_bias"]
+        if lens0[b]:
+            oracle.compress_append(one, hist["kv"][b:b + 1, :lens0[b]].copy(),
+                                   hist["gate"][b:b + 1, :lens0[b]].copy(),
+                                   hist["ikey"][b:b + 1, :lens0[b]].copy() if hi else None,
+                                   hist["igate"][b:b + 1, :lens0[b]].copy() if hi else None)
+        for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
+                  "ring_gate", "ring_ikey", "ring_igate"):
+            ref[f][b] = one[f][0]
+    lay = lca.Layer.from_host(ref)
+    pos = np.array(lens0)
+    for n in appends:
+        idx = pos[:, None] + np.arange(n)[None, :]
+        rows = np.arange(B)[:, None]
+        tk = {k: np.ascontiguousarray(v[rows, idx]) for k, v in hist.items()}
+        oracle.compress_append(ref, tk["kv"], tk["gate"], tk.get("ikey"), tk.get("igate"))
+        lca.compress_append(lay, _dev(tk["kv"]), _dev(tk["gate"]),
+                            _dev(tk["ikey"]) if hi else None, _dev(tk["igate"]) if hi else None)
+        pos = pos + n
+    torch.cuda.synchronize()
+    got = lay.download()
+    assert np.array_equal(got["seq_len"], ref["seq_len"])
+    assert lay.len_min == pos.min() and lay.len_max == pos.max()
+    for f in ("ring_kv", "ring_gate", "ring_ikey", "ring_igate"):
+        if ref[f].size:
+            assert np.array_equal(got[f], ref[f]), f
+    flips = 0
+    for b in range(B):
+        nb = int(pos[b]) // m
+        blocks = list(range(nb))
+        t = np.arange(nb * m).reshape(nb, m)
+        flips += compare_entries(got, ref, b, blocks, hist["kv"][b][t], hist["gate"][b][t],
+                                 hist["ikey"][b][t] if hi else None,
+                                 hist["igate"][b][t] if hi else None, ref["pos_bias"],
+                                 ref["ipos_bias"], m)
+        assert not got["nope"][b, nb:].any()
+    n_codes = sum(int(p) // m for p in pos) * (448 + 64 + (64 if hi else 0))
+    assert flips <= max(2, n_codes // 1000), flips
+
+
+# ------------------------------------------------------------------ indexer
+
+INDEXER_CASES = [
+    # (name, batch, lengths, n_q, H_I, k, needles)
+    ("tiny_h4_k64", 1, [4096], 1, 4, 64, 4),
+    ("ragged_h16_k512", 3, [9000, 4100, 6001], 1, 16, 512, 16),
+    ("prefill_nq5_h16", 2, [3000, 2999], 5, 16, 128, 0),
+    ("h20_two_groups", 2, [2500, 2600], 2, 20, 100, 0),
+    ("h32_k2048", 1, [12000], 1, 32, 2048, 0),
+    ("k_ge_visible", 2, [200, 37], 1, 8, 64, 0),
+]
+
+
+def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed):
+    m, W = 4, 128
+    MB = max(lens) // m + 8
+    ref = SL.make_layer(seed, name, B, m, W, 256, 1, MB, lens)
+    Q = SL.queries(seed, name, B, n_q, 16, H_I)
+    if needles:
+        for b in range(B):
+            SL.plant_needles(ref, seed, name, b, needles, Q["iq"][b, -1], Q["iw"][b, -1],
+                             Q["q"][b, -1])
+    lay = lca.Layer.from_host(ref)
+    return ref, lay, Q
+
+
+@pytest.mark.parametrize("case", INDEXER_CASES, ids=[c[0] for c in INDEXER_CASES])
+def test_indexer_topk_parity(case):
+    lca = _lca()
+    name, B, lens, n_q, H_I, k, needles = case
+    seed = 3000 + len(name)
+    say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed)
+    ref, lay, Q = _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed)
+    got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
+    # scores: the workspace holds one order key per visible block
+    ws = lay._ws[lay.seq_len.device]
+    nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
+    stride = nbytes // (4 * B * n_q)
+    keys = ws[:nbytes].view(torch.int32).cpu().numpy().view(np.uint32).reshape(B * n_q, stride)
+    for b in range(B):
+        for qi in range(n_q):
+            sc = oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"])
+            nv = len(sc)
+            if nv:
+                gs = decode_keys(keys[b * n_q + qi, :nv])
+                bad = np.nonzero(gs.view(np.uint32) != sc.view(np.uint32))[0]
+                assert bad.size == 0, (b, qi, bad[:5], gs[bad[:5]], sc[bad[:5]])
+            assert np.array_equal(got[b, qi], want[b, qi]), (b, qi)
+    if needles:
+        for b in range(B):
+            nd = SL.plant_needles(ref, seed, name, b, needles, Q["iq"][b, -1], Q["iw"][b, -1],
+                                  Q["q"][b, -1])
+            assert set(nd) <= set(got[b, -1].tolist())
+
+
+def test_indexer_equal_scores_take_lowest_indices():
+    lca = _lca()
+    say("indexer equal scores")
+    B, m, L, k = 1, 4, 4000, 50
+    ref = SL.make_layer(77, "eq", B, m, 128, 256, 1, L // m + 4, [L])
+    ref["idx_code"][:] = 0x22          # every key identical
+    ref["idx_scale"][:] = 127
+    Q = SL.queries(77, "eq", B, 1, 16, 4)
+    lay = lca.Layer.from_host(ref)
+    got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k).cpu().numpy()
+    want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
+    assert np.array_equal(got, want)
+    assert list(got[0, 0]) == list(range(k))
+
+
+# ------------------------------------------------------------------ attention
+
+ATTEND_CASES = [
+    # (name, csa, batch, lengths, n_q, H, k, splits)
+    ("hca_h16_small", 0, 1, [4096], 1, 16, 0, 0),
+    ("hca_h64_ragged", 0, 3, [20000, 9001, 300], 1, 64, 0, 0),
+    ("hca_h64_onesplit", 0, 2, [3000, 2000], 1, 64, 0, 1),
+    ("hca_nq4_h20", 0, 2, [5000, 4000], 4, 20, 0, 3),
+    ("csa_h64_k512", 1, 2, [9000, 6000], 1, 64, 512, 0),
+    ("csa_h16_k64_pad", 1, 2, [300, 100], 2, 16, 64, 0),
+    ("csa_h64_k512_onesplit", 1, 1, [8000], 1, 64, 512, 1),
+    ("short_rows", 0, 2, [1, 3], 1, 64, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", ATTEND_CASES, ids=[c[0] for c in ATTEND_CASES])
+def test_attend_parity(case, monkeypatch):
+    lca = _lca()
+    name, csa, B, lens, n_q, H, k, splits = case
+    seed = 4000 + len(name) * 7 + csa
+    say("attend", name, "csa", csa, "B", B, "lens", lens, "n_q", n_q, "H", H, "k", k,
+        "splits", splits, "seed", seed)
+    if splits:
+        monkeypatch.setenv("LCA_ATTEND_SPLITS", str(splits))
+    m = 4 if csa else 128
+    W = 128
+    MB = max(lens) // m + 8
+    R = max(256, n_q + W)
+    ref = SL.make_layer(seed, name, B, m, W, R, csa, MB, lens)
+    Q = SL.queries(seed, name, B, n_q, H)
+    lay = lca.Layer.from_host(ref)
+    q = _dev(Q["q"])
+    if csa:
+        # a selection list with padding, invisible entries and unsorted order
+        rng = np.random.default_rng(seed)
+        topk = np.full((B, n_q, k), -1, np.int32)
+        for b in range(B):
+            for qi in range(n_q):
+                p = lens[b] - n_q + qi
+                nv = (p + 1) // m
+                take = min(k - 2, nv)
+                sel = rng.choice(nv, size=take, replace=False) if nv else np.zeros(0, int)
+                topk[b, qi, :take] = np.sort(sel)
+                if take < k:
+                    topk[b, qi, take] = nv + 3          # not visible: ignored
+        want = oracle.csa_attend(ref, Q["q"], topk, SCALE)
+        got = lca.csa_attend(lay, q, _dev(topk), float(SCALE))
+    else:
+        want = oracle.hca_attend(ref, Q["q"], SCALE)
+        got = lca.hca_attend(lay, q, float(SCALE))
+    torch.cuda.synchronize()
+    err = attn_rel_err(got.cpu().numpy(), want)
+    print("max rel err", err)
+    assert err <= ATTN_TOL
+    # the same call twice gives bitwise-identical output (no races in LDS)
+    again = (lca.csa_attend(lay, q, _dev(topk), float(SCALE)) if csa
+             else lca.hca_attend(lay, q, float(SCALE)))
+    torch.cuda.synchronize()
+    assert torch.equal(again, got)
+
+
+def test_attend_outlier_channels():
+    """FP8 scales stressed by x20 outlier channels (5% of KV channels)."""
+    lca = _lca()
+    say("attend outliers")
+    seed, B, lens, H, m = 5150, 2, [30000, 20000], 64, 128
+    ref = SL.make_layer(seed, "out", B, m, 128, 256, 0, max(lens) // m + 4, lens)
+    rng = np.random.default_rng(seed)
+    ch = rng.choice(512, 26, replace=False)
+    big = ch[ch < 448]
+    # every FP8 group holding an outlier channel gets a x20 scale (once)
+    for g in np.unique(big // 64):
+        ref["kv_scale"][:, :, g] *= 20.0
+    rope_ch = ch[ch >= 448] - 448
+    vals = synth.bf16_to_f32(ref["rope"][:, :, rope_ch]) * 20.0
+    ref["rope"][:, :, rope_ch] = synth.bf16_bits(vals)
+    rk = synth.bf16_to_f32(ref["ring_kv"][:, :, ch]) * 20.0
+    ref["ring_kv"][:, :, ch] = synth.bf16_bits(rk)
+    Q = SL.queries(seed, "out", B, 1, H)
+    lay = lca.Layer.from_host(ref)
+    got = lca.hca_attend(lay, _dev(Q["q"]), float(SCALE))
+    want = oracle.hca_attend(ref, Q["q"], SCALE)
+    err = attn_rel_err(got.cpu().numpy(), want)
+    print("max rel err", err)
+    assert err <= ATTN_TOL
+
+
+# ------------------------------------------------------------------ errors
+
+def test_errors_enqueue_nothing():
+    lca = _lca()
+    say("errors")
+    lay = lca.Layer(1, 4, 16, 32, True, 16)
+    kv = torch.zeros((1, 40, 512), dtype=torch.int16, device="cuda")
+    g = torch.zeros((1, 40, 512), dtype=torch.float32, device="cuda")
+    ik = torch.zeros((1, 40, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(lca.LcaError) as e:
+        lca.compress_append(lay, kv, g, ik, ik)          # ring 32 < 40 + 16 - 1
+    assert e.value.code == -3
+    assert int(lay.seq_len[0]) == 0 and lay.len_max == 0
+    with pytest.raises(lca.LcaError) as e:
+        lca.indexer_topk(lay, torch.zeros((1, 1, 4, 64), device="cuda"),
+                         torch.zeros((1, 1, 4), device="cuda"), 8)   # n_q > shortest row
+    assert e.value.code == -1
