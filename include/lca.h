@@ -155,13 +155,18 @@ int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
  * p = seq_len - n_q + i), over the visible blocks b < floor((p+1)/m):
  *   q_h = MXFP4(iq[h]) (quantized in the call, same rule as the keys);
  *   dot_h = exact dot of the dequantized q_h and key b, rounded once to fp32;
- *   score = +0; for h = 0..H_I-1: score = fmaf(iw[h], max(dot_h, 0), score);
+ *   for each group g of eight heads (8g .. 8g+7): p_g = +0, then
+ *     p_g = fmaf(iw[h], max(dot_h, 0), p_g) for h ascending;
+ *   score = ((p_0 + p_1) + p_2) + ... (ascending groups), a zero score is +0;
  *   topk = the min(k, visible) largest (score desc, block asc), written in
  *          ascending block order, padded with -1.
  *   iq    float [B][n_q][H_I][64]     iw    float [B][n_q][H_I]
  *   topk  int32 [B][n_q][k]           (output)
  * Needs a CSA layer, 1 <= H_I <= 32, 1 <= k <= 2048, n_q <= len_min and
- * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes.
+ * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes, be
+ * zero-filled before its first use, and be used by nothing but
+ * lca_indexer_topk afterwards: its leading part holds per-query histograms
+ * that every call leaves zero-filled again.
  */
 size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k);
 int lca_indexer_topk(const lca_layer *layer, const float *iq, const float *iw, int32_t n_q,

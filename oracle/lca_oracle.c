@@ -315,35 +315,41 @@ int orc_compress_append(orc_layer *L, const uint16_t *kv, const float *gate,
  * weights; score = sum_h w_h * ReLU(q_h . k).  Order of evaluation (fixed so
  * that the selection can be compared bit for bit): each head's dot product is
  * the exact dot of the two dequantized MXFP4 vectors rounded once to fp32;
- * ReLU maps it to +0 unless positive; the heads are folded in ascending order
- * by fp32 fused multiply-adds starting from +0; a zero score is +0.
+ * ReLU maps it to +0 unless positive; heads are folded in groups of eight
+ * (heads 8g .. 8g+7): inside a group by fp32 fused multiply-adds in ascending
+ * head order starting from +0, and the group partials are added in ascending
+ * group order; a zero score is +0.
  * ====================================================================== */
 
 float orc_index_score(const uint8_t *qcode, const uint8_t *qe, const float *w,
                       int H, const uint8_t *kcode, const uint8_t *ke,
                       int *inexact) {
   float score = 0.0f;
-  for (int h = 0; h < H; h++) {
-    double part[2];
-    for (int j = 0; j < 2; j++) {
-      double d = 0.0;                      /* exact: products on a 1/4 grid, |sum| < 2^11 */
-      for (int i = 0; i < ORC_MX_BLOCK; i++) {
-        int el = j * ORC_MX_BLOCK + i;
-        uint8_t qb = qcode[h * 32 + el / 2], kb = kcode[el / 2];
-        uint8_t qn = (el & 1) ? (qb >> 4) : (qb & 15);
-        uint8_t kn = (el & 1) ? (kb >> 4) : (kb & 15);
-        d += orc_e2m1_value(qn) * orc_e2m1_value(kn);
+  for (int g = 0; g * 8 < H; g++) {
+    float part = 0.0f;
+    for (int h = 8 * g; h < H && h < 8 * g + 8; h++) {
+      double halfsum[2];
+      for (int j = 0; j < 2; j++) {
+        double d = 0.0;                    /* exact: products on a 1/4 grid, |sum| < 2^11 */
+        for (int i = 0; i < ORC_MX_BLOCK; i++) {
+          int el = j * ORC_MX_BLOCK + i;
+          uint8_t qb = qcode[h * 32 + el / 2], kb = kcode[el / 2];
+          uint8_t qn = (el & 1) ? (qb >> 4) : (qb & 15);
+          uint8_t kn = (el & 1) ? (kb >> 4) : (kb & 15);
+          d += orc_e2m1_value(qn) * orc_e2m1_value(kn);
+        }
+        halfsum[j] = ldexp(d, ((int)qe[h * 2 + j] - 127) + ((int)ke[j] - 127));
       }
-      part[j] = ldexp(d, ((int)qe[h * 2 + j] - 127) + ((int)ke[j] - 127));
+      double s = halfsum[0] + halfsum[1];
+      /* exactness of the double sum (TwoSum error term must vanish) */
+      double bv = s - halfsum[0], av = s - bv;
+      double err = (halfsum[0] - av) + (halfsum[1] - bv);
+      if (err != 0.0 && inexact) *inexact = 1;
+      float dot = (float)s;                /* the single rounding to fp32 */
+      float r = dot > 0.0f ? dot : 0.0f;
+      part = fmaf(w[h], r, part);
     }
-    double s = part[0] + part[1];
-    /* exactness of the double sum (TwoSum error term must vanish) */
-    double bv = s - part[0], av = s - bv;
-    double err = (part[0] - av) + (part[1] - bv);
-    if (err != 0.0 && inexact) *inexact = 1;
-    float dot = (float)s;                  /* the single rounding to fp32 */
-    float r = dot > 0.0f ? dot : 0.0f;
-    score = fmaf(w[h], r, score);
+    score = (g == 0) ? part : score + part;
   }
   if (score == 0.0f) score = 0.0f;         /* canonical +0 */
   return score;
