@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-attention decode hot path on one MI355X.
+
+Default workload (csa_decode_128k): CSA decode at 128K context, batch 32,
+64 query heads over one shared 512-d KV entry (448 FP8 + 64 BF16), 4x
+compression (32768 entries per row), indexer 16 heads x 64 dims FP4,
+top-k 512, window 128, 16 planted needle blocks per row.  One step = one
+decode token per row through the whole CSA path: compress_append (ring
+append; a block is pooled and quantised every 4th step), indexer_topk and
+csa_attend (with its split-K combine).  Steps rotate over --layers copies of
+the cache (distinct HBM addresses) so that every step reads its cache cold
+from HBM rather than from the 256 MB Infinity Cache, as a multi-layer decode
+does.  hca_decode_1m (HCA at 1M context, batch 16: compress_append +
+hca_attend) is the other workload.
+
+The timed region replays a HIP graph of the steps (captured through
+torch.cuda.graph on the library's stream); the dominant kernel's average
+duration is measured with HIP events around each of its launches (eager
+loop, same launch configuration).  The oracle (plain C, CPU) is timed on the
+host cores on a bounded sample of the same step as the CPU baseline.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode queries/s and HBM GB/s for CSA/HCA at 128K-1M ctx; % of roofline"
+
+WORKLOADS = {
+    # name: (csa?, batch, context, ratio, heads, indexer heads, k, needles, window)
+    "csa_decode_128k": (True, 32, 131072, 4, 64, 16, 512, 16, 128),
+    "hca_decode_1m": (False, 16, 1048576, 128, 64, 0, 0, 0, 128),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step (entries 604 B, idx keys 34 B,
+    window token 1024 B, q H*1024, out H*2048, iq+iw H_I*260, top-k 2*k*4)."""
+    csa, B, ctx, m, H, HI, k, _, W = wl
+    nv = ctx // m
+    per_row = W * 1024 + H * 1024 + H * 2048
+    if csa:
+        per_row += nv * 34 + HI * 260 + 2 * k * 4 + min(k, nv) * 604
+    else:
+        per_row += nv * 604
+    return per_row * B
+
+
+def dominant_bytes(wl):
+    """Algorithmic bytes of one launch of the dominant kernel."""
+    csa, B, ctx, m, H, HI, k, _, W = wl
+    nv = ctx // m
+    if csa:   # indexer_score: every visible key (34 B) plus the query and weights
+        return B * (nv * 34 + HI * 260)
+    # attend (HCA): every entry, the window, q in, partial/final out
+    return B * (nv * 604 + W * 1024 + H * 1024 + H * 2048)
+
+
+def build_host_layer(wl, seed):
+    from synth import layers as SL
+    csa, B, ctx, m, H, HI, k, needles, W = wl
+    L0 = ctx - 1                      # the step appends the query token -> ctx
+    tag = "csa" if csa else "hca"
+    t = time.time()
+    ref = SL.make_layer(seed, tag, B, m, W, 256, int(csa), ctx // m + 64, [L0] * B)
+    Q = SL.queries(seed, tag, B, 1, H, HI)
+    if needles:
+        for b in range(B):
+            SL.plant_needles(ref, seed, tag, b, needles, Q["iq"][b, 0], Q["iw"][b, 0], Q["q"][b, 0])
+    log(f"host image built in {time.time() - t:.1f}s")
+    return ref, Q
+
+
+def cpu_baseline(wl, ref, Q, tokens):
+    """The oracle, as it stands, on one step of the workload for a sample of rows."""
+    import oracle
+    csa, B, ctx, m, H, HI, k, _, W = wl
+    nthreads = min(16, len(os.sched_getaffinity(0)))
+    rows = B if csa else max(1, B // 4)
+    sub = dict(ref)
+    sub["batch"] = rows
+    for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
+              "ring_gate", "ring_ikey", "ring_igate"):
+        sub[f] = np.ascontiguousarray(ref[f][:rows]).copy()      # the oracle appends in place
+    scale = np.float32(1.0 / np.sqrt(512.0))
+    t0 = time.perf_counter()
+    oracle.compress_append(sub, tokens["kv"][:rows], tokens["gate"][:rows],
+                           tokens["ikey"][:rows] if csa else None,
+                           tokens["igate"][:rows] if csa else None)
+    if csa:
+        topk = oracle.indexer_topk(sub, Q["iq"][:rows], Q["iw"][:rows], k, nthreads=nthreads)
+        oracle.csa_attend(sub, Q["q"][:rows], topk, scale, nthreads=nthreads)
+    else:
+        oracle.hca_attend(sub, Q["q"][:rows], scale, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="queries/s", cores=nthreads, kind="oracle",
+                sample=f"one decode step (compress_append + "
+                       f"{'indexer_topk + csa_attend' if csa else 'hca_attend'}) for {rows} of "
+                       f"{B} rows at full context, {dt:.2f}s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="csa_decode_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across "
+              "GPUs with no exchange; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_compressed_append_amd as lca
+    from synth import layers as SL
+
+    wl = WORKLOADS[args.workload]
+    csa, B, ctx, m, H, HI, k, needles, W = wl
+    seed = 1001 if csa else 1002
+    NL = args.layers
+    total_steps = args.warmup + args.steps + NL          # + eager timing pass
+    ref, Q = build_host_layer(wl, seed)
+    # tokens: a few distinct sets, rotated
+    n_tok = 8
+    toks = [SL.tokens(seed, "step", B, 1, int(csa), step=s) for s in range(n_tok)]
+    qs = [SL.queries(seed, "stepq", B, 1, H, HI, step=s) for s in range(n_tok)]
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    t = time.time()
+    layers = []
+    base = lca.Layer.from_host(ref, device=dev)
+    for i in range(NL):
+        if i == 0:
+            lay = base
+        else:
+            lay = lca.Layer(B, m, W, ref["ring"], csa, ref["max_blocks"], device=dev,
+                            pos_bias=ref["pos_bias"], ipos_bias=ref.get("ipos_bias"))
+            for f in lca.Layer.PLANES:
+                src = getattr(base, f)
+                if src is not None:
+                    getattr(lay, f).copy_(src)
+            lay.len_min, lay.len_max = base.len_min, base.len_max
+        layers.append(lay)
+    # every layer gets at most ceil(total_steps / NL) appends: size the plans for that
+    grow = (total_steps + NL - 1) // NL + 1
+    for lay in layers:
+        assert (lay.len_max + grow) // m <= lay.max_blocks
+    torch.cuda.synchronize()
+    log(f"{NL} device layers ready in {time.time() - t:.1f}s "
+        f"({sum(x.nope.numel() for x in layers) / 1e9:.2f} GB of FP8 codes)")
+
+    d_tok = [{kk: up(v) for kk, v in tk.items()} for tk in toks]
+    d_q = [{kk: up(v) for kk, v in qq.items()} for qq in qs]
+    topk_buf = torch.empty((B, 1, max(k, 1)), dtype=torch.int32, device=dev)
+    out_buf = torch.empty((B, 1, H, 512), dtype=torch.float32, device=dev)
+
+    def step(i, plan_len=None):
+        lay = layers[i % NL]
+        tk, qq = d_tok[i % n_tok], d_q[i % n_tok]
+        lca.compress_append(lay, tk["kv"], tk["gate"], tk.get("ikey"), tk.get("igate"))
+        if plan_len is not None:          # graph capture: plan for the largest length reached
+            lay.len_max = plan_len
+        if csa:
+            lca.indexer_topk(lay, qq["iq"], qq["iw"], k, out=topk_buf)
+            lca.csa_attend(lay, qq["q"], topk_buf, out=out_buf)
+        else:
+            lca.hca_attend(lay, qq["q"], out=out_buf)
+
+    # warm-up (eager): allocates workspaces, loads code objects
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    done = args.warmup
+
+    dominant = "indexer_score" if csa else "attend"
+    # eager pass with the dominant kernel bracketed by HIP events
+    t0 = time.perf_counter()
+    with lca.KernelTimer(dominant) as kt:
+        for i in range(done, done + NL):
+            step(i)
+        torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / NL
+    done += NL
+    kernel_ms = kt.total_ms / max(1, kt.launches)
+
+    # graph of NL steps (one per layer), replayed; plans sized for the final lengths
+    graph_ms = None
+    if not args.eager:
+        reps = (args.steps + NL - 1) // NL
+        final_len = max(x.len_max for x in layers) + reps + 2
+        for lay in layers:
+            assert (final_len + 1) // m <= lay.max_blocks
+        lens_before = [(x.len_min, x.len_max) for x in layers]
+        for lay in layers:       # size the workspaces for the planned lengths before capture
+            lay.len_max = final_len
+            if csa:
+                lay.workspace(lca.indexer_workspace_bytes(lay, 1, HI, k), "indexer")
+            lay.workspace(lca.attend_workspace_bytes(lay, 1, H, k), "attend")
+        for lay, (a, b) in zip(layers, lens_before):
+            lay.len_min, lay.len_max = a, b
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(done, done + NL):
+                step(i, plan_len=final_len)
+        torch.cuda.synchronize()
+        # capture does not execute: restore the host mirrors, then replay
+        for lay, (a, b) in zip(layers, lens_before):
+            lay.len_min, lay.len_max = a, b
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        steps_timed = reps * NL
+        for lay in layers:
+            lay.len_min += reps
+            lay.len_max += reps
+        graph_ms = elapsed * 1e3 / steps_timed
+        ms_per_step = graph_ms
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(done, done + args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        steps_timed = args.steps
+        ms_per_step = elapsed * 1e3 / steps_timed
+
+    # final sanity: lengths on the device advanced as many steps as were run
+    dev_len = int(layers[0].seq_len[0].item())
+    log(f"layer 0 length {dev_len}, host mirror {layers[0].len_max}")
+
+    value = B / (ms_per_step / 1e3)
+    dom_bytes = dominant_bytes(wl)
+    achieved = dom_bytes / (kernel_ms / 1e3) / 1e9 if kernel_ms > 0 else 0.0
+    step_bytes = algorithmic_bytes(wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(wl, ref, Q, toks[0])
+        except Exception as e:  # report, never hide
+            cpu = dict(error=repr(e))
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps_timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4/fp8 storage; fp32 scores; bf16/fp16 MFMA with fp32 accumulate",
+        "data": "synthetic (seeded cache images, needle blocks)",
+        "config": {
+            "workload": args.workload,
+            "batch": B, "context": ctx, "ratio": m, "heads": H, "indexer_heads": HI, "topk": k,
+            "window": W, "layers_rotated": NL, "launch": "eager" if args.eager else "hip_graph",
+            "eager_ms_per_step": round(eager_ms, 4),
+            "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
+            "step_algorithmic_bytes": step_bytes,
+            "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_avg_us": round(kernel_ms * 1e3, 3),
+            "bytes_per_launch": dom_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

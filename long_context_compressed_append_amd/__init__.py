@@ -196,15 +196,16 @@ class Layer:
             setattr(s, f, t.data_ptr() if t is not None else None)
         return s
 
-    def workspace(self, nbytes):
-        """A cached device workspace of at least nbytes (per layer object)."""
+    def workspace(self, nbytes, kind="attend"):
+        """A cached, zero-initialised device workspace of at least nbytes, one
+        per kind ("indexer" keeps its histograms zeroed between calls and is
+        used by nothing else)."""
         if nbytes == 0:
             return None
-        dev = self.seq_len.device
-        ws = self._ws.get(dev)
+        ws = self._ws.get(kind)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
-            self._ws[dev] = ws
+            ws = torch.zeros(int(nbytes), dtype=torch.uint8, device=self.seq_len.device)
+            self._ws[kind] = ws
         return ws
 
 
@@ -246,7 +247,7 @@ def indexer_topk(layer: Layer, iq, iw, k, out=None):
     _dev(out, torch.int32, (B, n_q, k), "topk")
     s = layer.struct()
     nbytes = lib().lca_indexer_workspace(C.byref(s), n_q, H_I, k)
-    ws = layer.workspace(nbytes)
+    ws = layer.workspace(nbytes, "indexer")
     _check(lib().lca_indexer_topk(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _ptr(ws),
                                   nbytes, _stream()))
     return out

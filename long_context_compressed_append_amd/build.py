@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblca.so")
 SOURCES = ["api.hip", "compress.hip", "indexer.hip", "attend.hip"]
 # keep MFMA accumulators in arch VGPRs where the kernel rescales them with VALU
-EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

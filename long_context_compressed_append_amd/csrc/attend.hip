@@ -27,13 +27,15 @@ namespace lca {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;          // keys per tile
 constexpr int kKst = 520;          // bf16 per staged key row (512 + 8 pad)
 constexpr int kVst = 40;           // fp16 per staged value column (32 + 8 pad)
 constexpr int kPst = 40;
 constexpr int kMaxTopk = 2048;
-constexpr int kAttendTargetWGs = 512;
+constexpr int kAttendTargetWGs = 256;
 
 struct AttendArgs {
   int n_q, H, m, W, R, k, splits, chunk, csa;
@@ -48,7 +50,7 @@ struct AttendArgs {
   const int32_t* topk;
   float* out;
   float* ws_ml;
-  float* ws_o;
+  _Float16* ws_o;
 };
 
 __device__ __forceinline__ uint32_t scan_excl_256(uint32_t v, uint32_t* tmp, uint32_t* total) {
@@ -90,19 +92,19 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   if (a.csa) {
     // keep listed, visible blocks in list order
     const int32_t* sel = a.topk + (int64_t)srow * a.k;
-    const int per = (a.k + 255) / 256;
-    const int j0 = tid * per, j1 = min(a.k, j0 + per);
+    const int per = (a.k + 255) / 256;          // <= 8
+    const int j0 = tid * per;
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) ev[u] = (u < per && j0 + u < a.k) ? sel[j0 + u] : -1;
     uint32_t cnt = 0;
-    for (int j = j0; j < j1; j++) {
-      const int e = sel[j];
-      cnt += (e >= 0 && e < nv);
-    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) cnt += (ev[u] >= 0 && ev[u] < nv);
     uint32_t total;
     uint32_t pos = scan_excl_256(cnt, tmp, &total);
-    for (int j = j0; j < j1; j++) {
-      const int e = sel[j];
-      if (e >= 0 && e < nv && pos < (uint32_t)kMaxTopk) klist[pos++] = e;
-    }
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (ev[u] >= 0 && ev[u] < nv && pos < (uint32_t)kMaxTopk) klist[pos++] = ev[u];
     n_c = (int)total;
     __syncthreads();
   }
@@ -147,22 +149,28 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
         if (sg < 7) {
           const float s = a.kv_scale[ent * kScaleStride + sg];
           const uint4* src = reinterpret_cast<const uint4*>(a.nope + ent * kNope + sg * 64);
-#pragma unroll 1
+          uint4 cv[4];
+#pragma unroll
+          for (int v = 0; v < 4; v++) cv[v] = src[v];
+#pragma unroll
           for (int v = 0; v < 4; v++) {
-            const uint4 c16 = src[v];
+            const uint4 c16 = cv[v];
             const uint32_t w4[4] = {c16.x, c16.y, c16.z, c16.w};
             uint32_t kb4[8];
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
 #pragma unroll
-              for (int by = 0; by < 4; by++) {
-                const uint32_t code = (w4[q4] >> (8 * by)) & 0xFFu;
-                const int c = v * 16 + q4 * 4 + by;
-                const float val = e4m3_f32(code);
-                const uint32_t kbits = __float_as_uint(val) >> 16;
-                if (by & 1) kb4[q4 * 2 + (by >> 1)] |= kbits << 16;
-                else kb4[q4 * 2 + (by >> 1)] = kbits;
-                Vt[(sg * 64 + c) * kVst + sj] = (_Float16)__fmul_rn(val, s);
+              for (int hw = 0; hw < 2; hw++) {
+                // two codes -> exact fp32 (OCP e4m3 on gfx950), bf16 bits for K,
+                // fp16(value * scale) for V
+                const v2f f = hw ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
+                                 : __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], false);
+                kb4[q4 * 2 + hw] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+                const v2f sv = {__fmul_rn(f[0], s), __fmul_rn(f[1], s)};
+                const v2h hv = __builtin_convertvector(sv, v2h);
+                const int c = v * 16 + q4 * 4 + hw * 2;
+                Vt[(sg * 64 + c) * kVst + sj] = hv[0];
+                Vt[(sg * 64 + c + 1) * kVst + sj] = hv[1];
               }
             }
             uint4* kd = reinterpret_cast<uint4*>(kdst + v * 16);
@@ -172,16 +180,21 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
           sK[sj * 8 + sg] = s;
         } else {
           const uint4* src = reinterpret_cast<const uint4*>(a.rope + ent * kRope);
-#pragma unroll 1
+          uint4 rv[8];
+#pragma unroll
+          for (int v = 0; v < 8; v++) rv[v] = src[v];
+#pragma unroll
           for (int v = 0; v < 8; v++) {
-            const uint4 w = src[v];
+            const uint4 w = rv[v];
             reinterpret_cast<uint4*>(kdst)[v] = w;
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
               const int c = v * 8 + q4 * 2;
-              Vt[(448 + c) * kVst + sj] = (_Float16)bf16_f32((uint16_t)(ww[q4] & 0xFFFFu));
-              Vt[(448 + c + 1) * kVst + sj] = (_Float16)bf16_f32((uint16_t)(ww[q4] >> 16));
+              const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
+              const v2h hv = __builtin_convertvector(f, v2h);
+              Vt[(448 + c) * kVst + sj] = hv[0];
+              Vt[(448 + c + 1) * kVst + sj] = hv[1];
             }
           }
           sK[sj * 8 + 7] = 1.0f;
@@ -190,16 +203,21 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
         const int pos = w0 + (kk - n_c);
         const uint4* src = reinterpret_cast<const uint4*>(
             a.ring_kv + ((int64_t)brow * a.R + pos % a.R) * kKv + sg * 64);
-#pragma unroll 1
+        uint4 rv[8];
+#pragma unroll
+        for (int v = 0; v < 8; v++) rv[v] = src[v];
+#pragma unroll
         for (int v = 0; v < 8; v++) {
-          const uint4 w = src[v];
+          const uint4 w = rv[v];
           reinterpret_cast<uint4*>(kdst)[v] = w;
           const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int q4 = 0; q4 < 4; q4++) {
             const int c = sg * 64 + v * 8 + q4 * 2;
-            Vt[c * kVst + sj] = (_Float16)bf16_f32((uint16_t)(ww[q4] & 0xFFFFu));
-            Vt[(c + 1) * kVst + sj] = (_Float16)bf16_f32((uint16_t)(ww[q4] >> 16));
+            const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
+            const v2h hv = __builtin_convertvector(f, v2h);
+            Vt[c * kVst + sj] = hv[0];
+            Vt[(c + 1) * kVst + sj] = hv[1];
           }
         }
         sK[sj * 8 + sg] = 1.0f;
@@ -307,10 +325,11 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
         a.ws_ml[slot * 2 + 0] = mrow[r];
         a.ws_ml[slot * 2 + 1] = lrow[r];
       }
-      if (lrow[r] > 0.0f) {
-        float* dst = a.ws_o + slot * kKv;
+      if (lrow[r] > 0.0f) {       // normalised partial output, fp16 (values of V's range)
+        const float inv = 1.0f / lrow[r];
+        _Float16* dst = a.ws_o + slot * kKv;
 #pragma unroll
-        for (int ct = 0; ct < 32; ct++) dst[ct * 16 + (lane & 15)] = O[ct][r];
+        for (int ct = 0; ct < 32; ct++) dst[ct * 16 + (lane & 15)] = (_Float16)(O[ct][r] * inv);
       }
     }
   }
@@ -319,30 +338,49 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
 struct CombineArgs {
   int H, splits;
   const float* ws_ml;
-  const float* ws_o;
+  const _Float16* ws_o;
   float* out;
 };
 
 __global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
   const int srow = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   float M = -INFINITY;
-  for (int s = 0; s < a.splits; s++) {
-    const int64_t slot = ((int64_t)srow * a.splits + s) * a.H + h;
-    if (a.ws_ml[slot * 2 + 1] > 0.0f) M = fmaxf(M, a.ws_ml[slot * 2]);
-  }
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < a.splits; s++) {
-    const int64_t slot = ((int64_t)srow * a.splits + s) * a.H + h;
-    const float l = a.ws_ml[slot * 2 + 1];
-    if (!(l > 0.0f)) continue;
-    const float w = exp2f(a.ws_ml[slot * 2] - M);
-    L += l * w;
-    const float4 o = reinterpret_cast<const float4*>(a.ws_o + slot * kKv)[t];
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
+  // splits in groups of 8: every load of a group in flight before use
+  for (int s0 = 0; s0 < a.splits; s0 += 8) {
+    float mv[8], lv[8];
+    uint2 ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int64_t slot = ((int64_t)srow * a.splits + s0 + u) * a.H + h;
+      const bool in = s0 + u < a.splits;
+      mv[u] = in ? a.ws_ml[slot * 2] : -INFINITY;
+      lv[u] = in ? a.ws_ml[slot * 2 + 1] : 0.0f;
+      ov[u] = in ? reinterpret_cast<const uint2*>(a.ws_o + slot * kKv)[t] : make_uint2(0, 0);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (lv[u] > 0.0f) Mn = fmaxf(Mn, mv[u]);
+    const float rescale = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+    L *= rescale;
+    acc.x *= rescale;
+    acc.y *= rescale;
+    acc.z *= rescale;
+    acc.w *= rescale;
+    M = Mn;
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      if (!(lv[u] > 0.0f)) continue;
+      const float w = lv[u] * exp2f(mv[u] - M);
+      L += w;
+      const v2h o01 = __builtin_bit_cast(v2h, ov[u].x), o23 = __builtin_bit_cast(v2h, ov[u].y);
+      acc.x += w * (float)o01[0];
+      acc.y += w * (float)o01[1];
+      acc.z += w * (float)o23[0];
+      acc.w += w * (float)o23[1];
+    }
   }
   const float inv = 1.0f / L;
   reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + h) * kKv)[t] =
@@ -371,7 +409,7 @@ AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   pl.splits = (int)((pl.max_keys + pl.chunk - 1) / pl.chunk);
   if (pl.splits > 1) {
     pl.ml_bytes = (size_t)rows * pl.splits * H * 2 * sizeof(float);
-    pl.o_bytes = (size_t)rows * pl.splits * H * kKv * sizeof(float);
+    pl.o_bytes = (size_t)rows * pl.splits * H * kKv * sizeof(_Float16);
   } else {
     pl.ml_bytes = pl.o_bytes = 0;
   }
@@ -401,7 +439,7 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   a.topk = topk;
   a.out = out;
   a.ws_ml = static_cast<float*>(ws);
-  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + ((pl.ml_bytes + 255) & ~(size_t)255));
+  a.ws_o = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + ((pl.ml_bytes + 255) & ~(size_t)255));
   const int rows = L->batch * n_q;
   {
     TimedLaunch t(kKernelAttend, stream);

@@ -92,6 +92,33 @@ __device__ __forceinline__ float pool_channel(const CompressArgs& a, int row, in
     return ring_z[((int64_t)row * a.R + t % a.R) * C + c];
   };
   const int64_t t0 = bk * m;
+  if (m <= 8) {
+    // short blocks: every token's logit and value in registers, one load pass
+    float av[8], xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if (i < m) {
+        av[i] = __fadd_rn(zval(t0 + i), bias[i * C + c]);
+        xv[i] = xval(t0 + i);
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (i < m) M = av[i] > M ? av[i] : M;
+    float ev[8], S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (i < m) {
+        ev[i] = expf(__fsub_rn(av[i], M));
+        S = __fadd_rn(S, ev[i]);
+      }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (i < m) acc = __fadd_rn(acc, __fmul_rn(__fdiv_rn(ev[i], S), xv[i]));
+    return acc;
+  }
   float M = -INFINITY;
   for (int i = 0; i < m; i++) {
     float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
@@ -164,13 +191,18 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   }
   // The last workgroup to finish advances every row's length.  All reads of
   // seq_len by a workgroup happen before its counter increment.
+  __shared__ uint32_t is_last;
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
-    uint32_t done = atomicAdd(a.sync, 1u);
-    if (done == gridDim.x - 1) {
-      __threadfence();
-      for (int r = 0; r < a.B; r++) a.seq_len[r] += a.n;
+    is_last = atomicAdd(a.sync, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (is_last) {
+    __threadfence();
+    for (int r = threadIdx.x; r < a.B; r += blockDim.x) a.seq_len[r] += a.n;
+    __syncthreads();
+    if (threadIdx.x == 0) {
       atomicExch(a.sync, 0u);
       __threadfence();
     }

@@ -13,18 +13,25 @@
 //   score  = +0, then score = fma(w_h, max(dot_h, 0), score) for h ascending;
 //   a zero score is +0.  The selection is bitwise reproducible.
 //
-// Matrix-core mapping (v_mfma_scale_f32_32x32x64_f8f6f4, both operands e2m1,
-// unit scales): the 32 A rows are (head, half) pairs -- a row carries one
-// head's 32 codes of one MX half and zeros in the other half -- and the 32 B
-// columns are 32 consecutive blocks.  With the 32x32 output layout (lane l
-// holds column l%32 and rows 8i + 4*(l/32) + j), rows are placed so that lane
-// l < 32 receives heads 0..7 and lane l >= 32 heads 8..15 of block l%32, each
-// as its two per-half partial sums.  A per-half partial sum is a sum of 32
-// products on a 1/4 grid below 2^11, so it is exact in fp32 in any order; the
-// scales are then applied in fp32 as exact powers of two and the two halves
-// added by one fused multiply-add, which rounds the exact dot once.  The head
-// chain runs on the low lanes for heads 0..7, hops to the high lanes for
-// heads 8..15, and hops back for the next group of 16 heads.
+// Matrix-core mapping (v_mfma_scale_f32_32x32x64_f8f6f4, both operands e2m1):
+// the 32 A rows are (head, half) pairs -- a row carries one head's 32 codes of
+// one MX half and zeros in the other half -- and the 32 B columns are 32
+// consecutive blocks.  With the 32x32 output layout (lane l holds column l%32
+// and rows 8i + 4*(l/32) + j), rows are placed so that lane l < 32 receives
+// heads 0..7 and lane l >= 32 heads 8..15 of block l%32, each as its two
+// per-half partial dot products.  The hardware applies the E8M0 scales of the
+// query half (A) and of the key half (B).  A per-half partial is a sum of 32
+// products on one power-of-two grid, below 2^11 grid steps, so it is exact;
+// one fp32 add of the two halves then rounds the exact dot once.  Blocks whose
+// scaled partials could leave the fp32 normal range take an unscaled MFMA and
+// apply the scales in fp32 (double for the far ranges), with the same result.
+// The head chain runs on the low lanes for heads 0..7, hops to the high lanes
+// for heads 8..15, and hops back for the next group of 16 heads.
+//
+// While scoring, each workgroup histograms the top 12 bits of its order keys
+// and adds them to a per-query histogram; the selection reads that histogram
+// to find the bin that holds the k-th key, so it needs a single pass over the
+// keys plus an exact ranking of the few keys inside that bin.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -36,6 +43,11 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kScoreBlocksPerIter = 32;
 constexpr int kScoreItersPerWave = 8;
 constexpr int kScoreBlocksPerWG = 4 * kScoreItersPerWave * kScoreBlocksPerIter;  // 1024
+constexpr int kScoreTargetWGs = 512;
+constexpr int kDepth = 4;          // iterations of key loads in flight per wave
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
 
 struct ScoreArgs {
   int n_q, H, m;
@@ -46,6 +58,8 @@ struct ScoreArgs {
   const float* iq;
   const float* iw;
   uint32_t* keys;
+  uint32_t* hist;        // [rows][kHistBins], zero on entry
+  int cpw;               // chunks of 1024 blocks per workgroup
 };
 
 // exact value of D0 * 2^e0 + D1 * 2^e1 rounded once to fp32, where D0, D1 are
@@ -60,6 +74,32 @@ __device__ __forceinline__ float exact_pair(float D0, int e0, float D1, int e1) 
   return (float)v;
 }
 
+// Score of the lane's block when some exponent sum is out of the range where
+// the scaled partials are exact fp32 normals: unscaled MFMA, scales in fp32
+// (double beyond that range).  Rare; kept out of line.
+__device__ __noinline__ float score_unscaled(v8i A0, v8i A1, v8i Bm, int hgroups, int H, int kh,
+                                             const int (*q_exp)[2], const float* q_w, int ke0, int ke1) {
+  const v16f zero16 = {};
+  float total = 0.0f;
+  for (int hg = 0; hg < hgroups; hg++) {
+    const v16f acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(hg ? A1 : A0, Bm, zero16, 4, 4, 0,
+                                                                     127, 0, 127);
+    float part = 0.0f;
+#pragma unroll
+    for (int hl = 0; hl < 8; hl++) {
+      const int h = 16 * hg + 8 * kh + hl;
+      const bool hv = h < H;
+      const float rl = fmaxf(exact_pair(acc[2 * hl], (hv ? q_exp[h][0] : 0) + ke0, acc[2 * hl + 1],
+                                        (hv ? q_exp[h][1] : 0) + ke1), 0.0f);
+      part = __builtin_fmaf(hv ? q_w[h] : 0.0f, rl, part);
+    }
+    const float upper = __shfl_xor(part, 32, kWave);
+    total = (hg == 0) ? part : __fadd_rn(total, part);
+    total = __fadd_rn(total, upper);
+  }
+  return total;
+}
+
 __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   const int srow = blockIdx.y;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
@@ -67,43 +107,89 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   int64_t nv = (int64_t)(p + 1) / a.m;
   if (nv > a.stride) nv = a.stride;            // defensive: never past the key row
   if (nv > a.max_blocks) nv = a.max_blocks;
-  const int64_t base = (int64_t)blockIdx.x * kScoreBlocksPerWG;
-  if (base >= nv) return;
+  // this workgroup's chunks of 1024 blocks: [c0, c1)
+  const int64_t nchunks = (nv + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
+  const int64_t c0 = (int64_t)blockIdx.x * a.cpw;
+  const int64_t c1 = c0 + a.cpw < nchunks ? c0 + a.cpw : nchunks;
+  if (c0 >= c1) return;
 
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
   __shared__ float q_w[32];
+  __shared__ uint32_t lhist[kHistBins];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, kh = lane >> 5;
 
-  // MXFP4 quantisation of the query, one 32-lane half-wave per MX block.
+  const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
+  const uint8_t* ks = a.idx_scale + (int64_t)brow * a.max_blocks * 2;
+  // The wave walks iterations i = 0 .. n_it-1 of 32 blocks each: iteration i
+  // is group i % 8 of this wave's 256 blocks in chunk c0 + i / 8.  Keys are
+  // loaded kDepth iterations ahead of their use.
+  const int n_it = (int)(c1 - c0) * kScoreItersPerWave;
+  auto blk_of = [&](int i) -> int64_t {
+    return (c0 + i / kScoreItersPerWave) * kScoreBlocksPerWG +
+           (int64_t)wave * (kScoreItersPerWave * kScoreBlocksPerIter) +
+           (i % kScoreItersPerWave) * kScoreBlocksPerIter + r;
+  };
+  auto load = [&](int i, int4& kr, uint32_t& er) {
+    const int64_t blk = blk_of(i);
+    kr = make_int4(0, 0, 0, 0);
+    er = 0x7F7Fu;
+    if (i < n_it && blk < nv) {
+      kr = *reinterpret_cast<const int4*>(kc + blk * 32 + 16 * kh);
+      er = *reinterpret_cast<const uint16_t*>(ks + blk * 2);
+    }
+  };
+  // two blocks of kDepth iterations in flight
+  int4 kA[kDepth], kB[kDepth];
+  uint32_t eA[kDepth], eB[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; u++) {
+    load(u, kA[u], eA[u]);
+    load(kDepth + u, kB[u], eB[u]);
+  }
+
+  // query values and weights: all loads in flight before any is used
   const float* qsrc = a.iq + (int64_t)srow * a.H * kIdx;
-  for (int e = tid; e < a.H * kIdx; e += 256) {
-    float x = qsrc[e];
+  float qv[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int e = tid + 256 * u;
+    qv[u] = e < a.H * kIdx ? qsrc[e] : 0.0f;
+  }
+  const float wq = tid < a.H ? a.iw[(int64_t)srow * a.H + tid] : 0.0f;
+  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
+  // MXFP4 quantisation of the query, one 32-lane half-wave per MX block.
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int e = tid + 256 * u;
+    if (e >= a.H * kIdx) break;
+    const float x = qv[u];
     float amax = half_wave_max(fabsf(x));
     uint32_t code = 0;
-    int X = 0;
+    int X = -127;
     if (amax > 0.0f) {
       X = floor_log2(amax) - 2;
       X = X < -127 ? -127 : (X > 127 ? 127 : X);
       code = f32_e2m1(ldexpf(x, -X));
-    } else {
-      X = -127;
     }
     uint32_t hi = __shfl_xor(code, 1, kWave);
     const int h = e >> 6, el = e & 63;
     if ((el & 1) == 0) q_code[h][el >> 1] = (uint8_t)(code | (hi << 4));
     if ((el & 31) == 0) q_exp[h][el >> 5] = X;
   }
-  if (tid < a.H) q_w[tid] = a.iw[(int64_t)srow * a.H + tid];
+  if (tid < a.H) q_w[tid] = wq;
   __syncthreads();
 
-  // A operands: lane l feeds row l%32 with the K-half l/32.
-  const int r = lane & 31, kh = lane >> 5;
+  // A operands and their E8M0 scales: lane l feeds row l%32 with K-half l/32.
   const int hgroups = (a.H + 15) >> 4;
   v8i A[2];
+  int sa[2];
+  int qmin = 1 << 20, qmax = -(1 << 20);
 #pragma unroll
   for (int hg = 0; hg < 2; hg++) {
     A[hg] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    sa[hg] = 127;
     const int G = (r & 7) >> 2, v = 4 * (r >> 3) + (r & 3);
     const int h = 16 * hg + 8 * G + (v >> 1), half = v & 1;
     if (hg < hgroups && half == kh && h < a.H) {
@@ -112,88 +198,122 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
       A[hg][1] = src[1];
       A[hg][2] = src[2];
       A[hg][3] = src[3];
+      sa[hg] = q_exp[h][kh] + 127;
     }
   }
-  // Per-lane epilogue constants for the 8 heads of this lane's set.
-  int qe0[2][8], qe1[2][8];
+  // Per-lane epilogue constants for the 8 heads of this lane's set (octet
+  // 2*hg + kh); heads past H get weight 0, which leaves the chain unchanged.
   float wv[2][8];
-  bool hv[2][8];
 #pragma unroll
   for (int hg = 0; hg < 2; hg++)
 #pragma unroll
     for (int hl = 0; hl < 8; hl++) {
       const int h = 16 * hg + 8 * kh + hl;
-      hv[hg][hl] = h < a.H;
-      qe0[hg][hl] = h < a.H ? q_exp[h][0] : 0;
-      qe1[hg][hl] = h < a.H ? q_exp[h][1] : 0;
       wv[hg][hl] = h < a.H ? q_w[h] : 0.0f;
     }
+  for (int h = 0; h < a.H; h++) {
+    qmin = min(qmin, min(q_exp[h][0], q_exp[h][1]));
+    qmax = max(qmax, max(q_exp[h][0], q_exp[h][1]));
+  }
 
-  const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
-  const uint8_t* ks = a.idx_scale + (int64_t)brow * a.max_blocks * 2;
   uint32_t* out = a.keys + (int64_t)srow * a.stride;
   const v16f zero16 = {};
 
-  for (int it = 0; it < kScoreItersPerWave; it++) {
-    const int64_t blk0 = base + (int64_t)wave * (kScoreItersPerWave * kScoreBlocksPerIter) +
-                         (int64_t)it * kScoreBlocksPerIter;
-    if (blk0 >= nv) break;
-    const int64_t blk = blk0 + r;
-    const bool valid = blk < nv;
-    v8i Bm = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-    int ke0 = 0, ke1 = 0;
-    if (valid) {
-      const int4 kv4 = *reinterpret_cast<const int4*>(kc + blk * 32 + 16 * kh);
-      Bm[0] = kv4.x;
-      Bm[1] = kv4.y;
-      Bm[2] = kv4.z;
-      Bm[3] = kv4.w;
-      const uint16_t e2 = *reinterpret_cast<const uint16_t*>(ks + blk * 2);
-      ke0 = (int)(e2 & 0xFF) - 127;
-      ke1 = (int)(e2 >> 8) - 127;
+  // kDepth iterations at once: their matrix-core products and head chains are
+  // independent, so they interleave; one range check covers the block.
+  auto compute = [&](int i0, const int4 (&kr)[kDepth], const uint32_t (&er)[kDepth]) {
+    int ke0[kDepth], ke1[kDepth], sb[kDepth];
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) {
+      ke0[u] = (int)(er[u] & 0xFF) - 127;
+      ke1[u] = (int)(er[u] >> 8) - 127;
+      sb[u] = kh ? (ke1[u] + 127) : (ke0[u] + 127);
+      // scaled partials stay normal fp32 when every exponent sum is in range
+      ok = ok && (qmin + min(ke0[u], ke1[u]) >= -124) && (qmax + max(ke0[u], ke1[u]) <= 116);
     }
-    float part = 0.0f;
+    float total[kDepth];
+    if (__all(ok)) {
 #pragma unroll
-    for (int hg = 0; hg < 2; hg++) {
-      if (hg < hgroups) {
-        v16f acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[hg], Bm, zero16, 4, 4, 0, 127,
-                                                                   0, 127);
-        float rl[8];
+      for (int hg = 0; hg < 2; hg++) {
+        if (hg < hgroups) {
+          v16f acc[kDepth];
 #pragma unroll
-        for (int hl = 0; hl < 8; hl++) {
-          float s = exact_pair(acc[2 * hl], qe0[hg][hl] + ke0, acc[2 * hl + 1], qe1[hg][hl] + ke1);
-          rl[hl] = fmaxf(s, 0.0f);
+          for (int u = 0; u < kDepth; u++) {
+            const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
+            acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[hg], Bm, zero16, 4, 4, 0, sa[hg],
+                                                                     0, sb[u]);
+          }
+          // both lane sets fold their octet at once; the low set adds the octets
+          float part[kDepth], upper[kDepth];
+#pragma unroll
+          for (int u = 0; u < kDepth; u++) {
+            part[u] = 0.0f;
+#pragma unroll
+            for (int hl = 0; hl < 8; hl++)
+              part[u] = __builtin_fmaf(wv[hg][hl],
+                                       fmaxf(__fadd_rn(acc[u][2 * hl], acc[u][2 * hl + 1]), 0.0f), part[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < kDepth; u++) upper[u] = __shfl_xor(part[u], 32, kWave);
+#pragma unroll
+          for (int u = 0; u < kDepth; u++) {
+            total[u] = (hg == 0) ? part[u] : __fadd_rn(total[u], part[u]);
+            total[u] = __fadd_rn(total[u], upper[u]);
+          }
         }
-        // low lanes: heads 16hg+0..7
-        if (kh == 0) {
+      }
+    } else {
 #pragma unroll
-          for (int hl = 0; hl < 8; hl++)
-            if (hv[hg][hl]) part = __builtin_fmaf(wv[hg][hl], rl[hl], part);
-        }
-        float other = __shfl_xor(part, 32, kWave);
-        if (kh == 1) {
-          part = other;
-#pragma unroll
-          for (int hl = 0; hl < 8; hl++)
-            if (hv[hg][hl]) part = __builtin_fmaf(wv[hg][hl], rl[hl], part);
-        }
-        other = __shfl_xor(part, 32, kWave);
-        if (kh == 0) part = other;
+      for (int u = 0; u < kDepth; u++) {
+        const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
+        total[u] = score_unscaled(A[0], A[1], Bm, hgroups, a.H, kh, q_exp, q_w, ke0[u], ke1[u]);
       }
     }
-    if (kh == 0 && valid) {
-      const float sc = __fadd_rn(part, 0.0f);   // -0 -> +0
-      out[blk] = ord_key(sc);
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) {
+      const int64_t blk = blk_of(i0 + u);
+      if (kh == 0 && i0 + u < n_it && blk < nv) {
+        const uint32_t key = ord_key(__fadd_rn(total[u], 0.0f));   // -0 -> +0
+        out[blk] = key;
+        atomicAdd(&lhist[key >> kHistShift], 1u);
+      }
     }
+  };
+
+#pragma unroll 1
+  for (int i0 = 0; i0 < n_it; i0 += 2 * kDepth) {
+    compute(i0, kA, eA);
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) load(i0 + 2 * kDepth + u, kA[u], eA[u]);
+    compute(i0 + kDepth, kB, eB);
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) load(i0 + 3 * kDepth + u, kB[u], eB[u]);
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+  for (int i = tid; i < kHistBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-k by (score desc, block asc) over one score row per workgroup.
-// Radix select on the 32-bit order keys (12 + 12 + 8 bits) finds the k-th key
-// T and how many keys equal to T are needed; a compaction pass then emits, in
-// ascending block order, every block above T and the lowest-index blocks equal
-// to T.  Rows with at most k visible blocks emit them all, then -1.
+// Exact top-k by (score desc, block asc) for one query per workgroup.
+//   1. The query's histogram (top 12 key bits) gives the bin tb holding the
+//      k-th largest key and the count `above` of keys in higher bins; the
+//      histogram is zeroed for the next call.
+//   2. Pass over the keys: a ballot per 64 blocks writes the bitmap of keys
+//      above tb.  Keys inside tb either go straight to an LDS candidate list
+//      (when the bin is small) or are histogrammed on their next 12 bits, and
+//      a second pass marks those above the sub-bin and lists those inside it.
+//   3. A radix select over the candidate list finds the exact threshold key T;
+//      candidates above T are marked, and among keys equal to T the lowest
+//      block indices are taken.
+//   4. The bitmap is compacted into ascending block indices.
+// If even the second-level bin overflows the list (many nearly equal
+// scores), a radix select runs over all keys and the equal keys are ranked
+// by block index with a scan.
 // ---------------------------------------------------------------------------
 
 struct SelectArgs {
@@ -201,10 +321,14 @@ struct SelectArgs {
   int64_t stride;
   const int32_t* seq_len;
   const uint32_t* keys;
+  uint32_t* hist;
   int32_t* topk;
 };
 
 constexpr int kSelThreads = 1024;
+constexpr int kCandCap = 4096;
+constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
+static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
 
 // exclusive prefix sum over the 1024 threads; returns the block total in *total
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
@@ -233,83 +357,298 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return before_wave + x - v;
 }
 
+// Over the nb-bin histogram: the bin x where the count from the top reaches
+// `need`; found[0] = x, found[1] = keys in bins above x, found[2] = count(x).
+__device__ __noinline__ void find_bin(const uint32_t* hist, uint32_t nb, uint32_t need, uint32_t* tmp,
+                         uint32_t* found) {
+  const int tid = threadIdx.x;
+  const uint32_t per = nb >= kSelThreads ? nb / kSelThreads : 1;
+  const uint32_t lo = (uint32_t)tid * per;
+  const uint32_t hi = lo < nb ? lo + per : lo;
+  uint32_t local = 0;
+  for (uint32_t j = lo; j < hi; j++) local += hist[j];
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan(local, tmp, &total);
+  uint32_t running = total - below - local;
+  for (int j = (int)hi - 1; j >= (int)lo; j--) {
+    const uint32_t c = hist[j];
+    if (running < need && running + c >= need) {
+      found[0] = (uint32_t)j;
+      found[1] = running;
+      found[2] = c;
+    }
+    running += c;
+  }
+  __syncthreads();
+}
+
+// Visit the row's keys in 64-key words: wave w takes words w, w+16, ...; the
+// keys of 16 words are loaded before any is used, so the loads overlap.
+template <typename F>
+__device__ __forceinline__ void for_each_word(const uint32_t* keys, int nv, int nwords, F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kBatch = 8;
+#pragma unroll 1
+  for (int wb = wave; wb < nwords; wb += kBatch * (kSelThreads / 64)) {
+    uint32_t kk[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int j = (wb + u * (kSelThreads / 64)) * 64 + lane;
+      kk[u] = j < nv ? keys[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int w = wb + u * (kSelThreads / 64);
+      if (w < nwords) f(w, w * 64 + lane, kk[u]);
+    }
+  }
+}
+
+__device__ __forceinline__ void set_bit(uint32_t* bitmap, uint32_t j) {
+  atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+}
+
+// Marks the `need` best of nc listed candidates (key desc, block asc); all
+// candidates share the key bits above bit `shift`.
+__device__ __noinline__ void select_candidates(uint32_t nc, uint32_t need, int shift, const uint32_t* ck,
+                                  const uint32_t* ci, uint32_t* hist, uint32_t* tmp,
+                                  uint32_t* found, uint32_t* bitmap) {
+  const int tid = threadIdx.x;
+  uint32_t pfx = shift < 32 ? (ck[0] >> shift) : 0u;
+  while (shift > 0) {
+    const int width = shift >= 12 ? 12 : shift;
+    const int lo = shift - width;
+    const uint32_t nb = 1u << width;
+    for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < nc; i += kSelThreads) {
+      const uint32_t key = ck[i];
+      if ((key >> shift) == pfx) atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, nb, need, tmp, found);
+    need -= found[1];
+    pfx = (pfx << width) | found[0];
+    shift = lo;
+    __syncthreads();
+  }
+  const uint32_t T = pfx, need_eq = need;
+  // candidates above T are in; those equal to T are listed (hist is free now)
+  uint32_t* eq = hist;
+  if (tid == 0) found[3] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < nc; i += kSelThreads) {
+    const uint32_t key = ck[i];
+    if (key > T) {
+      set_bit(bitmap, ci[i]);
+    } else if (key == T) {
+      const uint32_t pos = atomicAdd(&found[3], 1u);
+      eq[pos] = ci[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t ne = found[3];
+  // ties at T (rare): the need_eq lowest block indices
+  for (uint32_t i = tid; i < ne; i += kSelThreads) {
+    const uint32_t me = eq[i];
+    uint32_t rank = 0;
+    if (ne > need_eq) {
+#pragma unroll 8
+      for (uint32_t j = 0; j < ne; j++) rank += eq[j] < me;
+    }
+    if (rank < need_eq) set_bit(bitmap, me);
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) {
   const int srow = blockIdx.x;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
   const int p = a.seq_len[brow] - a.n_q + qi;
   int nv = (p + 1) / a.m;
   if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
-  const int k = a.k, tid = threadIdx.x;
+  const int k = a.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* out = a.topk + (int64_t)srow * k;
+  const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t tmp[64];
+  __shared__ uint32_t found[4];
+  __shared__ uint32_t cand[2 * kCandCap];      // keys, then block indices
+  __shared__ uint32_t bitmap[2 * kMaxWords];
+  __shared__ uint32_t cand_n;
+  uint32_t* cand_key = cand;
+  uint32_t* cand_idx = cand + kCandCap;
+
+  // 1. histogram -> threshold bin; leave the global histogram zeroed
+  {
+    constexpr int kPer = kHistBins / kSelThreads;
+    uint32_t hv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) hv[u] = gh[tid + u * kSelThreads];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      hist[tid + u * kSelThreads] = hv[u];
+      gh[tid + u * kSelThreads] = 0;
+    }
+  }
   if (nv <= k) {
     for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t tmp[64];
-  __shared__ uint32_t found[2];
+  if (tid == 0) {
+    cand_n = 0;
+    found[0] = found[1] = found[2] = 0;
+  }
+  __syncthreads();
+  find_bin(hist, kHistBins, (uint32_t)k, tmp, found);
+  const uint32_t tb = found[0], above = found[1], inbin = found[2];
+  const uint32_t need1 = (uint32_t)k - above;
+  __syncthreads();
+  const int nwords = (nv + 63) >> 6;
 
-  uint32_t prefix = 0;
-  uint32_t remaining = (uint32_t)k;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  for (int d = 0; d < 3; d++) {
-    const int shift = shifts[d], width = widths[d];
-    const uint32_t nb = 1u << width, mask = nb - 1;
-    for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
-    __syncthreads();
-    for (int j = tid; j < nv; j += kSelThreads) {
-      const uint32_t key = keys[j];
-      if (d == 0 || (key >> (shift + width)) == prefix) atomicAdd(&hist[(key >> shift) & mask], 1u);
+  // 2. bitmap of keys above tb; keys inside tb listed or sub-histogrammed
+  const bool direct = inbin <= (uint32_t)kCandCap;
+  if (!direct)
+    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+    const bool inb = j < nv && (key >> kHistShift) == tb;
+    const uint64_t sm = __ballot(j < nv && (key >> kHistShift) > tb);
+    if (lane == 0) {
+      bitmap[2 * w] = (uint32_t)sm;
+      bitmap[2 * w + 1] = (uint32_t)(sm >> 32);
     }
-    __syncthreads();
-    // bins owned by this thread: [lo, hi)
-    const uint32_t per = nb >= kSelThreads ? nb / kSelThreads : 1;
-    const uint32_t lo = (uint32_t)tid * per;
-    const uint32_t hi = lo < nb ? lo + per : lo;
-    uint32_t local = 0;
-    for (uint32_t j = lo; j < hi; j++) local += hist[j];
-    uint32_t total;
-    const uint32_t below = block_exclusive_scan(local, tmp, &total);
-    uint32_t running = total - below - local;   // keys in bins above this thread's range
-    for (int j = (int)hi - 1; j >= (int)lo; j--) {
-      const uint32_t c = hist[j];
-      if (running < remaining && running + c >= remaining) {
-        found[0] = (uint32_t)j;
-        found[1] = running;
+    if (direct) {
+      const uint64_t cm = __ballot(inb);
+      if (cm) {
+        uint32_t basepos = 0;
+        if (lane == 0) basepos = atomicAdd(&cand_n, (uint32_t)__popcll(cm));
+        basepos = __shfl(basepos, 0, kWave);
+        if (inb) {
+          const uint32_t pos = basepos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
+          if (pos < (uint32_t)kCandCap) {
+            cand_key[pos] = key;
+            cand_idx[pos] = (uint32_t)j;
+          }
+        }
       }
-      running += c;
+    } else if (inb) {
+      atomicAdd(&hist[(key >> 8) & (kHistBins - 1)], 1u);
+    }
+  });
+  __syncthreads();
+
+  bool done = false;
+  if (direct) {
+    select_candidates(min(cand_n, (uint32_t)kCandCap), need1, kHistShift, cand_key, cand_idx, hist,
+                      tmp, found, bitmap);
+    done = true;
+  } else {
+    find_bin(hist, kHistBins, need1, tmp, found);
+    const uint32_t x2 = found[0], above2 = found[1], inbin2 = found[2];
+    __syncthreads();
+    if (inbin2 <= (uint32_t)kCandCap) {
+      const uint32_t pfx = (tb << 12) | x2;
+      for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+        const bool inb = j < nv && (key >> kHistShift) == tb;
+        const uint64_t sm = __ballot(inb && ((key >> 8) & (kHistBins - 1)) > x2);
+        if (lane == 0) {
+          bitmap[2 * w] |= (uint32_t)sm;
+          bitmap[2 * w + 1] |= (uint32_t)(sm >> 32);
+        }
+        const bool c2 = j < nv && (key >> 8) == pfx;
+        const uint64_t cm = __ballot(c2);
+        if (cm) {
+          uint32_t basepos = 0;
+          if (lane == 0) basepos = atomicAdd(&cand_n, (uint32_t)__popcll(cm));
+          basepos = __shfl(basepos, 0, kWave);
+          if (c2) {
+            const uint32_t pos = basepos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
+            if (pos < (uint32_t)kCandCap) {
+              cand_key[pos] = key;
+              cand_idx[pos] = (uint32_t)j;
+            }
+          }
+        }
+      });
+      __syncthreads();
+      select_candidates(min(cand_n, (uint32_t)kCandCap), need1 - above2, 8, cand_key, cand_idx, hist,
+                        tmp, found, bitmap);
+      done = true;
+    }
+  }
+
+  if (!done) {
+    // Many keys share 24 high bits: radix select over every key (12 + 12 + 8
+    // bits), then every key above T and the lowest-index keys equal to T.
+    uint32_t pfx = 0, need = (uint32_t)k;
+    const int shifts[3] = {20, 8, 0};
+    const int widths[3] = {12, 12, 8};
+    for (int d = 0; d < 3; d++) {
+      const int shift = shifts[d], width = widths[d];
+      const uint32_t nb = 1u << width, mask = nb - 1;
+      for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
+      __syncthreads();
+      for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+        if (j < nv && (d == 0 || (key >> (shift + width)) == pfx))
+          atomicAdd(&hist[(key >> shift) & mask], 1u);
+      });
+      __syncthreads();
+      find_bin(hist, nb, need, tmp, found);
+      need -= found[1];
+      pfx = (pfx << width) | found[0];
+      __syncthreads();
+    }
+    const uint32_t T = pfx, need_eq = need;
+    // equal keys per 64-block word (cand_key doubles as the count array)
+    uint32_t* eqc = cand;       // 2 * kCandCap = kMaxWords counters
+    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+      const uint64_t gm = __ballot(j < nv && key > T);
+      const uint64_t em = __ballot(j < nv && key == T);
+      if (lane == 0) {
+        bitmap[2 * w] = (uint32_t)gm;
+        bitmap[2 * w + 1] = (uint32_t)(gm >> 32);
+        eqc[w] = (uint32_t)__popcll(em);
+      }
+    });
+    __syncthreads();
+    const int wp = (nwords + kSelThreads - 1) / kSelThreads;
+    const int a0 = tid * wp, a1 = min(nwords, a0 + wp);
+    uint32_t loc = 0;
+    for (int w = a0; w < a1; w++) loc += eqc[w];
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan(loc, tmp, &tot);
+    for (int w = a0; w < a1; w++) {
+      const uint32_t c = eqc[w];
+      eqc[w] = run;
+      run += c;
     }
     __syncthreads();
-    remaining -= found[1];
-    prefix = (prefix << width) | found[0];
+    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+      const bool eq = j < nv && key == T;
+      const uint64_t em = __ballot(eq);
+      const uint32_t rank = eqc[w] + (uint32_t)__popcll(em & ((1ull << lane) - 1ull));
+      if (eq && rank < need_eq) set_bit(bitmap, (uint32_t)j);
+    });
     __syncthreads();
   }
-  const uint32_t T = prefix, need_eq = remaining;
 
-  // compaction in ascending block order
-  const int seg = (nv + kSelThreads - 1) / kSelThreads;
-  const int j0 = tid * seg, j1 = min(nv, j0 + seg);
-  uint32_t gt = 0, eq = 0;
-  for (int j = j0; j < j1; j++) {
-    const uint32_t key = keys[j];
-    gt += key > T;
-    eq += key == T;
-  }
+  // 4. compaction: ascending block order
+  const int wper = (nwords + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * wper, w1 = min(nwords, w0 + wper);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; w++) cnt += __popc(bitmap[2 * w]) + __popc(bitmap[2 * w + 1]);
   uint32_t tot;
-  uint32_t gt_run = block_exclusive_scan(gt, tmp, &tot);
-  uint32_t eq_run = block_exclusive_scan(eq, tmp, &tot);
-  for (int j = j0; j < j1; j++) {
-    const uint32_t key = keys[j];
-    if (key > T) {
-      const uint32_t pos = gt_run + min(eq_run, need_eq);
-      if (pos < (uint32_t)k) out[pos] = j;
-      gt_run++;
-    } else if (key == T) {
-      const uint32_t pos = gt_run + eq_run;
-      if (eq_run < need_eq && pos < (uint32_t)k) out[pos] = j;
-      eq_run++;
+  uint32_t pos = block_exclusive_scan(cnt, tmp, &tot);
+  for (int w = w0; w < w1; w++) {
+    uint64_t bits = ((uint64_t)bitmap[2 * w + 1] << 32) | bitmap[2 * w];
+    while (bits) {
+      const int b = __ffsll((unsigned long long)bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)k) out[pos] = w * 64 + b;
+      pos++;
     }
   }
 }
@@ -321,9 +660,19 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   const int64_t nvmax = L->len_max / L->ratio;   // visible blocks of the last query
   pl.stride = (nvmax + 63) & ~(int64_t)63;
   if (pl.stride < 64) pl.stride = 64;
-  pl.chunks = (int)((nvmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG);
-  if (pl.chunks < 1) pl.chunks = 1;
+  int64_t chunks = (nvmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
+  if (chunks < 1) chunks = 1;
+  // about kScoreTargetWGs workgroups in all, each with >= 1 chunk of one query
+  const int64_t rows = (int64_t)L->batch * n_q;
+  int64_t cpw = (rows * chunks + kScoreTargetWGs - 1) / kScoreTargetWGs;
+  const char* env = getenv("LCA_SCORE_CPW");
+  if (env && *env) cpw = atoi(env);
+  if (cpw < 1) cpw = 1;
+  if (cpw > chunks) cpw = chunks;
+  pl.cpw = (int)cpw;
+  pl.chunks = (int)((chunks + cpw - 1) / cpw);
   pl.keys_bytes = (size_t)L->batch * n_q * pl.stride * sizeof(uint32_t);
+  pl.hist_bytes = (size_t)L->batch * n_q * kHistBins * sizeof(uint32_t);
   return pl;
 }
 
@@ -341,7 +690,9 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.idx_scale = L->idx_scale;
   s.iq = iq;
   s.iw = iw;
-  s.keys = static_cast<uint32_t*>(ws);
+  s.hist = static_cast<uint32_t*>(ws);
+  s.cpw = pl.cpw;
+  s.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.hist_bytes);
   {
     TimedLaunch t(kKernelIndexerScore, stream);
     hipLaunchKernelGGL(indexer_score_kernel, dim3(pl.chunks, rows), dim3(256), 0, stream, s);
@@ -355,6 +706,7 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.stride = pl.stride;
   sa.seq_len = L->seq_len;
   sa.keys = s.keys;
+  sa.hist = s.hist;
   sa.topk = topk;
   TimedLaunch t(kKernelTopkSelect, stream);
   hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);

@@ -33,12 +33,15 @@ int set_error(int code, const char* fmt, ...);
 int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
                     const float* igate, int n, hipStream_t stream);
 
-// Indexer: scores as order-preserving uint32 keys, [rows][stride], then the
-// selection.  rows = B * n_q.
+// Indexer workspace: per-query key histograms [rows][4096] (zero between
+// calls), then scores as order-preserving uint32 keys [rows][stride].
+// rows = B * n_q.
 struct IndexerPlan {
   int64_t stride;       // keys per score row (>= visible blocks of any query)
   int chunks;           // workgroups per score row
+  int cpw;              // chunks of 1024 blocks per workgroup
   size_t keys_bytes;
+  size_t hist_bytes;    // per-query histograms at the start of the workspace
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,

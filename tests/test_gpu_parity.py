@@ -146,10 +146,13 @@ def test_indexer_topk_parity(case):
     got = got.cpu().numpy()
     want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
     # scores: the workspace holds one order key per visible block
-    ws = lay._ws[lay.seq_len.device]
+    ws = lay._ws["indexer"]
     nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
-    stride = nbytes // (4 * B * n_q)
-    keys = ws[:nbytes].view(torch.int32).cpu().numpy().view(np.uint32).reshape(B * n_q, stride)
+    hist_bytes = B * n_q * 4096 * 4
+    stride = (nbytes - hist_bytes) // (4 * B * n_q)
+    wsh = ws[:nbytes].view(torch.int32).cpu().numpy().view(np.uint32)
+    assert not wsh[: hist_bytes // 4].any()          # histograms left zeroed for the next call
+    keys = wsh[hist_bytes // 4:].reshape(B * n_q, stride)
     for b in range(B):
         for qi in range(n_q):
             sc = oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"])
@@ -179,6 +182,25 @@ def test_indexer_equal_scores_take_lowest_indices():
     want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
     assert np.array_equal(got, want)
     assert list(got[0, 0]) == list(range(k))
+
+
+def test_indexer_near_equal_scores():
+    """Most scores share their high bits (keys differ in one byte): exercises
+    the second-level candidate selection."""
+    lca = _lca()
+    say("indexer near-equal scores")
+    B, m, L, k = 2, 4, 48000, 512
+    ref = SL.make_layer(78, "neq", B, m, 128, 256, 1, L // m + 4, [L, L - 7])
+    rng = np.random.default_rng(78)
+    pattern = rng.integers(0, 256, 32).astype(np.uint8)
+    ref["idx_code"][:] = pattern
+    ref["idx_code"][:, :, 5] = rng.integers(0, 256, ref["idx_code"].shape[:2]).astype(np.uint8)
+    ref["idx_scale"][:] = 126
+    Q = SL.queries(78, "neq", B, 1, 16, 16)
+    lay = lca.Layer.from_host(ref)
+    got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k).cpu().numpy()
+    want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
+    assert np.array_equal(got, want)
 
 
 # ------------------------------------------------------------------ attention
