@@ -10,15 +10,22 @@
 //
 // All query heads of a row share one 512-d key/value vector per key, so a
 // workgroup stages each key once in LDS and 4 wavefronts x 16 heads use it.
-//   QK^T  bf16 matrix cores: a staged key holds the exact bf16 value of each
-//         e4m3 code (or the raw bf16 window token); the per-64-dim FP8 scale
-//         multiplies each 64-dim partial dot in fp32.
-//   P V   fp16 matrix cores: the staged value is fp16(code * scale) (or the
-//         window token), transposed so that the key index is the contraction
-//         dim; P is fp16 in [0, 1].
-// Online softmax in base 2 (logits pre-multiplied by log2 e).  Each workgroup
-// covers a contiguous chunk of the key list; chunks are merged by the combine
-// kernel (or written directly when there is one chunk).
+// Every product is computed transposed, keys x heads, so that a lane owns one
+// head throughout: lane l holds head l % 16 and key / channel quarter l / 16.
+//   S^T = K Q^T   bf16 matrix cores: a staged key holds the exact bf16 value of
+//                 each e4m3 code (or the raw bf16 window token); the per-64-dim
+//                 FP8 scale multiplies each 64-dim partial dot in fp32.  Lane l
+//                 ends with keys 4(l/16)+r and 16+4(l/16)+r of its head.
+//   softmax       online, base 2, per lane (one head) plus a max over the four
+//                 lanes that share the head; P stays in registers.
+//   O^T = V^T P^T fp16 matrix cores: the k-slots of the product are the eight
+//                 keys the lane already holds, so P^T is the B operand as is;
+//                 the V^T operand (fp16(code * scale) or the window token,
+//                 staged [key][channel]) comes from the LDS transpose read
+//                 ds_read_b64_tr_b16.  Lane l accumulates channels
+//                 16 ct + 4(l/16) + r of its head.
+// Each workgroup covers a contiguous chunk of the key list; chunks are merged
+// by the combine kernel (or written directly when there is one chunk).
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -29,16 +36,17 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;          // keys per tile
 constexpr int kKst = 520;          // bf16 per staged key row (512 + 8 pad)
-constexpr int kVst = 40;           // fp16 per staged value column (32 + 8 pad)
-constexpr int kPst = 40;
-constexpr int kMaxTopk = 2048;
+constexpr int kVst = 520;          // fp16 per staged value row (512 + 8 pad)
+constexpr int kMaxChunk = 1024;    // keys per split workgroup (list entries staged in LDS)
 constexpr int kAttendTargetWGs = 256;
 
 struct AttendArgs {
-  int n_q, H, m, W, R, k, splits, chunk, csa;
+  int n_q, H, m, W, R, k, splits, chunk, csa, hwaves;
   int64_t max_blocks;
   float scale_log2;
   const int32_t* seq_len;
@@ -53,69 +61,28 @@ struct AttendArgs {
   _Float16* ws_o;
 };
 
-__device__ __forceinline__ uint32_t scan_excl_256(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; w++) before += tmp[w];
-  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-  __syncthreads();
-  return before + x - v;
-}
+// Raw data of one staged (key, 64-dim group) slot, loaded one tile ahead.
+struct StageRegs {
+  uint4 d[8];       // nope: d[0..3] (64 codes); rope/window: d[0..7] (64 bf16)
+  float s;          // FP8 scale of the group (read for every slot, used for nope)
+  int kind;         // 0 padding, 1 nope group, 2 rope group of an entry, 3 window group
+};
 
 __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKst];
-  __shared__ __attribute__((aligned(16))) _Float16 Vt[kKv * kVst];
-  __shared__ float sK[kTile * 8];
-  __shared__ int kvalid[kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 Ps[4][16 * kPst];
-  __shared__ int klist[kMaxTopk];
-  __shared__ uint32_t tmp[8];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[kTile * kVst];
+  __shared__ __attribute__((aligned(16))) float sK[8 * kTile];     // [group][key]
+  __shared__ __attribute__((aligned(16))) float kbias[kTile];      // 0, or -inf for a masked key
+  __shared__ int klist[kMaxChunk];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int srow = blockIdx.y, split = blockIdx.x, hgrp = blockIdx.z;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
-  const int p = a.seq_len[brow] - a.n_q + qi;
-  int nv = (p + 1) / a.m;
-  if (nv > a.max_blocks) nv = (int)a.max_blocks;   // defensive
-  const int nw = min(a.W, p + 1);
-  const int w0 = p - nw + 1;
-
-  int n_c = nv;
-  if (a.csa) {
-    // keep listed, visible blocks in list order
-    const int32_t* sel = a.topk + (int64_t)srow * a.k;
-    const int per = (a.k + 255) / 256;          // <= 8
-    const int j0 = tid * per;
-    int ev[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) ev[u] = (u < per && j0 + u < a.k) ? sel[j0 + u] : -1;
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int u = 0; u < 8; u++) cnt += (ev[u] >= 0 && ev[u] < nv);
-    uint32_t total;
-    uint32_t pos = scan_excl_256(cnt, tmp, &total);
-#pragma unroll
-    for (int u = 0; u < 8; u++)
-      if (ev[u] >= 0 && ev[u] < nv && pos < (uint32_t)kMaxTopk) klist[pos++] = ev[u];
-    n_c = (int)total;
-    __syncthreads();
-  }
-  const int n_keys = n_c + nw;
-  const int kb = split * a.chunk;
-  const int ke = min(n_keys, kb + a.chunk);
-
   const int h0 = hgrp * 64 + wave * 16;
   const bool active = h0 < a.H;
-  const int hq = h0 + (lane & 15);            // head of this lane's A-operand row
-  const int kq = 8 * (lane >> 4);             // K offset of this lane inside a 32-K step
+  const int hq = h0 + (lane & 15);            // this lane's head
+  const int g = lane >> 4;                    // this lane's key / channel quarter
+  const int kq = 8 * g;                       // K offset of this lane inside a 32-K step
 
   v8bf qf[16];
   {
@@ -127,264 +94,308 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
       qf[ks] = __builtin_bit_cast(v8bf, v);
     }
   }
+
+  const int p = a.seq_len[brow] - a.n_q + qi;
+  int nv = (p + 1) / a.m;
+  if (nv > a.max_blocks) nv = (int)a.max_blocks;   // defensive
+  const int nw = min(a.W, p + 1);
+  const int w0 = p - nw + 1;
+  // key list: CSA = the k listed blocks (entries that are -1 or not yet
+  // visible are masked), HCA = the visible blocks; then the window tokens
+  const int n_c = a.csa ? a.k : nv;
+  const int n_keys = n_c + nw;
+  const int kb = split * a.chunk;
+  const int ke = min(n_keys, kb + a.chunk);
+  if (a.csa) {
+    for (int j = tid; j < a.chunk; j += 256) {
+      const int kk = kb + j;
+      klist[j] = kk < n_c ? a.topk[(int64_t)srow * a.k + kk] : -1;
+    }
+  }
+
   v4f O[32];
 #pragma unroll
   for (int c = 0; c < 32; c++) O[c] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.0f;
-  }
+  float mrow = -INFINITY, lrow = 0.0f;
+  __syncthreads();   // klist
 
   const int sj = tid >> 3, sg = tid & 7;      // staging: key sj, 64-dim group sg
-  for (int t0 = kb; t0 < ke; t0 += kTile) {
-    __syncthreads();
-    {
-      const int kk = t0 + sj;
-      uint16_t* kdst = Ks + sj * kKst + sg * 64;
-      if (kk < ke && kk < n_c) {
-        const int e = a.csa ? klist[kk] : kk;
-        const int64_t ent = (int64_t)brow * a.max_blocks + e;
-        if (sg < 7) {
-          const float s = a.kv_scale[ent * kScaleStride + sg];
-          const uint4* src = reinterpret_cast<const uint4*>(a.nope + ent * kNope + sg * 64);
-          uint4 cv[4];
-#pragma unroll
-          for (int v = 0; v < 4; v++) cv[v] = src[v];
-#pragma unroll
-          for (int v = 0; v < 4; v++) {
-            const uint4 c16 = cv[v];
-            const uint32_t w4[4] = {c16.x, c16.y, c16.z, c16.w};
-            uint32_t kb4[8];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++) {
-#pragma unroll
-              for (int hw = 0; hw < 2; hw++) {
-                // two codes -> exact fp32 (OCP e4m3 on gfx950), bf16 bits for K,
-                // fp16(value * scale) for V
-                const v2f f = hw ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
-                                 : __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], false);
-                kb4[q4 * 2 + hw] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
-                const v2f sv = {__fmul_rn(f[0], s), __fmul_rn(f[1], s)};
-                const v2h hv = __builtin_convertvector(sv, v2h);
-                const int c = v * 16 + q4 * 4 + hw * 2;
-                Vt[(sg * 64 + c) * kVst + sj] = hv[0];
-                Vt[(sg * 64 + c + 1) * kVst + sj] = hv[1];
-              }
-            }
-            uint4* kd = reinterpret_cast<uint4*>(kdst + v * 16);
-            kd[0] = make_uint4(kb4[0], kb4[1], kb4[2], kb4[3]);
-            kd[1] = make_uint4(kb4[4], kb4[5], kb4[6], kb4[7]);
-          }
-          sK[sj * 8 + sg] = s;
-        } else {
-          const uint4* src = reinterpret_cast<const uint4*>(a.rope + ent * kRope);
-          uint4 rv[8];
-#pragma unroll
-          for (int v = 0; v < 8; v++) rv[v] = src[v];
-#pragma unroll
-          for (int v = 0; v < 8; v++) {
-            const uint4 w = rv[v];
-            reinterpret_cast<uint4*>(kdst)[v] = w;
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++) {
-              const int c = v * 8 + q4 * 2;
-              const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
-              const v2h hv = __builtin_convertvector(f, v2h);
-              Vt[(448 + c) * kVst + sj] = hv[0];
-              Vt[(448 + c + 1) * kVst + sj] = hv[1];
-            }
-          }
-          sK[sj * 8 + 7] = 1.0f;
-        }
-      } else if (kk < ke) {
-        const int pos = w0 + (kk - n_c);
-        const uint4* src = reinterpret_cast<const uint4*>(
-            a.ring_kv + ((int64_t)brow * a.R + pos % a.R) * kKv + sg * 64);
-        uint4 rv[8];
-#pragma unroll
-        for (int v = 0; v < 8; v++) rv[v] = src[v];
-#pragma unroll
-        for (int v = 0; v < 8; v++) {
-          const uint4 w = rv[v];
-          reinterpret_cast<uint4*>(kdst)[v] = w;
-          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int q4 = 0; q4 < 4; q4++) {
-            const int c = sg * 64 + v * 8 + q4 * 2;
-            const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
-            const v2h hv = __builtin_convertvector(f, v2h);
-            Vt[c * kVst + sj] = hv[0];
-            Vt[(c + 1) * kVst + sj] = hv[1];
+  // Issue the global loads of this thread's slot of the tile at t0.  Every
+  // lane issues the same eight 16-byte loads (a masked slot reads a harmless
+  // in-bounds address, an FP8 group reads its 64 bytes twice), so the loads
+  // of one tile never wait on one another.
+  auto stage_load = [&](int t0, StageRegs& st) {
+    const int kk = t0 + sj;
+    int kind = 0;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.ring_kv);
+    const float* sp = a.kv_scale;
+    if (kk < ke) {
+      if (kk < n_c) {
+        const int e = a.csa ? klist[kk - kb] : kk;
+        if (e >= 0 && e < nv) {
+          const int64_t ent = (int64_t)brow * a.max_blocks + e;
+          if (sg < 7) {
+            src = a.nope + ent * kNope + sg * 64;
+            sp = a.kv_scale + ent * kScaleStride + sg;
+            kind = 1;
+          } else {
+            src = reinterpret_cast<const uint8_t*>(a.rope + ent * kRope);
+            kind = 2;
           }
         }
-        sK[sj * 8 + sg] = 1.0f;
       } else {
-#pragma unroll 1
-        for (int v = 0; v < 8; v++) reinterpret_cast<uint4*>(kdst)[v] = make_uint4(0, 0, 0, 0);
-#pragma unroll 1
-        for (int c = 0; c < 64; c++) Vt[(sg * 64 + c) * kVst + sj] = (_Float16)0.0f;
-        sK[sj * 8 + sg] = 0.0f;
+        const int pos = w0 + (kk - n_c);
+        src = reinterpret_cast<const uint8_t*>(a.ring_kv + ((int64_t)brow * a.R + pos % a.R) * kKv + sg * 64);
+        kind = 3;
       }
-      if (sg == 0) kvalid[sj] = kk < ke;
     }
+    const uint4* s0 = reinterpret_cast<const uint4*>(src);
+    const uint4* s1 = kind == 1 ? s0 : s0 + 4;
+#pragma unroll
+    for (int v = 0; v < 4; v++) st.d[v] = s0[v];
+#pragma unroll
+    for (int v = 0; v < 4; v++) st.d[4 + v] = s1[v];
+    st.s = *sp;
+    st.kind = kind;
+  };
+  // Convert the loaded slot into the LDS tile: K as exact bf16 values, V as
+  // fp16(value * scale), both [key][channel]; the group scale and key mask.
+  auto stage_store = [&](const StageRegs& st) {
+    uint16_t* kdst = Ks + sj * kKst + sg * 64;
+    _Float16* vdst = Vs + sj * kVst + sg * 64;
+    if (st.kind == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const uint32_t w4[4] = {st.d[v].x, st.d[v].y, st.d[v].z, st.d[v].w};
+        uint32_t kb4[8], vb4[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+#pragma unroll
+          for (int hw = 0; hw < 2; hw++) {
+            // two codes -> exact fp32 (OCP e4m3 on gfx950), bf16 bits for K,
+            // fp16(value * scale) for V
+            const v2f f = hw ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
+                             : __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], false);
+            kb4[q4 * 2 + hw] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+            const v2f sv = {__fmul_rn(f[0], st.s), __fmul_rn(f[1], st.s)};
+            vb4[q4 * 2 + hw] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sv, v2h));
+          }
+        }
+        uint4* kd = reinterpret_cast<uint4*>(kdst + v * 16);
+        kd[0] = make_uint4(kb4[0], kb4[1], kb4[2], kb4[3]);
+        kd[1] = make_uint4(kb4[4], kb4[5], kb4[6], kb4[7]);
+        uint4* vd = reinterpret_cast<uint4*>(vdst + v * 16);
+        vd[0] = make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]);
+        vd[1] = make_uint4(vb4[4], vb4[5], vb4[6], vb4[7]);
+      }
+    } else if (st.kind >= 2) {
+#pragma unroll
+      for (int v = 0; v < 8; v++) {
+        const uint4 w = st.d[v];
+        reinterpret_cast<uint4*>(kdst)[v] = w;
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        uint32_t vb4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
+          vb4[q4] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
+        }
+        reinterpret_cast<uint4*>(vdst)[v] = make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; v++) {
+        reinterpret_cast<uint4*>(kdst)[v] = make_uint4(0, 0, 0, 0);
+        reinterpret_cast<uint4*>(vdst)[v] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    sK[sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
+    // a key is valid when its first group is (every group of a key shares it)
+    if (sg == 0) kbias[sj] = st.kind ? 0.0f : -INFINITY;
+  };
+
+  // LDS transpose-read addresses of the V^T operand: k-slot j of quarter g is
+  // key 4g + j (j < 4) or 16 + 4g + (j - 4).  ds_read_b64_tr_b16 gives lane i
+  // of a 16-lane group element i % 4 of the 64-bit rows read by lanes
+  // 4j + i / 4, so lane L reads channels 16 ct + 4(L % 4) .. +3 of key
+  // 4g + L / 4 (and of key 16 + 4g + L / 4 for the second read).
+  const int Lq = lane & 15;
+  const _Float16* vrow0 = Vs + (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3);
+  const _Float16* vrow1 = vrow0 + 16 * kVst;
+
+  StageRegs st;
+  if (kb < ke) stage_load(kb, st);
+  for (int t0 = kb; t0 < ke; t0 += kTile) {
+    __syncthreads();                       // the previous tile is consumed
+    stage_store(st);
+    if (t0 + kTile < ke) stage_load(t0 + kTile, st);   // next tile in flight
     __syncthreads();
 
     if (active) {
-      // S = Q K^T for 16 heads x 32 keys, per 64-dim group scaled in fp32
+      // S^T = K Q^T for 32 keys x 16 heads, per 64-dim group scaled in fp32
       v4f S[2];
 #pragma unroll
       for (int nt = 0; nt < 2; nt++) {
         S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-        const int key = nt * 16 + (lane & 15);
-        const uint16_t* krow = Ks + key * kKst + kq;
+        const uint16_t* krow = Ks + (nt * 16 + Lq) * kKst + kq;
 #pragma unroll
-        for (int g = 0; g < 8; g++) {
+        for (int gq = 0; gq < 8; gq++) {
           v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s2 = 0; s2 < 2; s2++) {
-            const int ks = 2 * g + s2;
+            const int ks = 2 * gq + s2;
             const v8bf kb8 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(krow + ks * 32));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qf[ks], acc, 0, 0, 0);
           }
-          const float sc = sK[key * 8 + g];
+          const v4f sc = *reinterpret_cast<const v4f*>(sK + gq * kTile + nt * 16 + 4 * g);
 #pragma unroll
-          for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc, acc[r], S[nt][r]);
+          for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc[r], acc[r], S[nt][r]);
         }
       }
-      // online softmax (base 2); lane holds keys (lane&15)+{0,16}, heads 4*(lane>>4)+r
-      const bool v0 = kvalid[lane & 15], v1 = kvalid[16 + (lane & 15)];
-      float alpha[4];
+      // online softmax (base 2) of this lane's head over its eight keys
+      const v4f kb0 = *reinterpret_cast<const v4f*>(kbias + 4 * g);
+      const v4f kb1 = *reinterpret_cast<const v4f*>(kbias + 16 + 4 * g);
+      float x[8];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const float x0 = v0 ? S[0][r] * a.scale_log2 : -INFINITY;
-        const float x1 = v1 ? S[1][r] * a.scale_log2 : -INFINITY;
-        float mx = fmaxf(x0, x1);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        const float mnew = fmaxf(mrow[r], mx);
-        float p0 = 0.f, p1 = 0.f;
-        if (mnew == -INFINITY) {
-          alpha[r] = 1.0f;
-        } else {
-          alpha[r] = exp2f(mrow[r] - mnew);
-          p0 = exp2f(x0 - mnew);
-          p1 = exp2f(x1 - mnew);
-        }
-        lrow[r] = lrow[r] * alpha[r] + p0 + p1;
-        mrow[r] = mnew;
-        _Float16* prow = Ps[wave] + (4 * (lane >> 4) + r) * kPst;
-        prow[lane & 15] = (_Float16)p0;
-        prow[16 + (lane & 15)] = (_Float16)p1;
+        x[r] = S[0][r] * a.scale_log2 + kb0[r];
+        x[4 + r] = S[1][r] * a.scale_log2 + kb1[r];
       }
-      const bool rescale = (alpha[0] != 1.0f) | (alpha[1] != 1.0f) | (alpha[2] != 1.0f) | (alpha[3] != 1.0f);
-      if (__any(rescale)) {
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; j++) mx = fmaxf(mx, x[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mnew = fmaxf(mrow, mx);
+      const float mref = mnew == -INFINITY ? 0.0f : mnew;   // nothing seen yet
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
+      float ps = 0.0f;
+      v8h pb;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float pj = __builtin_amdgcn_exp2f(x[j] - mref);
+        ps += pj;
+        pb[j] = (_Float16)pj;
+      }
+      lrow = lrow * alpha + ps;
+      mrow = mnew;
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int c = 0; c < 32; c++)
 #pragma unroll
-          for (int r = 0; r < 4; r++) O[c][r] *= alpha[r];
+          for (int r = 0; r < 4; r++) O[c][r] *= alpha;
       }
-    }
-    __syncthreads();
-    if (active) {
-      const v8h pa = *reinterpret_cast<const v8h*>(Ps[wave] + (lane & 15) * kPst + kq);
+      // O^T += V^T P^T
 #pragma unroll
       for (int ct = 0; ct < 32; ct++) {
-        const v8h vb = *reinterpret_cast<const v8h*>(Vt + (ct * 16 + (lane & 15)) * kVst + kq);
-        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, O[ct], 0, 0, 0);
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * ct));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * ct));
+        const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
+        const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[ct], 0, 0, 0);
       }
     }
   }
 
   if (!active) return;
-#pragma unroll
-  for (int r = 0; r < 4; r++)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) lrow[r] += __shfl_xor(lrow[r], o, kWave);
-
-  const int hbase = h0 + 4 * (lane >> 4);
+  lrow += __shfl_xor(lrow, 16, kWave);
+  lrow += __shfl_xor(lrow, 32, kWave);
   if (a.splits == 1) {
+    if (hq < a.H) {
+      const float inv = 1.0f / lrow;
+      float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + hq) * kKv + 4 * g);
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int h = hbase + r;
-      if (h >= a.H) continue;
-      const float inv = 1.0f / lrow[r];
-      float* dst = a.out + ((int64_t)srow * a.H + h) * kKv;
-#pragma unroll
-      for (int ct = 0; ct < 32; ct++) dst[ct * 16 + (lane & 15)] = O[ct][r] * inv;
+      for (int ct = 0; ct < 32; ct++)
+        dst[ct * 4] = make_float4(O[ct][0] * inv, O[ct][1] * inv, O[ct][2] * inv, O[ct][3] * inv);
     }
   } else {
+    // partials: (m, l) per head, and this lane's 128 normalised outputs
+    // (value index ct * 4 + r) in fp16, as 16 uint4 interleaved across the wave
+    if (hq < a.H && g == 0) {
+      const int64_t slot = ((int64_t)srow * a.splits + split) * a.H + hq;
+      reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(mrow, lrow);
+    }
+    const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
+    const int64_t rec = ((int64_t)srow * a.splits + split) * a.hwaves + (hgrp * 4 + wave);
+    uint4* dst = reinterpret_cast<uint4*>(a.ws_o + rec * 8192) + lane;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int h = hbase + r;
-      if (h >= a.H) continue;
-      const int64_t slot = ((int64_t)srow * a.splits + split) * a.H + h;
-      if ((lane & 15) == 0) {
-        a.ws_ml[slot * 2 + 0] = mrow[r];
-        a.ws_ml[slot * 2 + 1] = lrow[r];
-      }
-      if (lrow[r] > 0.0f) {       // normalised partial output, fp16 (values of V's range)
-        const float inv = 1.0f / lrow[r];
-        _Float16* dst = a.ws_o + slot * kKv;
+    for (int q = 0; q < 16; q++) {
+      uint32_t w[4];
 #pragma unroll
-        for (int ct = 0; ct < 32; ct++) dst[ct * 16 + (lane & 15)] = (_Float16)(O[ct][r] * inv);
+      for (int e = 0; e < 4; e++) {
+        const int i0 = q * 8 + 2 * e;   // values i0, i0 + 1: (ct, r) = (i0 / 4, i0 % 4)
+        const v2f f = {O[i0 >> 2][i0 & 3] * inv, O[(i0 + 1) >> 2][(i0 + 1) & 3] * inv};
+        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
       }
+      dst[q * 64] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
 
 struct CombineArgs {
-  int H, splits;
+  int H, splits, hwaves;
   const float* ws_ml;
   const _Float16* ws_o;
   float* out;
 };
 
-__global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
-  const int srow = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  float M = -INFINITY;
-  float L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // splits in groups of 8: every load of a group in flight before use
+// Grid (row, wavefront of 16 heads, quarter): thread (q, lane) merges uint4 q
+// of the record that `lane` of every split wrote -- 8 values of head
+// hw * 16 + lane % 16, channels 16(2q + j / 4) + 4(lane / 16) + j % 4 -- with
+// an online rescale over batches of eight splits.
+__global__ void __launch_bounds__(256) attend_combine_kernel(CombineArgs a) {
+  const int srow = blockIdx.x, hw = blockIdx.y;
+  const int lane = threadIdx.x & 63, q = blockIdx.z * 4 + (threadIdx.x >> 6);
+  const int h = hw * 16 + (lane & 15), g = lane >> 4;
+  if (h >= a.H) return;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)srow * a.splits * a.H + h;
+  const uint4* rec0 = reinterpret_cast<const uint4*>(a.ws_o) + (int64_t)srow * a.splits * a.hwaves * 1024 +
+                      (int64_t)hw * 1024 + q * 64 + lane;
+  const int64_t rstride = (int64_t)a.hwaves * 1024;
+  float M = -INFINITY, L = 0.0f, acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = 0.0f;
   for (int s0 = 0; s0 < a.splits; s0 += 8) {
-    float mv[8], lv[8];
-    uint2 ov[8];
+    float2 mlu[8];
+    uint4 raw[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-      const int64_t slot = ((int64_t)srow * a.splits + s0 + u) * a.H + h;
-      const bool in = s0 + u < a.splits;
-      mv[u] = in ? a.ws_ml[slot * 2] : -INFINITY;
-      lv[u] = in ? a.ws_ml[slot * 2 + 1] : 0.0f;
-      ov[u] = in ? reinterpret_cast<const uint2*>(a.ws_o + slot * kKv)[t] : make_uint2(0, 0);
+      const int s = s0 + u;
+      mlu[u] = make_float2(-INFINITY, 0.0f);
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (s < a.splits) {
+        mlu[u] = ml[(int64_t)s * a.H];
+        raw[u] = rec0[s * rstride];
+      }
     }
-    float Mn = M;
+    float bm = M;
 #pragma unroll
     for (int u = 0; u < 8; u++)
-      if (lv[u] > 0.0f) Mn = fmaxf(Mn, mv[u]);
-    const float rescale = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-    L *= rescale;
-    acc.x *= rescale;
-    acc.y *= rescale;
-    acc.z *= rescale;
-    acc.w *= rescale;
-    M = Mn;
+      if (mlu[u].y > 0.0f) bm = fmaxf(bm, mlu[u].x);
+    if (bm == -INFINITY) continue;             // no split of this batch saw a key
+    const float c = __builtin_amdgcn_exp2f(M - bm);   // M = -inf -> 0
+    L *= c;
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[j] *= c;
+    M = bm;
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-      if (!(lv[u] > 0.0f)) continue;
-      const float w = lv[u] * exp2f(mv[u] - M);
+      const float w = mlu[u].y > 0.0f ? mlu[u].y * __builtin_amdgcn_exp2f(mlu[u].x - M) : 0.0f;
       L += w;
-      const v2h o01 = __builtin_bit_cast(v2h, ov[u].x), o23 = __builtin_bit_cast(v2h, ov[u].y);
-      acc.x += w * (float)o01[0];
-      acc.y += w * (float)o01[1];
-      acc.z += w * (float)o23[0];
-      acc.w += w * (float)o23[1];
+      const uint32_t ww[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const v2h v = __builtin_bit_cast(v2h, ww[e]);
+        acc[2 * e] += w * (float)v[0];
+        acc[2 * e + 1] += w * (float)v[1];
+      }
     }
   }
   const float inv = 1.0f / L;
-  reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + h) * kKv)[t] =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  float* dst = a.out + ((int64_t)srow * a.H + h) * kKv + 32 * q + 4 * g;
+  *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<float4*>(dst + 16) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
 }
 
 static int env_int(const char* name, int dflt) {
@@ -395,7 +406,7 @@ static int env_int(const char* name, int dflt) {
 AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   AttendPlan pl;
   const int64_t nvmax = L->len_max / L->ratio;
-  pl.max_keys = (csa ? (k < nvmax ? k : nvmax) : nvmax) + L->window;
+  pl.max_keys = (csa ? (int64_t)k : nvmax) + L->window;
   pl.head_groups = (H + 63) / 64;
   const int64_t rows = (int64_t)L->batch * n_q;
   const int64_t max_tiles = (pl.max_keys + kTile - 1) / kTile;
@@ -404,12 +415,14 @@ AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   if (forced > 0) s = forced;
   if (s > max_tiles) s = max_tiles;
   if (s < 1) s = 1;
-  const int64_t per = (pl.max_keys + s - 1) / s;
+  int64_t per = (pl.max_keys + s - 1) / s;
+  if (csa && per > kMaxChunk) per = kMaxChunk;
   pl.chunk = (int)(((per + kTile - 1) / kTile) * kTile);
   pl.splits = (int)((pl.max_keys + pl.chunk - 1) / pl.chunk);
   if (pl.splits > 1) {
     pl.ml_bytes = (size_t)rows * pl.splits * H * 2 * sizeof(float);
-    pl.o_bytes = (size_t)rows * pl.splits * H * kKv * sizeof(_Float16);
+    // one 128-value fp16 record per lane of every (split, wavefront of 16 heads)
+    pl.o_bytes = (size_t)rows * pl.splits * (pl.head_groups * 4) * 8192 * sizeof(_Float16);
   } else {
     pl.ml_bytes = pl.o_bytes = 0;
   }
@@ -428,6 +441,7 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   a.splits = pl.splits;
   a.chunk = pl.chunk;
   a.csa = topk != nullptr;
+  a.hwaves = pl.head_groups * 4;
   a.max_blocks = L->max_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.seq_len = L->seq_len;
@@ -451,11 +465,12 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
     CombineArgs c;
     c.H = H;
     c.splits = pl.splits;
+    c.hwaves = a.hwaves;   // record stride: every wavefront slot of the attention grid
     c.ws_ml = a.ws_ml;
     c.ws_o = a.ws_o;
     c.out = out;
     TimedLaunch t(kKernelAttendCombine, stream);
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, H), dim3(128), 0, stream, c);
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, (H + 15) / 16, 4), dim3(256), 0, stream, c);
     return t.done();
   }
   return LCA_OK;
