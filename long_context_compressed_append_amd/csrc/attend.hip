@@ -40,8 +40,12 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;          // keys per tile
+// Row pitches: a K row is 1040 bytes (16 mod 256), so 16 lanes writing or
+// reading one 16-byte chunk of 16 consecutive keys hit distinct banks; a V row
+// is 1056 bytes (32 mod 256), so the 8-byte transpose reads of 8 keys x 4
+// chunks by 32 lanes cover all banks once.
 constexpr int kKst = 520;          // bf16 per staged key row (512 + 8 pad)
-constexpr int kVst = 520;          // fp16 per staged value row (512 + 8 pad)
+constexpr int kVst = 528;          // fp16 per staged value row (512 + 16 pad)
 constexpr int kMaxChunk = 1024;    // keys per split workgroup (list entries staged in LDS)
 constexpr int kAttendTargetWGs = 256;
 
@@ -119,7 +123,8 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   float mrow = -INFINITY, lrow = 0.0f;
   __syncthreads();   // klist
 
-  const int sj = tid >> 3, sg = tid & 7;      // staging: key sj, 64-dim group sg
+  // staging: key sj, 64-dim group sg; a wavefront stages two groups of 32 keys
+  const int sj = tid & 31, sg = tid >> 5;
   // Issue the global loads of this thread's slot of the tile at t0.  Every
   // lane issues the same eight 16-byte loads (a masked slot reads a harmless
   // in-bounds address, an FP8 group reads its 64 bytes twice), so the loads
