@@ -9,21 +9,26 @@
 // tokens stay at raw precision; entries are FP8 with BF16 RoPE dims.
 //
 // All query heads of a row share one 512-d key/value vector per key, so a
-// workgroup stages each key once in LDS and 4 wavefronts x 16 heads use it.
+// workgroup stages each key once in LDS and 8 wavefronts use it: wavefront w
+// takes heads 16(w % 4) .. +15 of its head group and channel half w / 4.
 // Every product is computed transposed, keys x heads, so that a lane owns one
 // head throughout: lane l holds head l % 16 and key / channel quarter l / 16.
-//   S^T = K Q^T   bf16 matrix cores: a staged key holds the exact bf16 value of
-//                 each e4m3 code (or the raw bf16 window token); the per-64-dim
-//                 FP8 scale multiplies each 64-dim partial dot in fp32.  Lane l
-//                 ends with keys 4(l/16)+r and 16+4(l/16)+r of its head.
+//   S^T = K Q^T   bf16 matrix cores over the wavefront's 256 channels: a
+//                 staged key holds the exact bf16 value of each e4m3 code (or
+//                 the raw bf16 window token); the per-64-dim FP8 scale
+//                 multiplies each 64-dim partial dot in fp32.  The two halves
+//                 add their partial scores through LDS.  Lane l ends with keys
+//                 4(l/16)+r and 16+4(l/16)+r of its head.
 //   softmax       online, base 2, per lane (one head) plus a max over the four
-//                 lanes that share the head; P stays in registers.
+//                 lanes that share the head; the running maximum is only
+//                 moved when it grows by more than 2^8, so rescaling is rare
+//                 and P (<= 256) stays in registers as fp16.
 //   O^T = V^T P^T fp16 matrix cores: the k-slots of the product are the eight
 //                 keys the lane already holds, so P^T is the B operand as is;
 //                 the V^T operand (fp16(code * scale) or the window token,
 //                 staged [key][channel]) comes from the LDS transpose read
 //                 ds_read_b64_tr_b16.  Lane l accumulates channels
-//                 16 ct + 4(l/16) + r of its head.
+//                 16 ct + 4(l/16) + r of its head for the 16 ct of its half.
 // Each workgroup covers a contiguous chunk of the key list; chunks are merged
 // by the combine kernel (or written directly when there is one chunk).
 #include "lca_device.h"
@@ -65,34 +70,39 @@ struct AttendArgs {
   _Float16* ws_o;
 };
 
-// Raw data of one staged (key, 64-dim group) slot, loaded one tile ahead.
+constexpr int kThreads = 512;
+constexpr float kLazyMax = 8.0f;   // log2 headroom of the running maximum
+
+// Raw data of one staged (key, 32-dim half group) slot, loaded one tile ahead.
 struct StageRegs {
-  uint4 d[8];       // nope: d[0..3] (64 codes); rope/window: d[0..7] (64 bf16)
+  uint4 d[4];       // nope: d[0..1] (32 codes); rope/window: d[0..3] (32 bf16)
   float s;          // FP8 scale of the group (read for every slot, used for nope)
   int kind;         // 0 padding, 1 nope group, 2 rope group of an entry, 3 window group
 };
 
-__global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
+__global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKst];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[kTile * kVst];
   __shared__ __attribute__((aligned(16))) float sK[8 * kTile];     // [group][key]
   __shared__ __attribute__((aligned(16))) float kbias[kTile];      // 0, or -inf for a masked key
+  __shared__ __attribute__((aligned(16))) float Sx[8 * 64 * 8];    // partial scores per wave / lane
   __shared__ int klist[kMaxChunk];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hw = wave & 3, half = wave >> 2;  // head wavefront, channel half
   const int srow = blockIdx.y, split = blockIdx.x, hgrp = blockIdx.z;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
-  const int h0 = hgrp * 64 + wave * 16;
+  const int h0 = hgrp * 64 + hw * 16;
   const bool active = h0 < a.H;
   const int hq = h0 + (lane & 15);            // this lane's head
   const int g = lane >> 4;                    // this lane's key / channel quarter
   const int kq = 8 * g;                       // K offset of this lane inside a 32-K step
 
-  v8bf qf[16];
+  v8bf qf[8];   // q of this lane's head, channels 256 half + 32 ks + 8 g .. +7
   {
-    const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv;
+    const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv + 256 * half;
 #pragma unroll
-    for (int ks = 0; ks < 16; ks++) {
+    for (int ks = 0; ks < 8; ks++) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (active && hq < a.H) v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + kq);
       qf[ks] = __builtin_bit_cast(v8bf, v);
@@ -111,79 +121,81 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   const int kb = split * a.chunk;
   const int ke = min(n_keys, kb + a.chunk);
   if (a.csa) {
-    for (int j = tid; j < a.chunk; j += 256) {
+    for (int j = tid; j < a.chunk; j += kThreads) {
       const int kk = kb + j;
       klist[j] = kk < n_c ? a.topk[(int64_t)srow * a.k + kk] : -1;
     }
   }
 
-  v4f O[32];
+  v4f O[16];
 #pragma unroll
-  for (int c = 0; c < 32; c++) O[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 16; c++) O[c] = (v4f){0.f, 0.f, 0.f, 0.f};
   float mrow = -INFINITY, lrow = 0.0f;
   __syncthreads();   // klist
 
-  // staging: key sj, 64-dim group sg; a wavefront stages two groups of 32 keys
-  const int sj = tid & 31, sg = tid >> 5;
+  // staging: key sj, 64-dim group sg, 32-dim part sp; wavefront w stages
+  // group w of 32 keys (so a wavefront's slots are all of one kind)
+  const int sj = lane & 31, sg = wave, sp = lane >> 5;
   // Issue the global loads of this thread's slot of the tile at t0.  Every
-  // lane issues the same eight 16-byte loads (a masked slot reads a harmless
-  // in-bounds address, an FP8 group reads its 64 bytes twice), so the loads
+  // lane issues the same four 16-byte loads (a masked slot reads a harmless
+  // in-bounds address, an FP8 part reads its 32 bytes twice), so the loads
   // of one tile never wait on one another.
   auto stage_load = [&](int t0, StageRegs& st) {
     const int kk = t0 + sj;
     int kind = 0;
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.ring_kv);
-    const float* sp = a.kv_scale;
+    const float* scp = a.kv_scale;
     if (kk < ke) {
       if (kk < n_c) {
         const int e = a.csa ? klist[kk - kb] : kk;
         if (e >= 0 && e < nv) {
           const int64_t ent = (int64_t)brow * a.max_blocks + e;
           if (sg < 7) {
-            src = a.nope + ent * kNope + sg * 64;
-            sp = a.kv_scale + ent * kScaleStride + sg;
+            src = a.nope + ent * kNope + sg * 64 + sp * 32;
+            scp = a.kv_scale + ent * kScaleStride + sg;
             kind = 1;
           } else {
-            src = reinterpret_cast<const uint8_t*>(a.rope + ent * kRope);
+            src = reinterpret_cast<const uint8_t*>(a.rope + ent * kRope + sp * 32);
             kind = 2;
           }
         }
       } else {
         const int pos = w0 + (kk - n_c);
-        src = reinterpret_cast<const uint8_t*>(a.ring_kv + ((int64_t)brow * a.R + pos % a.R) * kKv + sg * 64);
+        src = reinterpret_cast<const uint8_t*>(a.ring_kv + ((int64_t)brow * a.R + pos % a.R) * kKv +
+                                               sg * 64 + sp * 32);
         kind = 3;
       }
     }
     const uint4* s0 = reinterpret_cast<const uint4*>(src);
-    const uint4* s1 = kind == 1 ? s0 : s0 + 4;
+    const uint4* s1 = kind == 1 ? s0 : s0 + 2;
 #pragma unroll
-    for (int v = 0; v < 4; v++) st.d[v] = s0[v];
+    for (int v = 0; v < 2; v++) st.d[v] = s0[v];
 #pragma unroll
-    for (int v = 0; v < 4; v++) st.d[4 + v] = s1[v];
-    st.s = *sp;
+    for (int v = 0; v < 2; v++) st.d[2 + v] = s1[v];
+    st.s = *scp;
     st.kind = kind;
   };
   // Convert the loaded slot into the LDS tile: K as exact bf16 values, V as
   // fp16(value * scale), both [key][channel]; the group scale and key mask.
   auto stage_store = [&](const StageRegs& st) {
-    uint16_t* kdst = Ks + sj * kKst + sg * 64;
-    _Float16* vdst = Vs + sj * kVst + sg * 64;
+    uint16_t* kdst = Ks + sj * kKst + sg * 64 + sp * 32;
+    _Float16* vdst = Vs + sj * kVst + sg * 64 + sp * 32;
     if (st.kind == 1) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
+      for (int v = 0; v < 2; v++) {
         const uint32_t w4[4] = {st.d[v].x, st.d[v].y, st.d[v].z, st.d[v].w};
         uint32_t kb4[8], vb4[8];
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
 #pragma unroll
-          for (int hw = 0; hw < 2; hw++) {
+          for (int hh = 0; hh < 2; hh++) {
             // two codes -> exact fp32 (OCP e4m3 on gfx950), bf16 bits for K,
             // fp16(value * scale) for V
-            const v2f f = hw ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
+            const v2f f = hh ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
                              : __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], false);
-            kb4[q4 * 2 + hw] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+            kb4[q4 * 2 + hh] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
             const v2f sv = {__fmul_rn(f[0], st.s), __fmul_rn(f[1], st.s)};
-            vb4[q4 * 2 + hw] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sv, v2h));
+            vb4[q4 * 2 + hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sv, v2h));
           }
         }
         uint4* kd = reinterpret_cast<uint4*>(kdst + v * 16);
@@ -195,7 +207,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
       }
     } else if (st.kind >= 2) {
 #pragma unroll
-      for (int v = 0; v < 8; v++) {
+      for (int v = 0; v < 4; v++) {
         const uint4 w = st.d[v];
         reinterpret_cast<uint4*>(kdst)[v] = w;
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -209,14 +221,14 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
       }
     } else {
 #pragma unroll
-      for (int v = 0; v < 8; v++) {
+      for (int v = 0; v < 4; v++) {
         reinterpret_cast<uint4*>(kdst)[v] = make_uint4(0, 0, 0, 0);
         reinterpret_cast<uint4*>(vdst)[v] = make_uint4(0, 0, 0, 0);
       }
     }
-    sK[sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
+    if (sp == 0) sK[sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
     // a key is valid when its first group is (every group of a key shares it)
-    if (sg == 0) kbias[sj] = st.kind ? 0.0f : -INFINITY;
+    if (sg == 0 && sp == 0) kbias[sj] = st.kind ? 0.0f : -INFINITY;
   };
 
   // LDS transpose-read addresses of the V^T operand: k-slot j of quarter g is
@@ -225,8 +237,10 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   // 4j + i / 4, so lane L reads channels 16 ct + 4(L % 4) .. +3 of key
   // 4g + L / 4 (and of key 16 + 4g + L / 4 for the second read).
   const int Lq = lane & 15;
-  const _Float16* vrow0 = Vs + (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3);
+  const _Float16* vrow0 = Vs + (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3) + 256 * half;
   const _Float16* vrow1 = vrow0 + 16 * kVst;
+  float* sx_mine = Sx + (wave * 64 + lane) * 8;
+  const float* sx_other = Sx + ((wave ^ 4) * 64 + lane) * 8;
 
   StageRegs st;
   if (kb < ke) stage_load(kb, st);
@@ -236,70 +250,83 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
     if (t0 + kTile < ke) stage_load(t0 + kTile, st);   // next tile in flight
     __syncthreads();
 
-    if (active) {
-      // S^T = K Q^T for 32 keys x 16 heads, per 64-dim group scaled in fp32
-      v4f S[2];
+    // partial S^T = K Q^T over this half's channels, 32 keys x 16 heads,
+    // per 64-dim group scaled in fp32
+    v4f S[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++) {
-        S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = Ks + (nt * 16 + Lq) * kKst + kq;
+    for (int nt = 0; nt < 2; nt++) {
+      S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = Ks + (nt * 16 + Lq) * kKst + kq + 256 * half;
 #pragma unroll
-        for (int gq = 0; gq < 8; gq++) {
-          v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int gl = 0; gl < 4; gl++) {
+        v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s2 = 0; s2 < 2; s2++) {
-            const int ks = 2 * gq + s2;
-            const v8bf kb8 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(krow + ks * 32));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qf[ks], acc, 0, 0, 0);
-          }
-          const v4f sc = *reinterpret_cast<const v4f*>(sK + gq * kTile + nt * 16 + 4 * g);
-#pragma unroll
-          for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc[r], acc[r], S[nt][r]);
+        for (int s2 = 0; s2 < 2; s2++) {
+          const int ks = 2 * gl + s2;
+          const v8bf kb8 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(krow + ks * 32));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qf[ks], acc, 0, 0, 0);
         }
+        const v4f sc = *reinterpret_cast<const v4f*>(sK + (4 * half + gl) * kTile + nt * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc[r], acc[r], S[nt][r]);
       }
-      // online softmax (base 2) of this lane's head over its eight keys
-      const v4f kb0 = *reinterpret_cast<const v4f*>(kbias + 4 * g);
-      const v4f kb1 = *reinterpret_cast<const v4f*>(kbias + 16 + 4 * g);
-      float x[8];
+    }
+    reinterpret_cast<v4f*>(sx_mine)[0] = S[0];
+    reinterpret_cast<v4f*>(sx_mine)[1] = S[1];
+    __syncthreads();
+    {
+      const v4f o0 = reinterpret_cast<const v4f*>(sx_other)[0];
+      const v4f o1 = reinterpret_cast<const v4f*>(sx_other)[1];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        x[r] = S[0][r] * a.scale_log2 + kb0[r];
-        x[4 + r] = S[1][r] * a.scale_log2 + kb1[r];
+        S[0][r] += o0[r];   // fp32 addition commutes: both halves get the same sum
+        S[1][r] += o1[r];
       }
-      float mx = x[0];
+    }
+    // online softmax (base 2) of this lane's head over its eight keys
+    const v4f kb0 = *reinterpret_cast<const v4f*>(kbias + 4 * g);
+    const v4f kb1 = *reinterpret_cast<const v4f*>(kbias + 16 + 4 * g);
+    float x[8];
 #pragma unroll
-      for (int j = 1; j < 8; j++) mx = fmaxf(mx, x[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    for (int r = 0; r < 4; r++) {
+      x[r] = S[0][r] * a.scale_log2 + kb0[r];
+      x[4 + r] = S[1][r] * a.scale_log2 + kb1[r];
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) mx = fmaxf(mx, x[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // move the reference only when the tile's maximum exceeds it by more
+    // than the headroom (always on the first key seen)
+    if (__any(mx > mrow + kLazyMax)) {
       const float mnew = fmaxf(mrow, mx);
-      const float mref = mnew == -INFINITY ? 0.0f : mnew;   // nothing seen yet
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
-      float ps = 0.0f;
-      v8h pb;
+      // first key seen: 0 (O and l are still 0); unchanged reference: 1
+      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mrow - mnew);
+      lrow *= alpha;
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float pj = __builtin_amdgcn_exp2f(x[j] - mref);
-        ps += pj;
-        pb[j] = (_Float16)pj;
-      }
-      lrow = lrow * alpha + ps;
+      for (int c = 0; c < 16; c++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) O[c][r] *= alpha;
       mrow = mnew;
-      if (__any(alpha != 1.0f)) {
+    }
+    const float mref = mrow == -INFINITY ? 0.0f : mrow;          // no key seen yet
+    v8h pb;
 #pragma unroll
-        for (int c = 0; c < 32; c++)
+    for (int j = 0; j < 8; j++) {
+      const float pj = __builtin_amdgcn_exp2f(x[j] - mref);
+      lrow += pj;
+      pb[j] = (_Float16)pj;
+    }
+    // O^T += V^T P^T over this half's 16 channel tiles
 #pragma unroll
-          for (int r = 0; r < 4; r++) O[c][r] *= alpha;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int ct = 0; ct < 32; ct++) {
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * ct));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * ct));
-        const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
-        const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
-        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[ct], 0, 0, 0);
-      }
+    for (int c = 0; c < 16; c++) {
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
+      const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
+      const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
     }
   }
 
@@ -309,27 +336,28 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   if (a.splits == 1) {
     if (hq < a.H) {
       const float inv = 1.0f / lrow;
-      float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + hq) * kKv + 4 * g);
+      float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + hq) * kKv + 256 * half + 4 * g);
 #pragma unroll
-      for (int ct = 0; ct < 32; ct++)
-        dst[ct * 4] = make_float4(O[ct][0] * inv, O[ct][1] * inv, O[ct][2] * inv, O[ct][3] * inv);
+      for (int c = 0; c < 16; c++)
+        dst[c * 4] = make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
     }
   } else {
-    // partials: (m, l) per head, and this lane's 128 normalised outputs
-    // (value index ct * 4 + r) in fp16, as 16 uint4 interleaved across the wave
-    if (hq < a.H && g == 0) {
+    // partials: (m, l) per head, and this lane's normalised outputs in fp16:
+    // value index ct * 4 + r of the head's 128 per lane, as 16 uint4 per lane
+    // interleaved across the wave; this half writes uint4 8 half .. +7
+    if (hq < a.H && g == 0 && half == 0) {
       const int64_t slot = ((int64_t)srow * a.splits + split) * a.H + hq;
       reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(mrow, lrow);
     }
     const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
-    const int64_t rec = ((int64_t)srow * a.splits + split) * a.hwaves + (hgrp * 4 + wave);
-    uint4* dst = reinterpret_cast<uint4*>(a.ws_o + rec * 8192) + lane;
+    const int64_t rec = ((int64_t)srow * a.splits + split) * a.hwaves + (hgrp * 4 + hw);
+    uint4* dst = reinterpret_cast<uint4*>(a.ws_o + rec * 8192) + (8 * half) * 64 + lane;
 #pragma unroll
-    for (int q = 0; q < 16; q++) {
+    for (int q = 0; q < 8; q++) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int i0 = q * 8 + 2 * e;   // values i0, i0 + 1: (ct, r) = (i0 / 4, i0 % 4)
+        const int i0 = q * 8 + 2 * e;   // values i0, i0 + 1 of this half: (c, r) = (i0 / 4, i0 % 4)
         const v2f f = {O[i0 >> 2][i0 & 3] * inv, O[(i0 + 1) >> 2][(i0 + 1) & 3] * inv};
         w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
       }
@@ -462,7 +490,7 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   const int rows = L->batch * n_q;
   {
     TimedLaunch t(kKernelAttend, stream);
-    hipLaunchKernelGGL(attend_kernel, dim3(pl.splits, rows, pl.head_groups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attend_kernel, dim3(pl.splits, rows, pl.head_groups), dim3(kThreads), 0, stream, a);
     int rc = t.done();
     if (rc) return rc;
   }
