@@ -114,6 +114,45 @@ def cpu_baseline(wl, ref, Q, tokens):
                        f"{B} rows at full context, {dt:.2f}s wall")
 
 
+def counter_traffic(dominant, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a plain copy), or None when the
+    summary is missing or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{dominant}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        nbytes = int(fields["traffic_bytes_per_launch"])
+        src_name, src_hash = fields["traffic_source"].split()
+    except (KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "long_context_compressed_append_amd", "csrc", src_name)
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != src_hash:
+        return None
+    return nbytes
+
+
+def calibrate_copy(mib):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+    factor between the counters and the bytes a kernel really moves."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,7 +162,13 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across "
               "GPUs with no exchange; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
@@ -301,7 +346,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(dominant, args.workload),
             "kernel_avg_us": round(kernel_ms * 1e3, 3),
             "bytes_per_launch": dom_bytes,
         },
