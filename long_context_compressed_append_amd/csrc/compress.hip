@@ -189,23 +189,19 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
       }
     }
   }
-  // The last workgroup to finish advances every row's length.  All reads of
-  // seq_len by a workgroup happen before its counter increment.
+  // The last workgroup to finish advances every row's length.  The barrier
+  // completes every load of this workgroup (seq_len included) before its
+  // counter increment, so no workgroup reads a length after it was advanced.
+  // Nothing else written here is read by another workgroup of this launch,
+  // so no memory fence is needed (a device-scope fence would write back and
+  // invalidate a whole L2); the next launch sees every write.
   __shared__ uint32_t is_last;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    is_last = atomicAdd(a.sync, 1u) == gridDim.x - 1;
-  }
+  if (threadIdx.x == 0) is_last = atomicAdd(a.sync, 1u) == gridDim.x - 1;
   __syncthreads();
   if (is_last) {
-    __threadfence();
     for (int r = threadIdx.x; r < a.B; r += blockDim.x) a.seq_len[r] += a.n;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      atomicExch(a.sync, 0u);
-      __threadfence();
-    }
+    if (threadIdx.x == 0) atomicExch(a.sync, 0u);
   }
 }
 

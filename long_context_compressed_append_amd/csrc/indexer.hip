@@ -103,15 +103,11 @@ __device__ __noinline__ float score_unscaled(v8i A0, v8i A1, v8i Bm, int hgroups
 __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   const int srow = blockIdx.y;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
-  const int p = a.seq_len[brow] - a.n_q + qi;
-  int64_t nv = (int64_t)(p + 1) / a.m;
-  if (nv > a.stride) nv = a.stride;            // defensive: never past the key row
-  if (nv > a.max_blocks) nv = a.max_blocks;
-  // this workgroup's chunks of 1024 blocks: [c0, c1)
-  const int64_t nchunks = (nv + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
+  // This workgroup's chunks of 1024 blocks are [c0, c0 + cpw).  The key loads
+  // are issued before the row length arrives: any block below the key row
+  // capacity is readable, and blocks past the visible count are masked later.
   const int64_t c0 = (int64_t)blockIdx.x * a.cpw;
-  const int64_t c1 = c0 + a.cpw < nchunks ? c0 + a.cpw : nchunks;
-  if (c0 >= c1) return;
+  const int64_t cap = a.stride < a.max_blocks ? a.stride : a.max_blocks;
 
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
@@ -125,30 +121,20 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   // The wave walks iterations i = 0 .. n_it-1 of 32 blocks each: iteration i
   // is group i % 8 of this wave's 256 blocks in chunk c0 + i / 8.  Keys are
   // loaded kDepth iterations ahead of their use.
-  const int n_it = (int)(c1 - c0) * kScoreItersPerWave;
+  const int n_it = a.cpw * kScoreItersPerWave;
   auto blk_of = [&](int i) -> int64_t {
     return (c0 + i / kScoreItersPerWave) * kScoreBlocksPerWG +
            (int64_t)wave * (kScoreItersPerWave * kScoreBlocksPerIter) +
            (i % kScoreItersPerWave) * kScoreBlocksPerIter + r;
   };
+  // Loads are unconditional (a block past the capacity reads block 0) so that
+  // no load waits on another; compute() masks what they return.
   auto load = [&](int i, int4& kr, uint32_t& er) {
     const int64_t blk = blk_of(i);
-    kr = make_int4(0, 0, 0, 0);
-    er = 0x7F7Fu;
-    if (i < n_it && blk < nv) {
-      kr = *reinterpret_cast<const int4*>(kc + blk * 32 + 16 * kh);
-      er = *reinterpret_cast<const uint16_t*>(ks + blk * 2);
-    }
+    const int64_t b = (i < n_it && blk < cap) ? blk : 0;
+    kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
+    er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
   };
-  // two blocks of kDepth iterations in flight
-  int4 kA[kDepth], kB[kDepth];
-  uint32_t eA[kDepth], eB[kDepth];
-#pragma unroll
-  for (int u = 0; u < kDepth; u++) {
-    load(u, kA[u], eA[u]);
-    load(kDepth + u, kB[u], eB[u]);
-  }
-
   // query values and weights: all loads in flight before any is used
   const float* qsrc = a.iq + (int64_t)srow * a.H * kIdx;
   float qv[8];
@@ -158,6 +144,22 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
     qv[u] = e < a.H * kIdx ? qsrc[e] : 0.0f;
   }
   const float wq = tid < a.H ? a.iw[(int64_t)srow * a.H + tid] : 0.0f;
+  // Key loads go out after the query's: the loads complete in issue order, so
+  // the query quantisation below does not wait for the keys.
+  // two blocks of kDepth iterations in flight
+  int4 kA[kDepth], kB[kDepth];
+  uint32_t eA[kDepth], eB[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; u++) {
+    load(u, kA[u], eA[u]);
+    load(kDepth + u, kB[u], eB[u]);
+  }
+  // the row length through the scalar cache, once every vector load is out
+  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+  const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
+  int64_t nv = (int64_t)(p + 1) / a.m;
+  if (nv > cap) nv = cap;                      // defensive: never past the key row
+
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
   // MXFP4 quantisation of the query, one 32-lane half-wave per MX block.
 #pragma unroll
@@ -211,9 +213,17 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
       const int h = 16 * hg + 8 * kh + hl;
       wv[hg][hl] = h < a.H ? q_w[h] : 0.0f;
     }
-  for (int h = 0; h < a.H; h++) {
-    qmin = min(qmin, min(q_exp[h][0], q_exp[h][1]));
-    qmax = max(qmax, max(q_exp[h][0], q_exp[h][1]));
+  {
+    // extremes of the query's 2H block exponents: lane l looks at entry l
+    const int e = lane < 2 * a.H ? q_exp[lane >> 1][lane & 1] : 0;
+    int lo = lane < 2 * a.H ? e : (1 << 20), hi = lane < 2 * a.H ? e : -(1 << 20);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      lo = min(lo, __shfl_xor(lo, o, kWave));
+      hi = max(hi, __shfl_xor(hi, o, kWave));
+    }
+    qmin = lo;
+    qmax = hi;
   }
 
   uint32_t* out = a.keys + (int64_t)srow * a.stride;
@@ -221,11 +231,14 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 
   // kDepth iterations at once: their matrix-core products and head chains are
   // independent, so they interleave; one range check covers the block.
-  auto compute = [&](int i0, const int4 (&kr)[kDepth], const uint32_t (&er)[kDepth]) {
+  auto compute = [&](int i0, const int4 (&kr)[kDepth], const uint32_t (&er_in)[kDepth]) {
     int ke0[kDepth], ke1[kDepth], sb[kDepth];
+    uint32_t er[kDepth];
     bool ok = true;
 #pragma unroll
     for (int u = 0; u < kDepth; u++) {
+      // a block that is not scored takes unit scales (its result is dropped)
+      er[u] = blk_of(i0 + u) < nv ? er_in[u] : 0x7F7Fu;
       ke0[u] = (int)(er[u] & 0xFF) - 127;
       ke1[u] = (int)(er[u] >> 8) - 127;
       sb[u] = kh ? (ke1[u] + 127) : (ke0[u] + 127);
