@@ -312,21 +312,22 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-k by (score desc, block asc) for one query per workgroup.
-//   1. The query's histogram (top 12 key bits) gives the bin tb holding the
-//      k-th largest key and the count `above` of keys in higher bins; the
-//      histogram is zeroed for the next call.
-//   2. Pass over the keys: a ballot per 64 blocks writes the bitmap of keys
-//      above tb.  Keys inside tb either go straight to an LDS candidate list
-//      (when the bin is small) or are histogrammed on their next 12 bits, and
-//      a second pass marks those above the sub-bin and lists those inside it.
-//   3. A radix select over the candidate list finds the exact threshold key T;
-//      candidates above T are marked, and among keys equal to T the lowest
-//      block indices are taken.
+// Exact top-k by (score desc, block asc) for one query per workgroup of 512
+// threads.  In every round of 32768 blocks, thread t owns the two bitmap
+// words of blocks 64t .. 64t+63 of the round.
+//   1. The query's histogram of the top 12 key bits (built while scoring)
+//      gives the bin tb holding the k-th largest key and the count `above` of
+//      keys in higher bins; the histogram is zeroed for the next call.
+//   2. Each thread compares its 32 keys with tb: keys above tb set their bit,
+//      keys inside tb are listed in LDS in block order (a block-wide scan
+//      places every thread's keys).
+//   3. Two radix passes of 10 bits over the listed keys give the exact
+//      threshold key T and how many keys equal to T are taken; listed keys
+//      above T set their bit, and keys equal to T are ranked by block index
+//      with a scan over the list, which is in block order.
 //   4. The bitmap is compacted into ascending block indices.
-// If even the second-level bin overflows the list (many nearly equal
-// scores), a radix select runs over all keys and the equal keys are ranked
-// by block index with a scan.
+// If more than kCandCap keys share tb (many nearly equal scores), a radix
+// select over all keys replaces steps 2-3.
 // ---------------------------------------------------------------------------
 
 struct SelectArgs {
@@ -338,12 +339,15 @@ struct SelectArgs {
   int32_t* topk;
 };
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRoundKeys = 64 * kSelThreads;   // blocks per round
 constexpr int kCandCap = 4096;
 constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
 static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
 
-// exclusive prefix sum over the 1024 threads; returns the block total in *total
+// exclusive prefix sum over the kSelThreads threads; returns the block total
+// in *total (tmp >= 32 words)
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
@@ -354,18 +358,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   }
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < 16 ? tmp[lane] : 0u;
+  uint32_t before_wave = 0, all = 0;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      uint32_t y = __shfl_up(t, o, kWave);
-      if (lane >= o) t += y;
-    }
-    if (lane < 16) tmp[16 + lane] = t;   // inclusive wave prefix
+  for (int w = 0; w < kSelWaves; w++) {
+    const uint32_t t = tmp[w];
+    before_wave += w < wave ? t : 0u;
+    all += t;
   }
-  __syncthreads();
-  const uint32_t before_wave = wave ? tmp[16 + wave - 1] : 0u;
-  *total = tmp[16 + 15];
+  *total = all;
   __syncthreads();
   return before_wave + x - v;
 }
@@ -395,19 +395,20 @@ __device__ __noinline__ void find_bin(const uint32_t* hist, uint32_t nb, uint32_
   __syncthreads();
 }
 
-// Visit the row's keys in 64-key words: wave w takes words w, w+16, ...; the
-// keys of 16 words are loaded before any is used, so the loads overlap.
+// Visit the row's keys in 64-key words from word w_start on: wave w takes
+// words w_start + w, + 16, ...; the keys of 8 words are loaded before any is
+// used, so the loads overlap.
 template <typename F>
-__device__ __forceinline__ void for_each_word(const uint32_t* keys, int nv, int nwords, F f) {
+__device__ __forceinline__ void for_each_word(const uint32_t* keys, int nv, int nwords, F f, int w_start = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kBatch = 8;
 #pragma unroll 1
-  for (int wb = wave; wb < nwords; wb += kBatch * (kSelThreads / 64)) {
+  for (int wb = w_start + wave; wb < nwords; wb += kBatch * (kSelThreads / 64)) {
     uint32_t kk[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; u++) {
       const int j = (wb + u * (kSelThreads / 64)) * 64 + lane;
-      kk[u] = j < nv ? keys[j] : 0u;
+      kk[u] = keys[j < nv ? j : 0];      // past the count: ignored by f (j >= nv)
     }
 #pragma unroll
     for (int u = 0; u < kBatch; u++) {
@@ -421,55 +422,21 @@ __device__ __forceinline__ void set_bit(uint32_t* bitmap, uint32_t j) {
   atomicOr(&bitmap[j >> 5], 1u << (j & 31));
 }
 
-// Marks the `need` best of nc listed candidates (key desc, block asc); all
-// candidates share the key bits above bit `shift`.
-__device__ __noinline__ void select_candidates(uint32_t nc, uint32_t need, int shift, const uint32_t* ck,
-                                  const uint32_t* ci, uint32_t* hist, uint32_t* tmp,
-                                  uint32_t* found, uint32_t* bitmap) {
-  const int tid = threadIdx.x;
-  uint32_t pfx = shift < 32 ? (ck[0] >> shift) : 0u;
-  while (shift > 0) {
-    const int width = shift >= 12 ? 12 : shift;
-    const int lo = shift - width;
-    const uint32_t nb = 1u << width;
-    for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < nc; i += kSelThreads) {
-      const uint32_t key = ck[i];
-      if ((key >> shift) == pfx) atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin(hist, nb, need, tmp, found);
-    need -= found[1];
-    pfx = (pfx << width) | found[0];
-    shift = lo;
-    __syncthreads();
-  }
-  const uint32_t T = pfx, need_eq = need;
-  // candidates above T are in; those equal to T are listed (hist is free now)
-  uint32_t* eq = hist;
-  if (tid == 0) found[3] = 0;
-  __syncthreads();
-  for (uint32_t i = tid; i < nc; i += kSelThreads) {
-    const uint32_t key = ck[i];
-    if (key > T) {
-      set_bit(bitmap, ci[i]);
-    } else if (key == T) {
-      const uint32_t pos = atomicAdd(&found[3], 1u);
-      eq[pos] = ci[i];
-    }
-  }
-  __syncthreads();
-  const uint32_t ne = found[3];
-  // ties at T (rare): the need_eq lowest block indices
-  for (uint32_t i = tid; i < ne; i += kSelThreads) {
-    const uint32_t me = eq[i];
-    uint32_t rank = 0;
-    if (ne > need_eq) {
-#pragma unroll 8
-      for (uint32_t j = 0; j < ne; j++) rank += eq[j] < me;
-    }
-    if (rank < need_eq) set_bit(bitmap, me);
+// In a 1024-bin histogram, thread t holding bins 2t and 2t+1 (counts c0,
+// c1): the bin where the count from the top reaches `need`: found[0] = bin,
+// found[1] = keys in higher bins.  found[] must be preset; it is left
+// unchanged when the histogram holds fewer than `need` keys.
+__device__ __forceinline__ void find_bin_1024(uint32_t c0, uint32_t c1, uint32_t need, uint32_t* tmp,
+                                              uint32_t* found) {
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan(c0 + c1, tmp, &total);
+  const uint32_t higher = total - below - c0 - c1;     // keys in bins above 2t + 1
+  if (higher < need && higher + c1 >= need) {
+    found[0] = 2 * threadIdx.x + 1;
+    found[1] = higher;
+  } else if (higher + c1 < need && higher + c1 + c0 >= need) {
+    found[0] = 2 * threadIdx.x;
+    found[1] = higher + c1;
   }
   __syncthreads();
 }
@@ -477,10 +444,7 @@ __device__ __noinline__ void select_candidates(uint32_t nc, uint32_t need, int s
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) {
   const int srow = blockIdx.x;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
-  const int p = a.seq_len[brow] - a.n_q + qi;
-  int nv = (p + 1) / a.m;
-  if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
-  const int k = a.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = a.k, tid = threadIdx.x, lane = tid & 63;
   int32_t* out = a.topk + (int64_t)srow * k;
   const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
   uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
@@ -488,119 +452,171 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t tmp[64];
   __shared__ uint32_t found[4];
-  __shared__ uint32_t cand[2 * kCandCap];      // keys, then block indices
-  __shared__ uint32_t bitmap[2 * kMaxWords];
-  __shared__ uint32_t cand_n;
-  uint32_t* cand_key = cand;
-  uint32_t* cand_idx = cand + kCandCap;
+  __shared__ uint32_t cand[2 * kCandCap];      // listed keys, then their blocks (block order)
+  __shared__ uint32_t bitmap[2 * kMaxWords];   // bit j of word w: block 32 w + j
 
-  // 1. histogram -> threshold bin; leave the global histogram zeroed
+  // The histogram loads go out first, then round 0's keys, so that the
+  // histogram phase does not wait for the keys (loads complete in issue
+  // order).  Key loads are unconditional: a block past the count reads block
+  // 0 of the row and is masked at use.
+  // Nothing here waits for the row length: the loads are addressed within
+  // the key row (a round past its end reads the row's last 64 keys), and
+  // the length comes through the scalar cache after they are issued.
+  const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
+  uint4 kv[16];
+  auto load_round = [&](int r) {
+    int b0 = r * kRoundKeys + 64 * tid;
+    b0 = b0 + 64 <= a.stride ? b0 : (int)a.stride - 64;
+    const uint4* src = reinterpret_cast<const uint4*>(keys + b0);
+#pragma unroll
+    for (int v = 0; v < 16; v++) kv[v] = src[v];
+  };
+  load_round(0);
+  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+  const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
+  int nv = (p + 1) / a.m;
+  if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
+  const int rounds = (nv + kRoundKeys - 1) / kRoundKeys;
+  if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
+  // 1. threshold bin tb from the histogram (thread t holds bins 8t .. 8t+7)
   {
-    constexpr int kPer = kHistBins / kSelThreads;
-    uint32_t hv[kPer];
+    const uint32_t c8 = hv0.x + hv0.y + hv0.z + hv0.w + hv1.x + hv1.y + hv1.z + hv1.w;
+    uint32_t total;
+    const uint32_t below = block_exclusive_scan(c8, tmp, &total);
+    reinterpret_cast<uint4*>(gh)[2 * tid] = make_uint4(0, 0, 0, 0);   // for the next call
+    reinterpret_cast<uint4*>(gh)[2 * tid + 1] = make_uint4(0, 0, 0, 0);
+    // walk the eight bins from the top (branch-free: at most one hits)
+    const uint32_t cs[8] = {hv1.w, hv1.z, hv1.y, hv1.x, hv0.w, hv0.z, hv0.y, hv0.x};
+    const uint32_t ku = (uint32_t)k;
+    uint32_t run = total - below - c8;          // keys in bins above this thread's eight
+    uint32_t hit = 0, hbin = 0, hrun = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; u++) hv[u] = gh[tid + u * kSelThreads];
-#pragma unroll
-    for (int u = 0; u < kPer; u++) {
-      hist[tid + u * kSelThreads] = hv[u];
-      gh[tid + u * kSelThreads] = 0;
+    for (int i = 0; i < 8; i++) {
+      const uint32_t h = (run < ku) & (run + cs[i] >= ku);
+      hbin = h ? (uint32_t)(8 * tid + 7 - i) : hbin;
+      hrun = h ? run : hrun;
+      hit |= h;
+      run += cs[i];
+    }
+    if (hit) {
+      found[0] = hbin;
+      found[1] = hrun;
     }
   }
   if (nv <= k) {
     for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  if (tid == 0) {
-    cand_n = 0;
-    found[0] = found[1] = found[2] = 0;
-  }
   __syncthreads();
-  find_bin(hist, kHistBins, (uint32_t)k, tmp, found);
-  const uint32_t tb = found[0], above = found[1], inbin = found[2];
-  const uint32_t need1 = (uint32_t)k - above;
-  __syncthreads();
-  const int nwords = (nv + 63) >> 6;
+  const uint32_t tb = found[0], above = found[1];
+  const int nwords32 = (nv + 31) >> 5;
 
-  // 2. bitmap of keys above tb; keys inside tb listed or sub-histogrammed
-  const bool direct = inbin <= (uint32_t)kCandCap;
-  if (!direct)
-    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
-  __syncthreads();
-  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
-    const bool inb = j < nv && (key >> kHistShift) == tb;
-    const uint64_t sm = __ballot(j < nv && (key >> kHistShift) > tb);
-    if (lane == 0) {
-      bitmap[2 * w] = (uint32_t)sm;
-      bitmap[2 * w + 1] = (uint32_t)(sm >> 32);
+  // 2. bits above tb, keys inside tb listed in block order
+  uint32_t nc = 0;
+  for (int r = 0; r < rounds; r++) {
+    if (r) load_round(r);
+    const int b0 = r * kRoundKeys + 64 * tid;
+    const int lim = nv - b0;                    // keys of this thread below the count
+    // bits by plain integer arithmetic (no per-key lane masks): for bins in
+    // [0, 4096), tb - bin < 0 iff bin > tb, and (bin ^ tb) - 1 wraps iff equal
+    uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int e = 4 * v + i;
+        const uint32_t bin = q[i] >> kHistShift;
+        gt[e >> 5] |= ((tb - bin) >> 31) << (e & 31);
+        eq[e >> 5] |= (((bin ^ tb) - 1u) >> 31) << (e & 31);
+      }
     }
-    if (direct) {
-      const uint64_t cm = __ballot(inb);
-      if (cm) {
-        uint32_t basepos = 0;
-        if (lane == 0) basepos = atomicAdd(&cand_n, (uint32_t)__popcll(cm));
-        basepos = __shfl(basepos, 0, kWave);
-        if (inb) {
-          const uint32_t pos = basepos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
-          if (pos < (uint32_t)kCandCap) {
-            cand_key[pos] = key;
-            cand_idx[pos] = (uint32_t)j;
+    // keys past the count are dropped
+    const uint32_t m0 = lim >= 32 ? 0xFFFFFFFFu : (lim <= 0 ? 0u : (1u << lim) - 1u);
+    const uint32_t m1 = lim >= 64 ? 0xFFFFFFFFu : (lim <= 32 ? 0u : (1u << (lim - 32)) - 1u);
+    gt[0] &= m0;
+    gt[1] &= m1;
+    eq[0] &= m0;
+    eq[1] &= m1;
+    const uint32_t cnt = (uint32_t)(__popc(eq[0]) + __popc(eq[1]));
+    if (lim > 0) bitmap[2 * (r * kSelThreads + tid)] = gt[0];
+    if (lim > 32) bitmap[2 * (r * kSelThreads + tid) + 1] = gt[1];
+    uint32_t tot;
+    uint32_t pos = nc + block_exclusive_scan(cnt, tmp, &tot);
+    if (nc + tot <= (uint32_t)kCandCap && cnt) {
+      // the few listed keys, in block order
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = 4 * v + i;
+          if ((eq[e >> 5] >> (e & 31)) & 1u) {
+            cand[pos] = q[i];
+            cand[kCandCap + pos] = (uint32_t)(b0 + e);
+            pos++;
           }
         }
       }
-    } else if (inb) {
-      atomicAdd(&hist[(key >> 8) & (kHistBins - 1)], 1u);
     }
-  });
-  __syncthreads();
-
-  bool done = false;
-  if (direct) {
-    select_candidates(min(cand_n, (uint32_t)kCandCap), need1, kHistShift, cand_key, cand_idx, hist,
-                      tmp, found, bitmap);
-    done = true;
-  } else {
-    find_bin(hist, kHistBins, need1, tmp, found);
-    const uint32_t x2 = found[0], above2 = found[1], inbin2 = found[2];
-    __syncthreads();
-    if (inbin2 <= (uint32_t)kCandCap) {
-      const uint32_t pfx = (tb << 12) | x2;
-      for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
-        const bool inb = j < nv && (key >> kHistShift) == tb;
-        const uint64_t sm = __ballot(inb && ((key >> 8) & (kHistBins - 1)) > x2);
-        if (lane == 0) {
-          bitmap[2 * w] |= (uint32_t)sm;
-          bitmap[2 * w + 1] |= (uint32_t)(sm >> 32);
-        }
-        const bool c2 = j < nv && (key >> 8) == pfx;
-        const uint64_t cm = __ballot(c2);
-        if (cm) {
-          uint32_t basepos = 0;
-          if (lane == 0) basepos = atomicAdd(&cand_n, (uint32_t)__popcll(cm));
-          basepos = __shfl(basepos, 0, kWave);
-          if (c2) {
-            const uint32_t pos = basepos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
-            if (pos < (uint32_t)kCandCap) {
-              cand_key[pos] = key;
-              cand_idx[pos] = (uint32_t)j;
-            }
-          }
-        }
-      });
-      __syncthreads();
-      select_candidates(min(cand_n, (uint32_t)kCandCap), need1 - above2, 8, cand_key, cand_idx, hist,
-                        tmp, found, bitmap);
-      done = true;
-    }
+    nc += tot;
   }
 
-  if (!done) {
+  if (nc <= (uint32_t)kCandCap) {
+    // 3. exact threshold among the listed keys: bits 19..10, then 9..0
+    uint32_t need = (uint32_t)k - above;
+    uint32_t pfx = tb;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; pass++) {
+      const int shift = pass ? 0 : 10;
+      hist[2 * tid] = 0;
+      hist[2 * tid + 1] = 0;
+      if (tid == 0) found[0] = found[1] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < nc; i += kSelThreads) {
+        const uint32_t key = cand[i];
+        if ((key >> (shift + 10)) == pfx) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      find_bin_1024(hist[2 * tid], hist[2 * tid + 1], need, tmp, found);
+      need -= found[1];
+      pfx = (pfx << 10) | found[0];
+      __syncthreads();
+    }
+    const uint32_t T = pfx, need_eq = need;
+    // listed keys above T are taken; keys equal to T by list (= block) order
+    uint32_t neq = 0;
+    constexpr int kPerT = kCandCap / kSelThreads;
+    const uint32_t i0 = kPerT * tid;
+#pragma unroll
+    for (int i = 0; i < kPerT; i++) {
+      const uint32_t j = i0 + i;
+      if (j < nc) {
+        const uint32_t key = cand[j];
+        if (key > T) set_bit(bitmap, cand[kCandCap + j]);
+        neq += key == T;
+      }
+    }
+    uint32_t tot;
+    uint32_t rank = block_exclusive_scan(neq, tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < kPerT; i++) {
+      const uint32_t j = i0 + i;
+      if (j < nc && cand[j] == T) {
+        if (rank < need_eq) set_bit(bitmap, cand[kCandCap + j]);
+        rank++;
+      }
+    }
+    __syncthreads();
+  } else {
+    const int nwords = (nv + 63) >> 6;
     // Many keys share 24 high bits: radix select over every key (12 + 12 + 8
     // bits), then every key above T and the lowest-index keys equal to T.
     uint32_t pfx = 0, need = (uint32_t)k;
-    const int shifts[3] = {20, 8, 0};
-    const int widths[3] = {12, 12, 8};
+#pragma unroll
     for (int d = 0; d < 3; d++) {
-      const int shift = shifts[d], width = widths[d];
+      const int shift = d == 0 ? 20 : (d == 1 ? 8 : 0), width = d == 2 ? 8 : 12;
       const uint32_t nb = 1u << width, mask = nb - 1;
       for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
       __syncthreads();
@@ -648,19 +664,19 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
     __syncthreads();
   }
 
-  // 4. compaction: ascending block order
-  const int wper = (nwords + kSelThreads - 1) / kSelThreads;
-  const int w0 = tid * wper, w1 = min(nwords, w0 + wper);
+  // 4. compaction: ascending block order, thread t owns a run of 32-bit words
+  const int wper = (nwords32 + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * wper, w1 = min(nwords32, w0 + wper);
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; w++) cnt += __popc(bitmap[2 * w]) + __popc(bitmap[2 * w + 1]);
+  for (int w = w0; w < w1; w++) cnt += __popc(bitmap[w]);
   uint32_t tot;
   uint32_t pos = block_exclusive_scan(cnt, tmp, &tot);
   for (int w = w0; w < w1; w++) {
-    uint64_t bits = ((uint64_t)bitmap[2 * w + 1] << 32) | bitmap[2 * w];
+    uint32_t bits = bitmap[w];
     while (bits) {
-      const int b = __ffsll((unsigned long long)bits) - 1;
+      const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (pos < (uint32_t)k) out[pos] = w * 64 + b;
+      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
       pos++;
     }
   }
