@@ -424,8 +424,9 @@ __device__ __forceinline__ void set_bit(uint32_t* bitmap, uint32_t j) {
 
 // In a 1024-bin histogram, thread t holding bins 2t and 2t+1 (counts c0,
 // c1): the bin where the count from the top reaches `need`: found[0] = bin,
-// found[1] = keys in higher bins.  found[] must be preset; it is left
-// unchanged when the histogram holds fewer than `need` keys.
+// found[1] = keys in higher bins, found[2] = keys in the bin.  found[] must be
+// preset; it is left unchanged when the histogram holds fewer than `need`
+// keys.
 __device__ __forceinline__ void find_bin_1024(uint32_t c0, uint32_t c1, uint32_t need, uint32_t* tmp,
                                               uint32_t* found) {
   uint32_t total;
@@ -434,9 +435,11 @@ __device__ __forceinline__ void find_bin_1024(uint32_t c0, uint32_t c1, uint32_t
   if (higher < need && higher + c1 >= need) {
     found[0] = 2 * threadIdx.x + 1;
     found[1] = higher;
+    found[2] = c1;
   } else if (higher + c1 < need && higher + c1 + c0 >= need) {
     found[0] = 2 * threadIdx.x;
     found[1] = higher + c1;
+    found[2] = c0;
   }
   __syncthreads();
 }
@@ -564,15 +567,19 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
   }
 
   if (nc <= (uint32_t)kCandCap) {
-    // 3. exact threshold among the listed keys: bits 19..10, then 9..0
+    // 3. exact threshold among the listed keys: bits 19..10, then 9..0.  A
+    // pass whose bin holds exactly the keys still needed ends the search:
+    // every listed key at or above that bin is taken.
     uint32_t need = (uint32_t)k - above;
     uint32_t pfx = tb;
+    int shift = 20;
+    bool exact = false;
 #pragma unroll 1
-    for (int pass = 0; pass < 2; pass++) {
-      const int shift = pass ? 0 : 10;
+    for (int pass = 0; pass < 2 && !exact; pass++) {
+      shift -= 10;
       hist[2 * tid] = 0;
       hist[2 * tid + 1] = 0;
-      if (tid == 0) found[0] = found[1] = 0;
+      if (tid == 0) found[0] = found[1] = found[2] = 0;
       __syncthreads();
       for (uint32_t i = tid; i < nc; i += kSelThreads) {
         const uint32_t key = cand[i];
@@ -582,30 +589,34 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
       find_bin_1024(hist[2 * tid], hist[2 * tid + 1], need, tmp, found);
       need -= found[1];
       pfx = (pfx << 10) | found[0];
+      exact = found[2] == need;      // the bin's keys are exactly the ones needed
       __syncthreads();
     }
-    const uint32_t T = pfx, need_eq = need;
-    // listed keys above T are taken; keys equal to T by list (= block) order
-    uint32_t neq = 0;
+    // key >> shift compared with pfx: above -> taken; equal -> taken when the
+    // bin is exactly what is needed, else ranked by block (list) order
     constexpr int kPerT = kCandCap / kSelThreads;
     const uint32_t i0 = kPerT * tid;
+    uint32_t neq = 0;
 #pragma unroll
     for (int i = 0; i < kPerT; i++) {
       const uint32_t j = i0 + i;
       if (j < nc) {
-        const uint32_t key = cand[j];
-        if (key > T) set_bit(bitmap, cand[kCandCap + j]);
-        neq += key == T;
+        const uint32_t kp = cand[j] >> shift;
+        if (kp > pfx || (exact && kp == pfx)) set_bit(bitmap, cand[kCandCap + j]);
+        neq += kp == pfx;
       }
     }
-    uint32_t tot;
-    uint32_t rank = block_exclusive_scan(neq, tmp, &tot);
+    if (!exact) {
+      // shift is 0 here: pfx is the threshold key T, `need` keys equal to it
+      uint32_t tot;
+      uint32_t rank = block_exclusive_scan(neq, tmp, &tot);
 #pragma unroll
-    for (int i = 0; i < kPerT; i++) {
-      const uint32_t j = i0 + i;
-      if (j < nc && cand[j] == T) {
-        if (rank < need_eq) set_bit(bitmap, cand[kCandCap + j]);
-        rank++;
+      for (int i = 0; i < kPerT; i++) {
+        const uint32_t j = i0 + i;
+        if (j < nc && cand[j] == pfx) {
+          if (rank < need) set_bit(bitmap, cand[kCandCap + j]);
+          rank++;
+        }
       }
     }
     __syncthreads();
