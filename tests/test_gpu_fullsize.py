@@ -1,0 +1,188 @@
+"""GPU parity at the full workload sizes, checked on sampled rows / queries.
+
+The GPU runs one step of each workload over every row with the same launches
+as the benchmark (one append, the indexer, the attention); the oracle then
+repeats the step for a few sampled rows (or, for the prefill chunk, a few
+sampled queries) and every sampled output is held to the usual bar: entries
+equal up to rounding-midpoint code flips, scores and top-k sets bit exact,
+attention within 2e-3 (per-row max error over max magnitude).
+
+Inputs come from synth (seeded); expected values come from the oracle only.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from synth import layers as SL
+
+from gpu_helpers import ATTN_TOL, attn_rel_err, compare_entries, decode_keys
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+SCALE = np.float32(1.0 / np.sqrt(512.0))
+
+
+def _lca():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import long_context_compressed_append_amd as lca
+    return lca
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def _ring_tokens(V, f, p0, n):
+    """tokens p0 .. p0+n-1 of the one-row oracle view, from its ring: [1][n][C]"""
+    slots = np.arange(p0, p0 + n) % V["ring"]
+    return V[f][0][slots][None]
+
+
+def _score_keys(lay, lca, n_q, H_I, k):
+    """the order keys the indexer left in its workspace: [rows][stride] u32"""
+    ws = lay._ws["indexer"]
+    nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
+    rows = lay.batch * n_q
+    stride = max(64, (lay.len_max // lay.ratio + 63) // 64 * 64)
+    wsh = ws[:nbytes].view(torch.int32)
+    hist_words = rows * 4096
+    assert not wsh[:hist_words].any().item()        # histograms left zeroed
+    return wsh[hist_words: hist_words + rows * stride].view(rows, stride)
+
+
+def _check_finalised(got, V, r, block, m, has_idx):
+    flips = compare_entries(got, V, r, [block],
+                            _ring_tokens(V, "ring_kv", block * m, m),
+                            _ring_tokens(V, "ring_gate", block * m, m),
+                            _ring_tokens(V, "ring_ikey", block * m, m) if has_idx else None,
+                            _ring_tokens(V, "ring_igate", block * m, m) if has_idx else None,
+                            V["pos_bias"], V.get("ipos_bias"), m)
+    return flips
+
+
+def test_csa_decode_128k_fullsize():
+    """32 rows x 131072 tokens (32768 blocks), 64 heads, 16 indexer heads,
+    k = 512, W = 128, 16 needles per row; the step finalises block 32767."""
+    lca = _lca()
+    B, ctx, m, H, HI, k, W, needles = 32, 131072, 4, 64, 16, 512, 128, 16
+    seed, tag = 1001, "csa"
+    say("csa_decode_128k fullsize B", B, "ctx", ctx, "seed", seed)
+    ref = SL.make_layer(seed, tag, B, m, W, 256, 1, ctx // m + 64, [ctx - 1] * B)
+    Q = SL.queries(seed, tag, B, 1, H, HI)
+    planted = [SL.plant_needles(ref, seed, tag, b, needles, Q["iq"][b, 0], Q["iw"][b, 0], Q["q"][b, 0])
+               for b in range(B)]
+    tok = SL.tokens(seed, "fullsize_step", B, 1, 1)
+    lay = lca.Layer.from_host(ref)
+    lca.compress_append(lay, _dev(tok["kv"]), _dev(tok["gate"]), _dev(tok["ikey"]), _dev(tok["igate"]))
+    topk = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
+    out = lca.csa_attend(lay, _dev(Q["q"]), topk, float(SCALE))
+    torch.cuda.synchronize()
+    got_topk, got_out = topk.cpu().numpy(), out.cpu().numpy()
+    keys = _score_keys(lay, lca, 1, HI, k)
+    got = lay.download()
+    flips = 0
+    for r in (0, 13, 31):
+        say("csa_decode_128k row", r)
+        V = oracle.row_view(ref, r)
+        oracle.compress_append(V, tok["kv"][r:r + 1], tok["gate"][r:r + 1], tok["ikey"][r:r + 1],
+                               tok["igate"][r:r + 1])
+        assert int(got["seq_len"][r]) == ctx
+        slot = (ctx - 1) % V["ring"]
+        assert np.array_equal(got["ring_kv"][r, slot], V["ring_kv"][0, slot])
+        flips += _check_finalised(got, V, r, ctx // m - 1, m, True)
+        sc = oracle.indexer_scores(V, 0, 0, 1, Q["iq"][r:r + 1], Q["iw"][r:r + 1])
+        gs = decode_keys(keys[r, :len(sc)].cpu().numpy().view(np.uint32))
+        assert np.array_equal(gs.view(np.uint32), sc.view(np.uint32))
+        want = oracle.indexer_topk(V, Q["iq"][r:r + 1], Q["iw"][r:r + 1], k)
+        assert np.array_equal(got_topk[r], want[0])
+        assert set(planted[r]) <= set(got_topk[r, 0].tolist())
+        wo = oracle.csa_attend(V, Q["q"][r:r + 1], got_topk[r:r + 1], SCALE)
+        err = attn_rel_err(got_out[r:r + 1], wo)
+        print("row", r, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
+    assert flips <= 2
+
+
+def test_hca_decode_1m_fullsize():
+    """16 rows x 1048576 tokens (8192 entries), 64 heads, W = 128; the step
+    finalises entry 8191 (a 128-token pooling)."""
+    lca = _lca()
+    B, ctx, m, H, W = 16, 1048576, 128, 64, 128
+    seed, tag = 1002, "hca"
+    say("hca_decode_1m fullsize B", B, "ctx", ctx, "seed", seed)
+    ref = SL.make_layer(seed, tag, B, m, W, 256, 0, ctx // m + 64, [ctx - 1] * B)
+    Q = SL.queries(seed, tag, B, 1, H)
+    tok = SL.tokens(seed, "fullsize_step", B, 1, 0)
+    lay = lca.Layer.from_host(ref)
+    lca.compress_append(lay, _dev(tok["kv"]), _dev(tok["gate"]))
+    out = lca.hca_attend(lay, _dev(Q["q"]), float(SCALE))
+    torch.cuda.synchronize()
+    got_out = out.cpu().numpy()
+    got = lay.download()
+    flips = 0
+    for r in (0, 9, 15):
+        say("hca_decode_1m row", r)
+        V = oracle.row_view(ref, r)
+        oracle.compress_append(V, tok["kv"][r:r + 1], tok["gate"][r:r + 1])
+        assert int(got["seq_len"][r]) == ctx
+        flips += _check_finalised(got, V, r, ctx // m - 1, m, False)
+        wo = oracle.hca_attend(V, Q["q"][r:r + 1], SCALE)
+        err = attn_rel_err(got_out[r:r + 1], wo)
+        print("row", r, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
+    assert flips <= 2
+
+
+def test_csa_prefill_chunk_fullsize():
+    """One row with a 262144-token prior context (65536 blocks): a 4096-token
+    chunk goes through compress_append (1024 new blocks), then 4096 queries
+    select their causal top-512 among up to 66560 blocks and attend.  Sampled
+    queries are checked against the oracle."""
+    lca = _lca()
+    prior, n, m, H, HI, k, W, R = 262144, 4096, 4, 64, 16, 512, 128, 8192
+    seed, tag = 1004, "prefill"
+    say("csa_prefill_chunk fullsize prior", prior, "chunk", n, "seed", seed)
+    ref = SL.make_layer(seed, tag, 1, m, W, R, 1, (prior + n) // m + 64, [prior])
+    tok = SL.tokens(seed, "chunk", 1, n, 1)
+    Q = SL.queries(seed, tag, 1, n, H, HI)
+    lay = lca.Layer.from_host(ref)
+    lca.compress_append(lay, _dev(tok["kv"]), _dev(tok["gate"]), _dev(tok["ikey"]), _dev(tok["igate"]))
+    topk = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
+    out = lca.csa_attend(lay, _dev(Q["q"]), topk, float(SCALE))
+    torch.cuda.synchronize()
+    got_topk = topk.cpu().numpy()
+    keys = _score_keys(lay, lca, n, HI, k)
+    got = lay.download()
+    V = oracle.row_view(ref, 0)
+    oracle.compress_append(V, tok["kv"], tok["gate"], tok["ikey"], tok["igate"])
+    assert int(got["seq_len"][0]) == prior + n
+    flips = 0
+    for b in (prior // m, prior // m + 511, (prior + n) // m - 1):
+        flips += _check_finalised(got, V, 0, b, m, True)
+    assert flips <= 2
+    for qi in (0, 1, 1234, 4094, 4095):
+        say("csa_prefill query", qi)
+        sc = oracle.indexer_scores(V, 0, qi, n, Q["iq"], Q["iw"])
+        gs = decode_keys(keys[qi, :len(sc)].cpu().numpy().view(np.uint32))
+        assert np.array_equal(gs.view(np.uint32), sc.view(np.uint32))
+        assert np.array_equal(got_topk[0, qi], oracle.topk_select(sc, k))
+        # one query alone: a view whose length ends at the query's position
+        p = prior + qi
+        Vq = dict(V)
+        Vq["seq_len"] = np.array([p + 1], np.int32)
+        wo = oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], got_topk[:, qi:qi + 1], SCALE)
+        err = attn_rel_err(out[:, qi:qi + 1].cpu().numpy(), wo)
+        print("query", qi, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
