@@ -69,6 +69,49 @@ __device__ __forceinline__ void ring_copy(const CompressArgs& a, int row, int j,
   }
 }
 
+// Longer blocks (m = 16 .. 128): the m logits (then weights) of this lane's
+// channel go to the wavefront's LDS slice lds[i * 64 + lane]; the loads of a
+// batch of 32 tokens are all issued before any is used.
+template <typename XF, typename ZF>
+__device__ __forceinline__ float pool_long(int m, XF xval, ZF zval, const float* bias, int C, int c,
+                                           float* lds, int lane) {
+  constexpr int NB = 32;
+  float mx = -INFINITY;
+#pragma unroll 1
+  for (int i0 = 0; i0 < m; i0 += NB) {
+    float zv[NB], bv[NB];
+#pragma unroll
+    for (int i = 0; i < NB; i++) zv[i] = zval(i0 + i);
+#pragma unroll
+    for (int i = 0; i < NB; i++) bv[i] = bias[(i0 + i) * C + c];
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const float ai = __fadd_rn(zv[i], bv[i]);
+      lds[(i0 + i) * 64 + lane] = ai;
+      mx = ai > mx ? ai : mx;
+    }
+  }
+  float S = 0.0f;
+#pragma unroll 8
+  for (int i = 0; i < m; i++) {
+    const float e = expf(__fsub_rn(lds[i * 64 + lane], mx));
+    lds[i * 64 + lane] = e;
+    S = __fadd_rn(S, e);
+  }
+  // the weighted sum in ascending order
+  float acc = 0.0f;
+#pragma unroll 1
+  for (int i0 = 0; i0 < m; i0 += NB) {
+    float xv[NB];
+#pragma unroll
+    for (int i = 0; i < NB; i++) xv[i] = xval(i0 + i);
+#pragma unroll
+    for (int i = 0; i < NB; i++)
+      acc = __fadd_rn(acc, __fmul_rn(__fdiv_rn(lds[(i0 + i) * 64 + lane], S), xv[i]));
+  }
+  return acc;
+}
+
 // Pool channel `c` (of a stream with C channels) over the m tokens of block bk.
 // Token t of the block comes from this call's input when t >= L0, else from
 // the ring.  Same operation order as the definition: logits, max, exp and
@@ -77,29 +120,42 @@ template <bool kBf16>
 __device__ __forceinline__ float pool_channel(const CompressArgs& a, int row, int64_t bk, int L0,
                                               int c, int C, const void* in_x, const float* in_z,
                                               const void* ring_x, const float* ring_z,
-                                              const float* bias) {
+                                              const float* bias, float* lds, int lane) {
   const int m = a.m;
-  auto xval = [&](int64_t t) -> float {
-    if (t >= L0) {
-      int64_t i = ((int64_t)row * a.n + (t - L0)) * C + c;
-      return kBf16 ? bf16_f32(static_cast<const uint16_t*>(in_x)[i]) : static_cast<const float*>(in_x)[i];
-    }
-    int64_t i = ((int64_t)row * a.R + t % a.R) * C + c;
-    return kBf16 ? bf16_f32(static_cast<const uint16_t*>(ring_x)[i]) : static_cast<const float*>(ring_x)[i];
-  };
-  auto zval = [&](int64_t t) -> float {
-    if (t >= L0) return in_z[((int64_t)row * a.n + (t - L0)) * C + c];
-    return ring_z[((int64_t)row * a.R + t % a.R) * C + c];
-  };
   const int64_t t0 = bk * m;
+  // element index of token t0 + i: the call's input from position L0 on, the
+  // ring (slot (t0 + i) % R) before it; branch-free so that loads batch
+  const int slot0 = (int)(t0 % a.R);
+  auto elem = [&](int i, bool& from_input) -> int64_t {
+    const int64_t t = t0 + i;
+    from_input = t >= L0;
+    int slot = slot0 + i;
+    slot = slot >= a.R ? slot - a.R : slot;     // i < m <= R
+    return from_input ? ((int64_t)row * a.n + (t - L0)) * C + c : ((int64_t)row * a.R + slot) * C + c;
+  };
+  auto xval = [&](int i) -> float {
+    bool in;
+    const int64_t e = elem(i, in);
+    if (kBf16) {
+      const uint16_t* base = static_cast<const uint16_t*>(in ? in_x : ring_x);
+      return bf16_f32(base[e]);
+    }
+    const float* base = static_cast<const float*>(in ? in_x : ring_x);
+    return base[e];
+  };
+  auto zval = [&](int i) -> float {
+    bool in;
+    const int64_t e = elem(i, in);
+    return (in ? in_z : ring_z)[e];
+  };
   if (m <= 8) {
     // short blocks: every token's logit and value in registers, one load pass
     float av[8], xv[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       if (i < m) {
-        av[i] = __fadd_rn(zval(t0 + i), bias[i * C + c]);
-        xv[i] = xval(t0 + i);
+        av[i] = __fadd_rn(zval(i), bias[i * C + c]);
+        xv[i] = xval(i);
       }
     }
     float M = -INFINITY;
@@ -119,27 +175,16 @@ __device__ __forceinline__ float pool_channel(const CompressArgs& a, int row, in
       if (i < m) acc = __fadd_rn(acc, __fmul_rn(__fdiv_rn(ev[i], S), xv[i]));
     return acc;
   }
-  float M = -INFINITY;
-  for (int i = 0; i < m; i++) {
-    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
-    M = ai > M ? ai : M;
-  }
-  float S = 0.0f;
-  for (int i = 0; i < m; i++) {
-    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
-    S = __fadd_rn(S, expf(__fsub_rn(ai, M)));
-  }
-  float acc = 0.0f;
-  for (int i = 0; i < m; i++) {
-    float ai = __fadd_rn(zval(t0 + i), bias[i * C + c]);
-    float w = __fdiv_rn(expf(__fsub_rn(ai, M)), S);
-    acc = __fadd_rn(acc, __fmul_rn(w, xval(t0 + i)));
-  }
-  return acc;
+  // m = 16 .. 128 (a power of two): a multiple of the 32-token batch above 16
+  return pool_long(m, xval, zval, bias, C, c, lds, lane);
 }
 
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
+  // per-wavefront LDS slices of 64 x m floats for blocks of m >= 16 tokens
+  // (dynamic shared memory, sized at launch; empty for shorter blocks)
+  extern __shared__ float pool_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* lds = pool_lds + (a.m > 8 ? wave * 64 * a.m : 0);
   const int64_t task = (int64_t)blockIdx.x * 4 + wave;
   if (task < a.ring_tasks) {
     ring_copy(a, (int)(task / a.n), (int)(task % a.n), lane);
@@ -156,7 +201,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
       if (g < 8) {
         const int c = g * 64 + lane;
         float y = pool_channel<true>(a, row, bk, L0, c, kKv, a.kv, a.gate, a.ring_kv, a.ring_gate,
-                                     a.pos_bias);
+                                     a.pos_bias, lds, lane);
         if (g < 7) {
           float amax = wave_max(fabsf(y));
           uint32_t code = 0;
@@ -174,7 +219,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
         }
       } else {
         float y = pool_channel<false>(a, row, bk, L0, lane, kIdx, a.ikey, a.igate, a.ring_ikey,
-                                      a.ring_igate, a.ipos_bias);
+                                      a.ring_igate, a.ipos_bias, lds, lane);
         float amax = half_wave_max(fabsf(y));
         uint32_t code = 0, ebyte = 0;
         if (amax > 0.0f) {
@@ -238,7 +283,8 @@ int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, c
   int64_t blocks = (a.total_tasks + 3) / 4;
   if (blocks > 0x7FFFFFFF) return LCA_EUNSUPPORTED;
   TimedLaunch t(kKernelCompress, stream);
-  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  const size_t lds_bytes = a.m > 8 ? (size_t)4 * 64 * a.m * sizeof(float) : 0;   // <= 128 KB
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), lds_bytes, stream, a);
   return t.done();
 }
 
