@@ -44,6 +44,15 @@ WORKLOADS = {
 }
 
 
+# Interleaved streaming decode: `pairs` x (CSA layer, HCA layer) at `ctx`,
+# each step appends one token per row to every layer and runs every layer.
+# name: (batch, context, pairs, CSA heads, CSA indexer heads, CSA k, HCA heads, window)
+INTERLEAVED = {
+    "interleaved_1m": (8, 1 << 20, 8, 16, 4, 64, 64, 128),          # CSA layers shaped as the tiny decode
+    "interleaved_1m_wide": (8, 1 << 20, 8, 64, 16, 512, 64, 128),   # CSA layers shaped as the 128K decode
+}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -138,6 +147,135 @@ def counter_traffic(dominant, workload):
     return nbytes
 
 
+def interleaved_bytes(B, ctx, H_c, HI, k, H_h, W):
+    """Algorithmic bytes of one layer pair (per the per-row figures above)."""
+    csa = B * ((ctx // 4) * 34 + HI * 260 + 2 * k * 4 + k * 604 + W * 1024 + H_c * 1024 + H_c * 2048)
+    hca = B * ((ctx // 128) * 604 + W * 1024 + H_h * 1024 + H_h * 2048)
+    return csa, hca
+
+
+def run_interleaved(args):
+    import torch
+    import long_context_compressed_append_amd as lca
+    from synth import layers as SL
+
+    B, ctx, P, H_c, HI, k, H_h, W = INTERLEAVED[args.workload]
+    seed = 1005
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t = time.time()
+    # one host image per layer kind (each with its outlier channels), copied to
+    # every layer of that kind; from then on the layers diverge by their tokens
+    images = {}
+    for kind, m, has_idx in (("csa", 4, 1), ("hca", 128, 0)):
+        ref = SL.make_layer(seed, kind, B, m, W, 256, has_idx, ctx // m + 64, [ctx - 1] * B)
+        SL.apply_outliers(ref, SL.outlier_channels(seed, kind, 0))
+        images[kind] = ref
+    log(f"host images built in {time.time() - t:.1f}s")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    layers = {"csa": [], "hca": []}
+    for kind in ("csa", "hca"):
+        base = lca.Layer.from_host(images[kind], device=dev)
+        layers[kind].append(base)
+        for _ in range(P - 1):
+            lay = lca.Layer(base.batch, base.ratio, base.window, base.ring, base.has_indexer,
+                            base.max_blocks, device=dev, pos_bias=images[kind]["pos_bias"],
+                            ipos_bias=images[kind].get("ipos_bias"))
+            for f in lca.Layer.PLANES:
+                src = getattr(base, f)
+                if src is not None:
+                    getattr(lay, f).copy_(src)
+            lay.len_min, lay.len_max = base.len_min, base.len_max
+            layers[kind].append(lay)
+    del images
+    torch.cuda.synchronize()
+    log(f"{2 * P} device layers ready in {time.time() - t:.1f}s")
+    n_set = 4
+    toks = {kind: [[{kk: up(v) for kk, v in SL.outlier_tokens(
+        SL.tokens(seed, f"{kind}{l}", B, 1, kind == "csa", step=s),
+        SL.outlier_channels(seed, kind, 0)).items()} for s in range(n_set)] for l in range(P)]
+        for kind in ("csa", "hca")}
+    qs = {"csa": [up(SL.queries(seed, "csaq", B, 1, H_c, HI, step=s)["q"]) for s in range(n_set)],
+          "hca": [up(SL.queries(seed, "hcaq", B, 1, H_h, step=s)["q"]) for s in range(n_set)]}
+    iqs = [SL.queries(seed, "csaq", B, 1, H_c, HI, step=s) for s in range(n_set)]
+    iq = [(up(x["iq"]), up(x["iw"])) for x in iqs]
+    topk = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    out_c = torch.empty((B, 1, H_c, 512), dtype=torch.float32, device=dev)
+    out_h = torch.empty((B, 1, H_h, 512), dtype=torch.float32, device=dev)
+
+    def step(s):
+        for l in range(P):
+            c, h = layers["csa"][l], layers["hca"][l]
+            tc, th = toks["csa"][l][s % n_set], toks["hca"][l][s % n_set]
+            lca.compress_append(c, tc["kv"], tc["gate"], tc["ikey"], tc["igate"])
+            lca.indexer_topk(c, iq[s % n_set][0], iq[s % n_set][1], k, out=topk)
+            lca.csa_attend(c, qs["csa"][s % n_set], topk, out=out_c)
+            lca.compress_append(h, th["kv"], th["gate"])
+            lca.hca_attend(h, qs["hca"][s % n_set], out=out_h)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    # timed, eager, one step at a time (per-step latency) over `steps` steps;
+    # the HCA layers finalise a block on the first step after every 128th token
+    nsteps = min(args.steps, 128)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        ev0[i].record()
+        step(args.warmup + i)
+        ev1[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = np.array([ev0[i].elapsed_time(ev1[i]) for i in range(nsteps)])
+    # the dominant kernel (CSA indexer score) alone, HIP events around its launches
+    with lca.KernelTimer("indexer_score") as kt:
+        step(args.warmup + nsteps)
+        torch.cuda.synchronize()
+    kernel_ms = kt.total_ms / max(1, kt.launches)
+    csa_b, hca_b = interleaved_bytes(B, ctx, H_c, HI, k, H_h, W)
+    step_ms = float(times.mean())
+    dom_bytes = B * ((ctx // 4) * 34 + HI * 260)
+    achieved = dom_bytes / (kernel_ms / 1e3) / 1e9 if kernel_ms > 0 else 0.0
+    res = {
+        "metric": METRIC,
+        "value": round(B / (step_ms / 1e3), 1),
+        "unit": "tokens/s (one token per row through every layer)",
+        "n_gpus": 1, "steps": nsteps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4/fp8 storage; fp32 scores; bf16/fp16 MFMA with fp32 accumulate",
+        "data": "synthetic (seeded cache images, 26 outlier channels x20 per layer kind)",
+        "config": {
+            "workload": args.workload, "batch": B, "context": ctx, "layer_pairs": P,
+            "csa": {"heads": H_c, "indexer_heads": HI, "topk": k, "ratio": 4},
+            "hca": {"heads": H_h, "ratio": 128}, "window": W, "launch": "eager",
+            "pair_latency_us": {"mean": round(step_ms * 1e3 / P, 2),
+                                "p50": round(float(np.median(times)) * 1e3 / P, 2),
+                                "max": round(float(times.max()) * 1e3 / P, 2)},
+            "step_ms": {"mean": round(step_ms, 4), "p50": round(float(np.median(times)), 4),
+                        "max": round(float(times.max()), 4)},
+            "step_algorithmic_bytes": P * (csa_b + hca_b),
+            "step_hbm_gbs": round(P * (csa_b + hca_b) / (step_ms / 1e3) / 1e9, 1),
+            "wall_ms_per_step": round(wall * 1e3 / nsteps, 4),
+        },
+        "roofline": {
+            "kernel": "indexer_score", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "kernel_avg_us": round(kernel_ms * 1e3, 3), "bytes_per_launch": dom_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res))
+
+
 def calibrate_copy(mib):
     """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
     factor between the counters and the bytes a kernel really moves."""
@@ -158,7 +296,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="csa_decode_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="csa_decode_128k",
+                    choices=sorted(WORKLOADS) + sorted(INTERLEAVED))
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -170,9 +309,12 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across "
-              "GPUs with no exchange; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (decode rows would shard "
+              "across GPUs with no exchange).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in INTERLEAVED:
+        return run_interleaved(args)
 
     import torch
     import long_context_compressed_append_amd as lca

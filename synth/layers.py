@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (abs_normal_f32, bf16_normal, distinct_choice, e2m1_code_image,
+from . import (bf16_bits, bf16_to_f32, abs_normal_f32, bf16_normal, distinct_choice, e2m1_code_image,
                e4m3_code_image, e8m0_image, fp8_scale_image, normal_f32)
 
 KV, NOPE, ROPE, IDX = 512, 448, 64, 64
@@ -121,3 +121,27 @@ def plant_needles(L, seed, tag, row, count, iq_row, iw_row, q_row):
         L["idx_scale"][row, b] = 128
         L["nope"][row, b] = kv_code
     return blocks
+
+
+def outlier_channels(seed, tag, layer, count=26):
+    """`count` distinct KV channels (of 512) that carry outliers in one layer."""
+    return np.sort(distinct_choice(seed, "outliers", count, 0, KV - 1, tag, layer)).astype(np.int64)
+
+
+def apply_outliers(L, ch, factor=20.0):
+    """Stress pattern on a cache image: every FP8 group holding an outlier
+    channel gets its scale multiplied by `factor`, outlier RoPE dims and the
+    ring's raw tokens in those channels are multiplied by `factor` (bf16)."""
+    groups = np.unique(ch[ch < NOPE] // 64)
+    for g in groups:
+        L["kv_scale"][:, :, g] *= np.float32(factor)
+    rc = ch[ch >= NOPE] - NOPE
+    if rc.size:
+        L["rope"][:, :, rc] = bf16_bits(bf16_to_f32(L["rope"][:, :, rc]) * np.float32(factor))
+    L["ring_kv"][:, :, ch] = bf16_bits(bf16_to_f32(L["ring_kv"][:, :, ch]) * np.float32(factor))
+
+
+def outlier_tokens(tok, ch, factor=20.0):
+    """The same stress on a batch of raw tokens (in place)."""
+    tok["kv"][:, :, ch] = bf16_bits(bf16_to_f32(tok["kv"][:, :, ch]) * np.float32(factor))
+    return tok

@@ -186,3 +186,99 @@ def test_csa_prefill_chunk_fullsize():
         err = attn_rel_err(out[:, qi:qi + 1].cpu().numpy(), wo)
         print("query", qi, "attention max rel err", err, flush=True)
         assert err <= ATTN_TOL
+
+
+def _row_copy(L, r):
+    """an independent one-row copy of row r of a layer image"""
+    V = dict(L)
+    V["batch"] = 1
+    for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv", "ring_gate",
+              "ring_ikey", "ring_igate"):
+        V[f] = np.ascontiguousarray(L[f][r:r + 1]).copy()
+    return V
+
+
+def _device_row(lay, r):
+    """row r of a device layer as a one-row host dict (the planes an entry check reads)"""
+    out = {}
+    for f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale"):
+        t = getattr(lay, f)
+        if t is not None and t.numel():
+            a = t[r:r + 1].cpu().numpy()
+            out[f] = a.view(np.uint16) if a.dtype == np.int16 else a
+    return out
+
+
+def test_interleaved_1m_fullsize():
+    """8 rows at a 1048575-token context, 8 CSA layers (16 heads, 4 indexer
+    heads, k = 64) interleaved with 8 HCA layers (64 heads), 26 outlier
+    channels x20; six decode steps (step 0 finalises CSA block 262143 and HCA
+    entry 8191, step 4 finalises CSA block 262144).  Two sampled rows of the
+    first CSA and the last HCA layer are followed by the oracle through every
+    step and checked at the end."""
+    lca = _lca()
+    B, ctx, P, H_c, HI, k, H_h, W = 8, 1 << 20, 8, 16, 4, 64, 64, 128
+    seed = 1005
+    say("interleaved_1m fullsize B", B, "pairs", P, "seed", seed)
+    images, ch = {}, {}
+    for kind, m, has_idx in (("csa", 4, 1), ("hca", 128, 0)):
+        ref = SL.make_layer(seed, kind, B, m, W, 256, has_idx, ctx // m + 64, [ctx - 1] * B)
+        ch[kind] = SL.outlier_channels(seed, kind, 0)
+        SL.apply_outliers(ref, ch[kind])
+        images[kind] = ref
+    layers = {kind: [lca.Layer.from_host(images[kind]) for _ in range(P)] for kind in ("csa", "hca")}
+    rows = (2, 7)
+    track = {("csa", 0): {r: _row_copy(images["csa"], r) for r in rows},
+             ("hca", P - 1): {r: _row_copy(images["hca"], r) for r in rows}}
+    del images
+    steps = 6
+    for s in range(steps):
+        say("interleaved step", s)
+        qc = SL.queries(seed, "csaq", B, 1, H_c, HI, step=s)
+        qh = SL.queries(seed, "hcaq", B, 1, H_h, step=s)
+        for l in range(P):
+            tc = SL.outlier_tokens(SL.tokens(seed, f"csa{l}", B, 1, 1, step=s), ch["csa"])
+            th = SL.outlier_tokens(SL.tokens(seed, f"hca{l}", B, 1, 0, step=s), ch["hca"])
+            c, h = layers["csa"][l], layers["hca"][l]
+            lca.compress_append(c, _dev(tc["kv"]), _dev(tc["gate"]), _dev(tc["ikey"]), _dev(tc["igate"]))
+            topk = lca.indexer_topk(c, _dev(qc["iq"]), _dev(qc["iw"]), k)
+            out_c = lca.csa_attend(c, _dev(qc["q"]), topk, float(SCALE))
+            lca.compress_append(h, _dev(th["kv"]), _dev(th["gate"]))
+            out_h = lca.hca_attend(h, _dev(qh["q"]), float(SCALE))
+            for (kind, tl), views in track.items():
+                if tl != l:
+                    continue
+                t = tc if kind == "csa" else th
+                for r, V in views.items():
+                    if kind == "csa":
+                        oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1], t["ikey"][r:r + 1],
+                                               t["igate"][r:r + 1])
+                    else:
+                        oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1])
+            if l == 0:
+                csa_topk, csa_out = topk, out_c
+            if l == P - 1:
+                hca_out = out_h
+        torch.cuda.synchronize()
+    got_topk, got_c, got_h = csa_topk.cpu().numpy(), csa_out.cpu().numpy(), hca_out.cpu().numpy()
+    flips = 0
+    for r, V in track[("csa", 0)].items():
+        say("interleaved csa layer 0 row", r)
+        dev_row = _device_row(layers["csa"][0], r)
+        for b in (ctx // 4 - 1, ctx // 4):
+            flips += _check_finalised(dev_row, V, 0, b, 4, True)
+        want = oracle.indexer_topk(V, qc["iq"][r:r + 1], qc["iw"][r:r + 1], k)
+        assert np.array_equal(got_topk[r], want[0])
+        wo = oracle.csa_attend(V, qc["q"][r:r + 1], got_topk[r:r + 1], SCALE)
+        err = attn_rel_err(got_c[r:r + 1], wo)
+        print("csa row", r, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
+    for r, V in track[("hca", P - 1)].items():
+        say("interleaved hca layer", P - 1, "row", r)
+        dev_row = _device_row(layers["hca"][P - 1], r)
+        flips += _check_finalised(dev_row, V, 0, ctx // 128 - 1, 128, False)
+        wo = oracle.hca_attend(V, qh["q"][r:r + 1], SCALE)
+        err = attn_rel_err(got_h[r:r + 1], wo)
+        print("hca row", r, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
+    assert flips <= 4
