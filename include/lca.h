@@ -216,7 +216,8 @@ const char *lca_last_error(void);
  * launch of the named kernel is bracketed by HIP events on its stream;
  * lca_timing_end synchronizes on them and returns the summed duration (ms)
  * and the number of launches.  Kernel names: "indexer_score", "topk_select",
- * "attend", "attend_combine", "compress".  At most 4096 launches are
+ * "attend", "attend_combine", "compress" ("topk_select" spans the
+ * selection's one or two launches).  At most 4096 launches are
  * recorded per session.  Errors: EINVAL (unknown name or nested session),
  * EHIP.
  */

@@ -139,7 +139,7 @@ int lca_compress_append(lca_layer* L, const uint16_t* kv, const float* gate, con
 size_t lca_indexer_workspace(const lca_layer* L, int32_t n_q, int32_t H_I, int32_t k) {
   if (!L || n_q < 1 || L->ratio < 1 || L->batch < 1) return 0;
   IndexerPlan pl = plan_indexer(L, n_q, H_I, k);
-  return pl.hist_bytes + pl.keys_bytes;
+  return pl.total();
 }
 
 int lca_indexer_topk(const lca_layer* L, const float* iq, const float* iw, int32_t n_q, int32_t H_I,
@@ -158,7 +158,7 @@ int lca_indexer_topk(const lca_layer* L, const float* iq, const float* iw, int32
   if ((rc = check_ptr(iq, "iq")) || (rc = check_ptr(iw, "iw")) || (rc = check_ptr(topk, "topk")))
     return rc;
   IndexerPlan pl = plan_indexer(L, n_q, H_I, k);
-  const size_t need = pl.hist_bytes + pl.keys_bytes;
+  const size_t need = pl.total();
   if (!ws || ws_bytes < need)
     return set_error(LCA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   if (!aligned16(ws)) return set_error(LCA_EINVAL, "workspace is not 16-byte aligned");

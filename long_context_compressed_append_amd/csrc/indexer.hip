@@ -312,23 +312,47 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-k by (score desc, block asc) for one query per workgroup of 512
-// threads.  In every round of 32768 blocks, thread t owns the two bitmap
-// words of blocks 64t .. 64t+63 of the round.
+// Exact top-k by (score desc, block asc) for one query, on workgroups of 512
+// threads.  Keys are taken in rounds of 32768 blocks; in a round, thread t
+// owns the 64 blocks 64t .. 64t+63 (two 32-bit bitmap words).
 //   1. The query's histogram of the top 12 key bits (built while scoring)
 //      gives the bin tb holding the k-th largest key and the count `above` of
-//      keys in higher bins; the histogram is zeroed for the next call.
-//   2. Each thread compares its 32 keys with tb: keys above tb set their bit,
-//      keys inside tb are listed in LDS in block order (a block-wide scan
-//      places every thread's keys).
+//      keys in higher bins.
+//   2. Each thread compares its keys with tb: keys above tb set their bit,
+//      keys inside tb are listed in block order (a block-wide scan places
+//      every thread's keys).
 //   3. Two radix passes of 10 bits over the listed keys give the exact
 //      threshold key T and how many keys equal to T are taken; listed keys
 //      above T set their bit, and keys equal to T are ranked by block index
 //      with a scan over the list, which is in block order.
 //   4. The bitmap is compacted into ascending block indices.
 // If more than kCandCap keys share tb (many nearly equal scores), a radix
-// select over all keys replaces steps 2-3.
+// select over all keys replaces steps 2-3.  The histogram is zeroed for the
+// next call.
+//
+// Short rows or many rows: one workgroup per query does all four steps
+// (topk_select_kernel).  Few long rows: step 2 runs on one workgroup per
+// (part of 16384 blocks, query) (topk_slice_kernel), which leaves the part's
+// bitmap words, its count of listed keys and the list in the workspace; a
+// second launch (topk_finish_kernel), one workgroup per query, gathers them
+// and does steps 3-4.  The kernel boundary orders the hand-over.  Lists of
+// at most 128 keys are ranked in step 3 by direct comparison instead of the
+// radix passes.
 // ---------------------------------------------------------------------------
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRoundKeys = 64 * kSelThreads;   // blocks per round
+constexpr int kCandCap = 4096;
+constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
+constexpr int kPartKeys = 32 * kSelThreads;   // blocks per workgroup of the sliced path
+constexpr int kMaxParts = 64 * kMaxWords / kPartKeys;     // 32
+constexpr int kDirectRank = 128;   // lists up to this long are ranked by direct comparison
+constexpr int kSliceMaxRows = 256;   // the sliced path is taken below this many queries
+constexpr int kSliceMinBlocks = 3 * kRoundKeys / 2;   // ... and above this many blocks per row
+static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
+static_assert(kMaxParts <= 64 && kMaxParts * kSelThreads == 2 * kMaxWords, "part bookkeeping");
+static_assert(kDirectRank <= kSelThreads && kDirectRank <= 4096, "one list entry per thread, 12-bit positions");
 
 struct SelectArgs {
   int n_q, m, k;
@@ -337,25 +361,35 @@ struct SelectArgs {
   const uint32_t* keys;
   uint32_t* hist;
   int32_t* topk;
+  // sliced path: per (query, round) bitmap words [rows][slices][1024], listed
+  // key counts [rows][slices] and lists [rows][slices][2][kCandCap]
+  int slices;
+  uint32_t* part_bits;
+  uint32_t* part_count;
+  uint32_t* part_cand;
 };
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRoundKeys = 64 * kSelThreads;   // blocks per round
-constexpr int kCandCap = 4096;
-constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
-static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
+// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the total of row 0 (lane 15) is added to row 1, that of row 2 (lane
+// 47) to row 3, and that of rows 0-1 (lane 31) to rows 2 and 3.  Lanes whose
+// source lies outside the row read 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xc, 0xf, false);
+  return x;
+}
 
 // exclusive prefix sum over the kSelThreads threads; returns the block total
 // in *total (tmp >= 32 words)
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   uint32_t before_wave = 0, all = 0;
@@ -444,10 +478,309 @@ __device__ __forceinline__ void find_bin_1024(uint32_t c0, uint32_t c1, uint32_t
   __syncthreads();
 }
 
+// The 64 keys of round r of this thread (blocks r * kRoundKeys + 64 t ..),
+// loaded unconditionally: a round past the end of the key row reads the
+// row's last 64 keys, which are masked at use.  Buffer loads keep each
+// 16-byte load whole (no re-split into overlapping pieces) and need no
+// per-round address registers; the descriptor's range is the key row.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit data format (gfx9 V# dword 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_row_rsrc(const uint32_t* keys, int64_t stride) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(keys), (short)0, (int)(stride * 4),
+                                           kBufferWord3);
+}
+
+template <int NV>
+__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t row, int64_t stride, int b0, uint4 (&kv)[NV]) {
+  b0 = b0 + 4 * NV <= stride ? b0 : (int)stride - 4 * NV;
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(row, 4 * b0 + 16 * v, 0, 0);
+    kv[v] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
+__device__ __forceinline__ void load_round(__amdgpu_buffer_rsrc_t row, int64_t stride, int r, uint4 (&kv)[16]) {
+  load_keys(row, stride, r * kRoundKeys + 64 * (int)threadIdx.x, kv);
+}
+
+// Step 1 on the histogram held as thread t's bins 8t .. 8t+7 (hv0, hv1):
+// found[0] = tb, found[1] = keys in higher bins.  found[] must be preset and
+// read after a barrier.
+__device__ __forceinline__ void threshold_bin(uint4 hv0, uint4 hv1, uint32_t k, uint32_t* tmp,
+                                              uint32_t* found, uint32_t* gh_zero) {
+  const int tid = threadIdx.x;
+  const uint32_t c8 = hv0.x + hv0.y + hv0.z + hv0.w + hv1.x + hv1.y + hv1.z + hv1.w;
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan(c8, tmp, &total);
+  if (gh_zero) {   // for the next call
+    reinterpret_cast<uint4*>(gh_zero)[2 * tid] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(gh_zero)[2 * tid + 1] = make_uint4(0, 0, 0, 0);
+  }
+  // walk the eight bins from the top (branch-free: at most one hits)
+  const uint32_t cs[8] = {hv1.w, hv1.z, hv1.y, hv1.x, hv0.w, hv0.z, hv0.y, hv0.x};
+  uint32_t run = total - below - c8;          // keys in bins above this thread's eight
+  uint32_t hit = 0, hbin = 0, hrun = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t h = (run < k) & (run + cs[i] >= k);
+    hbin = h ? (uint32_t)(8 * tid + 7 - i) : hbin;
+    hrun = h ? run : hrun;
+    hit |= h;
+    run += cs[i];
+  }
+  if (hit) {
+    found[0] = hbin;
+    found[1] = hrun;
+  }
+}
+
+// Step 2 for one thread's 4 NV keys of blocks b0 .. (lim = keys below the
+// count): bit e of gt / eq set when key e is above / inside bin tb.  Plain
+// integer arithmetic, no per-key lane masks: for bins in [0, 4096),
+// tb - bin < 0 iff bin > tb, and (bin ^ tb) - 1 wraps iff they are equal.
+template <int NV>
+__device__ __forceinline__ void round_bits(const uint4 (&kv)[NV], uint32_t tb, int lim, uint32_t (&gt)[NV / 8],
+                                           uint32_t (&eq)[NV / 8]) {
+#pragma unroll
+  for (int w = 0; w < NV / 8; w++) gt[w] = eq[w] = 0u;
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e = 4 * v + i;
+      const uint32_t bin = q[i] >> kHistShift;
+      gt[e >> 5] |= ((tb - bin) >> 31) << (e & 31);
+      eq[e >> 5] |= (((bin ^ tb) - 1u) >> 31) << (e & 31);
+    }
+  }
+  // keys past the count are dropped
+#pragma unroll
+  for (int w = 0; w < NV / 8; w++) {
+    const int l = lim - 32 * w;
+    const uint32_t m = l >= 32 ? 0xFFFFFFFFu : (l <= 0 ? 0u : (1u << l) - 1u);
+    gt[w] &= m;
+    eq[w] &= m;
+  }
+}
+
+// The keys inside bin tb, in block order, from list position pos on: keys to
+// ckey[], their blocks to cblk[].
+template <int NV>
+__device__ __forceinline__ void list_round(const uint4 (&kv)[NV], const uint32_t (&eq)[NV / 8], int b0, uint32_t pos,
+                                           uint32_t* ckey, uint32_t* cblk) {
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e = 4 * v + i;
+      if ((eq[e >> 5] >> (e & 31)) & 1u) {
+        ckey[pos] = q[i];
+        cblk[pos] = (uint32_t)(b0 + e);
+        pos++;
+      }
+    }
+  }
+}
+
+// Step 3: the nc listed keys (cand[0..nc) keys, cand[kCandCap..) blocks, in
+// block order) all lie in bin tb, and `above` keys lie in higher bins.  Sets
+// the bits of the listed keys that complete the top k.
+__device__ __forceinline__ void rank_listed(const uint32_t* cand, uint32_t nc, uint32_t tb, uint32_t above,
+                                            uint32_t k, uint32_t* hist, uint32_t* tmp, uint32_t* found,
+                                            uint32_t* bitmap) {
+  const int tid = threadIdx.x;
+  uint32_t need = k - above;
+  if (nc <= (uint32_t)kDirectRank) {
+    // Short list: entry i is taken when fewer than `need` listed keys come
+    // before it in (key desc, block asc) order.  Every listed key has the
+    // bin's 12 high bits and the list is in block order, so the order is
+    // that of the 32-bit value (low 20 key bits, 4095 - list position).
+    __syncthreads();     // every thread's list entries are in place
+    uint32_t* comp = hist;
+    if ((uint32_t)tid < nc) comp[tid] = ((cand[tid] & 0xFFFFFu) << 12) | (4095u - (uint32_t)tid);
+    __syncthreads();
+    if ((uint32_t)tid < nc) {
+      const uint32_t ci = comp[tid];
+      uint32_t rank = 0;
+#pragma unroll 8
+      for (uint32_t j = 0; j < nc; j++) rank += comp[j] > ci ? 1u : 0u;
+      if (rank < need) set_bit(bitmap, cand[kCandCap + tid]);
+    }
+    __syncthreads();
+    return;
+  }
+  // exact threshold among the listed keys: bits 19..10, then 9..0.  A pass
+  // whose bin holds exactly the keys still needed ends the search: every
+  // listed key at or above that bin is taken.
+  uint32_t pfx = tb;
+  int shift = 20;
+  bool exact = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 && !exact; pass++) {
+    shift -= 10;
+    hist[2 * tid] = 0;
+    hist[2 * tid + 1] = 0;
+    if (tid == 0) found[0] = found[1] = found[2] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < nc; i += kSelThreads) {
+      const uint32_t key = cand[i];
+      if ((key >> (shift + 10)) == pfx) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin_1024(hist[2 * tid], hist[2 * tid + 1], need, tmp, found);
+    need -= found[1];
+    pfx = (pfx << 10) | found[0];
+    exact = found[2] == need;      // the bin's keys are exactly the ones needed
+    __syncthreads();
+  }
+  // key >> shift compared with pfx: above -> taken; equal -> taken when the
+  // bin is exactly what is needed, else ranked by block (list) order
+  constexpr int kPerT = kCandCap / kSelThreads;
+  const uint32_t i0 = kPerT * tid;
+  uint32_t neq = 0;
+#pragma unroll
+  for (int i = 0; i < kPerT; i++) {
+    const uint32_t j = i0 + i;
+    if (j < nc) {
+      const uint32_t kp = cand[j] >> shift;
+      if (kp > pfx || (exact && kp == pfx)) set_bit(bitmap, cand[kCandCap + j]);
+      neq += kp == pfx;
+    }
+  }
+  if (!exact) {
+    // shift is 0 here: pfx is the threshold key T, `need` keys equal to it
+    uint32_t tot;
+    uint32_t rank = block_exclusive_scan(neq, tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < kPerT; i++) {
+      const uint32_t j = i0 + i;
+      if (j < nc && cand[j] == pfx) {
+        if (rank < need) set_bit(bitmap, cand[kCandCap + j]);
+        rank++;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Steps 2-3 when too many keys share bin tb: radix select over every key
+// (12 + 12 + 8 bits), then every key above the threshold T and the
+// lowest-index keys equal to T.  Writes every bitmap word of the row.
+__device__ __forceinline__ void select_all(const uint32_t* keys, int nv, uint32_t k, uint32_t* hist,
+                                           uint32_t* tmp, uint32_t* found, uint32_t* cand, uint32_t* bitmap) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nwords = (nv + 63) >> 6;
+  uint32_t pfx = 0, need = k;
+#pragma unroll
+  for (int d = 0; d < 3; d++) {
+    const int shift = d == 0 ? 20 : (d == 1 ? 8 : 0), width = d == 2 ? 8 : 12;
+    const uint32_t nb = 1u << width, mask = nb - 1;
+    for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
+    __syncthreads();
+    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+      if (j < nv && (d == 0 || (key >> (shift + width)) == pfx))
+        atomicAdd(&hist[(key >> shift) & mask], 1u);
+    });
+    __syncthreads();
+    find_bin(hist, nb, need, tmp, found);
+    need -= found[1];
+    pfx = (pfx << width) | found[0];
+    __syncthreads();
+  }
+  const uint32_t T = pfx, need_eq = need;
+  // equal keys per 64-block word (the candidate list doubles as the counts)
+  uint32_t* eqc = cand;       // 2 * kCandCap >= kMaxWords counters
+  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+    const uint64_t gm = __ballot(j < nv && key > T);
+    const uint64_t em = __ballot(j < nv && key == T);
+    if (lane == 0) {
+      bitmap[2 * w] = (uint32_t)gm;
+      bitmap[2 * w + 1] = (uint32_t)(gm >> 32);
+      eqc[w] = (uint32_t)__popcll(em);
+    }
+  });
+  __syncthreads();
+  const int wp = (nwords + kSelThreads - 1) / kSelThreads;
+  const int a0 = tid * wp, a1 = min(nwords, a0 + wp);
+  uint32_t loc = 0;
+  for (int w = a0; w < a1; w++) loc += eqc[w];
+  uint32_t tot;
+  uint32_t run = block_exclusive_scan(loc, tmp, &tot);
+  for (int w = a0; w < a1; w++) {
+    const uint32_t c = eqc[w];
+    eqc[w] = run;
+    run += c;
+  }
+  __syncthreads();
+  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+    const bool eq = j < nv && key == T;
+    const uint64_t em = __ballot(eq);
+    const uint32_t rank = eqc[w] + (uint32_t)__popcll(em & ((1ull << lane) - 1ull));
+    if (eq && rank < need_eq) set_bit(bitmap, (uint32_t)j);
+  });
+  __syncthreads();
+}
+
+// Step 4: ascending block order.  Wave w takes `steps` runs of 64 words,
+// from word 64 * steps * w on; in a run, lane l holds word l (consecutive
+// lanes read consecutive words, free of bank conflicts).  The words are read
+// once into registers; their bit counts and a block scan give each wave its
+// first output position, and a wave scan per run places each word's bits.
+// Runs without a set bit are skipped, and a wave stops once its positions
+// pass k.
+__device__ __forceinline__ void compact(const uint32_t* bitmap, int nv, int k, int32_t* out, uint32_t* tmp) {
+  constexpr int kMaxSteps = 2 * kMaxWords / (64 * kSelWaves);   // 32
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwords32 = (nv + 31) >> 5;
+  const int steps = (nwords32 + 64 * kSelWaves - 1) / (64 * kSelWaves);
+  const int wbase = wave * steps * 64;
+  uint32_t wv[kMaxSteps];
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxSteps; j++) {
+    const int w = wbase + 64 * j + lane;
+    wv[j] = (j < steps && w < nwords32) ? bitmap[w] : 0u;
+    c += (uint32_t)__popc(wv[j]);
+  }
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(c, tmp, &tot);
+  uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, 0);   // bits in the waves before this one
+#pragma unroll
+  for (int j = 0; j < kMaxSteps; j++) {
+    if (j >= steps || base >= (uint32_t)k) break;
+    uint32_t bits = wv[j];
+    if (__ballot(bits != 0u) == 0) continue;
+    const int w = wbase + 64 * j + lane;
+    const uint32_t cw = (uint32_t)__popc(bits);
+    const uint32_t incl = wave_inclusive_scan(cw);
+    uint32_t pos = base + incl - cw;
+    base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
+      pos++;
+    }
+  }
+}
+
+// visible blocks of query row srow (row length through the scalar cache)
+__device__ __forceinline__ int visible_blocks(const SelectArgs& a, int srow) {
+  const int brow = srow / a.n_q, qi = srow % a.n_q;
+  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+  const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
+  int nv = (p + 1) / a.m;
+  if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
+  return nv;
+}
+
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) {
   const int srow = blockIdx.x;
-  const int brow = srow / a.n_q, qi = srow % a.n_q;
-  const int k = a.k, tid = threadIdx.x, lane = tid & 63;
+  const int k = a.k, tid = threadIdx.x;
   int32_t* out = a.topk + (int64_t)srow * k;
   const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
   uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
@@ -458,239 +791,213 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
   __shared__ uint32_t cand[2 * kCandCap];      // listed keys, then their blocks (block order)
   __shared__ uint32_t bitmap[2 * kMaxWords];   // bit j of word w: block 32 w + j
 
-  // The histogram loads go out first, then round 0's keys, so that the
-  // histogram phase does not wait for the keys (loads complete in issue
-  // order).  Key loads are unconditional: a block past the count reads block
-  // 0 of the row and is masked at use.
-  // Nothing here waits for the row length: the loads are addressed within
-  // the key row (a round past its end reads the row's last 64 keys), and
-  // the length comes through the scalar cache after they are issued.
+  // The histogram loads go out first, then the keys of rounds 0 and 1, so
+  // that the histogram phase does not wait for the keys (loads complete in
+  // issue order).  Nothing here waits for the row length: the loads are
+  // addressed within the key row, and the length comes through the scalar
+  // cache after they are issued.  Round r + 2 is loaded while round r + 1
+  // is processed (two register sets, no copies).
   const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
   const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
-  uint4 kv[16];
-  auto load_round = [&](int r) {
-    int b0 = r * kRoundKeys + 64 * tid;
-    b0 = b0 + 64 <= a.stride ? b0 : (int)a.stride - 64;
-    const uint4* src = reinterpret_cast<const uint4*>(keys + b0);
-#pragma unroll
-    for (int v = 0; v < 16; v++) kv[v] = src[v];
-  };
-  load_round(0);
-  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
-  const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
-  int nv = (p + 1) / a.m;
-  if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
+  const __amdgpu_buffer_rsrc_t krow = key_row_rsrc(keys, a.stride);
+  uint4 ka[16], kb[16];
+  load_round(krow, a.stride, 0, ka);
+  load_round(krow, a.stride, 1, kb);
+  const int nv = visible_blocks(a, srow);
   const int rounds = (nv + kRoundKeys - 1) / kRoundKeys;
   if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
-  // 1. threshold bin tb from the histogram (thread t holds bins 8t .. 8t+7)
-  {
-    const uint32_t c8 = hv0.x + hv0.y + hv0.z + hv0.w + hv1.x + hv1.y + hv1.z + hv1.w;
-    uint32_t total;
-    const uint32_t below = block_exclusive_scan(c8, tmp, &total);
-    reinterpret_cast<uint4*>(gh)[2 * tid] = make_uint4(0, 0, 0, 0);   // for the next call
-    reinterpret_cast<uint4*>(gh)[2 * tid + 1] = make_uint4(0, 0, 0, 0);
-    // walk the eight bins from the top (branch-free: at most one hits)
-    const uint32_t cs[8] = {hv1.w, hv1.z, hv1.y, hv1.x, hv0.w, hv0.z, hv0.y, hv0.x};
-    const uint32_t ku = (uint32_t)k;
-    uint32_t run = total - below - c8;          // keys in bins above this thread's eight
-    uint32_t hit = 0, hbin = 0, hrun = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const uint32_t h = (run < ku) & (run + cs[i] >= ku);
-      hbin = h ? (uint32_t)(8 * tid + 7 - i) : hbin;
-      hrun = h ? run : hrun;
-      hit |= h;
-      run += cs[i];
-    }
-    if (hit) {
-      found[0] = hbin;
-      found[1] = hrun;
-    }
-  }
+  threshold_bin(hv0, hv1, (uint32_t)k, tmp, found, gh);
   if (nv <= k) {
     for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
     return;
   }
   __syncthreads();
   const uint32_t tb = found[0], above = found[1];
-  const int nwords32 = (nv + 31) >> 5;
 
-  // 2. bits above tb, keys inside tb listed in block order
   uint32_t nc = 0;
-  for (int r = 0; r < rounds; r++) {
-    if (r) load_round(r);
+  auto one_round = [&](const uint4 (&kv)[16], int r) {
     const int b0 = r * kRoundKeys + 64 * tid;
     const int lim = nv - b0;                    // keys of this thread below the count
-    // bits by plain integer arithmetic (no per-key lane masks): for bins in
-    // [0, 4096), tb - bin < 0 iff bin > tb, and (bin ^ tb) - 1 wraps iff equal
-    uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int e = 4 * v + i;
-        const uint32_t bin = q[i] >> kHistShift;
-        gt[e >> 5] |= ((tb - bin) >> 31) << (e & 31);
-        eq[e >> 5] |= (((bin ^ tb) - 1u) >> 31) << (e & 31);
-      }
-    }
-    // keys past the count are dropped
-    const uint32_t m0 = lim >= 32 ? 0xFFFFFFFFu : (lim <= 0 ? 0u : (1u << lim) - 1u);
-    const uint32_t m1 = lim >= 64 ? 0xFFFFFFFFu : (lim <= 32 ? 0u : (1u << (lim - 32)) - 1u);
-    gt[0] &= m0;
-    gt[1] &= m1;
-    eq[0] &= m0;
-    eq[1] &= m1;
+    uint32_t gt[2], eq[2];
+    round_bits(kv, tb, lim, gt, eq);
     const uint32_t cnt = (uint32_t)(__popc(eq[0]) + __popc(eq[1]));
     if (lim > 0) bitmap[2 * (r * kSelThreads + tid)] = gt[0];
     if (lim > 32) bitmap[2 * (r * kSelThreads + tid) + 1] = gt[1];
     uint32_t tot;
-    uint32_t pos = nc + block_exclusive_scan(cnt, tmp, &tot);
-    if (nc + tot <= (uint32_t)kCandCap && cnt) {
-      // the few listed keys, in block order
+    const uint32_t pos = nc + block_exclusive_scan(cnt, tmp, &tot);
+    if (nc + tot <= (uint32_t)kCandCap && cnt) list_round(kv, eq, b0, pos, cand, cand + kCandCap);
+    nc += tot;
+  };
+#pragma unroll 1
+  for (int r = 0; r < rounds; r += 2) {
+    one_round(ka, r);
+    if (r + 1 >= rounds) break;
+    load_round(krow, a.stride, r + 2, ka);
+    one_round(kb, r + 1);
+    load_round(krow, a.stride, r + 3, kb);
+  }
+
+  if (nc <= (uint32_t)kCandCap)
+    rank_listed(cand, nc, tb, above, (uint32_t)k, hist, tmp, found, bitmap);
+  else
+    select_all(keys, nv, (uint32_t)k, hist, tmp, found, cand, bitmap);
+  compact(bitmap, nv, k, out, tmp);
+}
+
+// Step 2 of one part of kPartKeys blocks (blockIdx.x) of one query
+// (blockIdx.y); thread t takes the 32 blocks of bitmap word 512 p + t.
+__global__ void __launch_bounds__(kSelThreads) topk_slice_kernel(SelectArgs a) {
+  const int p = blockIdx.x, srow = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
+  const uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+
+  __shared__ uint32_t tmp[64];
+  __shared__ uint32_t found[4];
+
+  const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
+  const int b0 = p * kPartKeys + 32 * tid;
+  uint4 kv[8];
+  load_keys(key_row_rsrc(keys, a.stride), a.stride, b0, kv);
+  const int nv = visible_blocks(a, srow);
+  if (nv <= a.k || p * kPartKeys >= nv) return;   // nothing of this part is read
+  if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
+  threshold_bin(hv0, hv1, (uint32_t)a.k, tmp, found, nullptr);
+  __syncthreads();
+  const uint32_t tb = found[0];
+  uint32_t gt[1], eq[1];
+  round_bits(kv, tb, nv - b0, gt, eq);
+  const int64_t part = (int64_t)srow * a.slices + p;
+  a.part_bits[part * kSelThreads + tid] = gt[0];
+  const uint32_t cnt = (uint32_t)__popc(eq[0]);
+  uint32_t tot;
+  const uint32_t pos = block_exclusive_scan(cnt, tmp, &tot);
+  if (tid == 0) a.part_count[part] = tot;
+  uint32_t* pc = a.part_cand + part * 2 * kCandCap;
+  if (tot <= (uint32_t)kCandCap && cnt) list_round(kv, eq, b0, pos, pc, pc + kCandCap);
+}
+
+// Steps 3-4 of one query from the parts that topk_slice_kernel left.  The
+// first S = kCandCap / slices (rounded down to 8) entries of every part's
+// list are loaded with everything else, before the counts are known; only a
+// part with more than S listed keys needs a second, dependent gather.
+__global__ void __launch_bounds__(kSelThreads) topk_finish_kernel(SelectArgs a) {
+  const int srow = blockIdx.x;
+  const int k = a.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* out = a.topk + (int64_t)srow * k;
+  const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+  const int nw4 = a.slices * (kSelThreads / 4);   // uint4 words of the row's part bitmaps
+  const uint4* pb = reinterpret_cast<const uint4*>(a.part_bits + (int64_t)srow * a.slices * kSelThreads);
+  const uint32_t* pn = a.part_count + (int64_t)srow * a.slices;
+  const uint32_t* pc = a.part_cand + (int64_t)srow * a.slices * 2 * kCandCap;
+
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t tmp[64];
+  __shared__ uint32_t found[4];
+  __shared__ uint32_t soff[kMaxParts + 2];     // list offset of each part, the total, a spill flag
+  __shared__ uint32_t cand[2 * kCandCap];
+  __shared__ uint32_t bitmap[2 * kMaxWords];
+
+  // Everything this query needs goes out before any of it is used, in the
+  // order of use: histogram, counts, list entries, bitmap words.
+  const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
+  const uint32_t my_count = pn[tid < a.slices ? tid : 0];
+  const uint32_t S = (uint32_t)(kCandCap / a.slices) & ~7u;
+  const uint32_t j0 = 8u * (uint32_t)tid;      // this thread's entry slots j0 .. j0+7
+  const uint32_t ss = j0 / S;                  // their part
+  const uint32_t si = j0 - ss * S;             // their first entry in that part
+  const bool slot_ok = ss < (uint32_t)a.slices;
+  const uint4* sk = reinterpret_cast<const uint4*>(pc + (slot_ok ? ss * 2 * kCandCap + si : 0));
+  const uint4 sk0 = sk[0], sk1 = sk[1];
+  const uint4 sb0 = sk[kCandCap / 4], sb1 = sk[kCandCap / 4 + 1];
+  constexpr int kBw = 2 * kMaxWords / 4 / kSelThreads;   // uint4 words per thread: 8
+  uint4 bw[kBw];
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const uint32_t q[4] = {kv[v].x, kv[v].y, kv[v].z, kv[v].w};
+  for (int i = 0; i < kBw; i++) {
+    const int j = i * kSelThreads + tid;
+    bw[i] = pb[j < nw4 ? j : 0];
+  }
+  const int nv = visible_blocks(a, srow);
+  if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
+  threshold_bin(hv0, hv1, (uint32_t)k, tmp, found, gh);
+  if (nv <= k) {
+    for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const int parts = (nv + kPartKeys - 1) / kPartKeys;
+  if (wave == 0) {
+    // part offsets by a wave scan over the counts (parts <= kMaxParts <= 64)
+    const uint32_t c = lane < parts ? my_count : 0u;
+    const uint32_t incl = wave_inclusive_scan(c);
+    if (lane < kMaxParts) soff[lane] = incl - c;
+    if (lane == 63) soff[kMaxParts] = incl;
+    const bool spill = __ballot(c > S) != 0;
+    if (lane == 0) soff[kMaxParts + 1] = spill ? 1u : 0u;
+  }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int e = 4 * v + i;
-          if ((eq[e >> 5] >> (e & 31)) & 1u) {
-            cand[pos] = q[i];
-            cand[kCandCap + pos] = (uint32_t)(b0 + e);
-            pos++;
+  for (int i = 0; i < kBw; i++) {
+    const int j = i * kSelThreads + tid;
+    if (j < nw4) reinterpret_cast<uint4*>(bitmap)[j] = bw[i];
+  }
+  __syncthreads();
+  const uint32_t tb = found[0], above = found[1];
+  const uint32_t nc = soff[kMaxParts];
+  if (nc <= (uint32_t)kCandCap) {
+    if (!soff[kMaxParts + 1]) {
+      // every list fits its S slots: place the loaded entries
+      if (slot_ok && ss < (uint32_t)parts) {
+        const uint32_t b = soff[ss], cnt = soff[ss + 1] - b;
+        const uint32_t ks[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
+        const uint32_t bs[8] = {sb0.x, sb0.y, sb0.z, sb0.w, sb1.x, sb1.y, sb1.z, sb1.w};
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          if (si + u < cnt) {
+            cand[b + si + u] = ks[u];
+            cand[kCandCap + b + si + u] = bs[u];
           }
         }
       }
-    }
-    nc += tot;
-  }
-
-  if (nc <= (uint32_t)kCandCap) {
-    // 3. exact threshold among the listed keys: bits 19..10, then 9..0.  A
-    // pass whose bin holds exactly the keys still needed ends the search:
-    // every listed key at or above that bin is taken.
-    uint32_t need = (uint32_t)k - above;
-    uint32_t pfx = tb;
-    int shift = 20;
-    bool exact = false;
-#pragma unroll 1
-    for (int pass = 0; pass < 2 && !exact; pass++) {
-      shift -= 10;
-      hist[2 * tid] = 0;
-      hist[2 * tid + 1] = 0;
-      if (tid == 0) found[0] = found[1] = found[2] = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < nc; i += kSelThreads) {
-        const uint32_t key = cand[i];
-        if ((key >> (shift + 10)) == pfx) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
-      }
-      __syncthreads();
-      find_bin_1024(hist[2 * tid], hist[2 * tid + 1], need, tmp, found);
-      need -= found[1];
-      pfx = (pfx << 10) | found[0];
-      exact = found[2] == need;      // the bin's keys are exactly the ones needed
-      __syncthreads();
-    }
-    // key >> shift compared with pfx: above -> taken; equal -> taken when the
-    // bin is exactly what is needed, else ranked by block (list) order
-    constexpr int kPerT = kCandCap / kSelThreads;
-    const uint32_t i0 = kPerT * tid;
-    uint32_t neq = 0;
+    } else {
+      // gather the lists: entry i of the row comes from the part r with
+      // soff[r] <= i < soff[r + 1]
+      uint32_t off[kMaxParts];
 #pragma unroll
-    for (int i = 0; i < kPerT; i++) {
-      const uint32_t j = i0 + i;
-      if (j < nc) {
-        const uint32_t kp = cand[j] >> shift;
-        if (kp > pfx || (exact && kp == pfx)) set_bit(bitmap, cand[kCandCap + j]);
-        neq += kp == pfx;
-      }
-    }
-    if (!exact) {
-      // shift is 0 here: pfx is the threshold key T, `need` keys equal to it
-      uint32_t tot;
-      uint32_t rank = block_exclusive_scan(neq, tmp, &tot);
+      for (int r = 0; r < kMaxParts; r++) off[r] = soff[r];
+      constexpr int kPerT = kCandCap / kSelThreads;
+      uint32_t ck[kPerT], cb[kPerT];
 #pragma unroll
-      for (int i = 0; i < kPerT; i++) {
-        const uint32_t j = i0 + i;
-        if (j < nc && cand[j] == pfx) {
-          if (rank < need) set_bit(bitmap, cand[kCandCap + j]);
-          rank++;
+      for (int u = 0; u < kPerT; u++) {
+        const uint32_t i = (uint32_t)(u * kSelThreads + tid);
+        uint32_t r = 0, o = 0;
+#pragma unroll
+        for (int t = 1; t < kMaxParts; t++) {
+          const bool in = t < parts && off[t] <= i;   // parts <= slices
+          r += in ? 1u : 0u;
+          o = in ? off[t] : o;
+        }
+        const uint32_t* src = pc + (int64_t)r * 2 * kCandCap;
+        const uint32_t e = i < nc ? i - o : 0u;
+        ck[u] = src[e];
+        cb[u] = src[kCandCap + e];
+      }
+#pragma unroll
+      for (int u = 0; u < kPerT; u++) {
+        const uint32_t i = (uint32_t)(u * kSelThreads + tid);
+        if (i < nc) {
+          cand[i] = ck[u];
+          cand[kCandCap + i] = cb[u];
         }
       }
     }
     __syncthreads();
+    rank_listed(cand, nc, tb, above, (uint32_t)k, hist, tmp, found, bitmap);
   } else {
-    const int nwords = (nv + 63) >> 6;
-    // Many keys share 24 high bits: radix select over every key (12 + 12 + 8
-    // bits), then every key above T and the lowest-index keys equal to T.
-    uint32_t pfx = 0, need = (uint32_t)k;
-#pragma unroll
-    for (int d = 0; d < 3; d++) {
-      const int shift = d == 0 ? 20 : (d == 1 ? 8 : 0), width = d == 2 ? 8 : 12;
-      const uint32_t nb = 1u << width, mask = nb - 1;
-      for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
-      __syncthreads();
-      for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
-        if (j < nv && (d == 0 || (key >> (shift + width)) == pfx))
-          atomicAdd(&hist[(key >> shift) & mask], 1u);
-      });
-      __syncthreads();
-      find_bin(hist, nb, need, tmp, found);
-      need -= found[1];
-      pfx = (pfx << width) | found[0];
-      __syncthreads();
-    }
-    const uint32_t T = pfx, need_eq = need;
-    // equal keys per 64-block word (cand_key doubles as the count array)
-    uint32_t* eqc = cand;       // 2 * kCandCap = kMaxWords counters
-    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
-      const uint64_t gm = __ballot(j < nv && key > T);
-      const uint64_t em = __ballot(j < nv && key == T);
-      if (lane == 0) {
-        bitmap[2 * w] = (uint32_t)gm;
-        bitmap[2 * w + 1] = (uint32_t)(gm >> 32);
-        eqc[w] = (uint32_t)__popcll(em);
-      }
-    });
-    __syncthreads();
-    const int wp = (nwords + kSelThreads - 1) / kSelThreads;
-    const int a0 = tid * wp, a1 = min(nwords, a0 + wp);
-    uint32_t loc = 0;
-    for (int w = a0; w < a1; w++) loc += eqc[w];
-    uint32_t tot;
-    uint32_t run = block_exclusive_scan(loc, tmp, &tot);
-    for (int w = a0; w < a1; w++) {
-      const uint32_t c = eqc[w];
-      eqc[w] = run;
-      run += c;
-    }
-    __syncthreads();
-    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
-      const bool eq = j < nv && key == T;
-      const uint64_t em = __ballot(eq);
-      const uint32_t rank = eqc[w] + (uint32_t)__popcll(em & ((1ull << lane) - 1ull));
-      if (eq && rank < need_eq) set_bit(bitmap, (uint32_t)j);
-    });
-    __syncthreads();
+    select_all(keys, nv, (uint32_t)k, hist, tmp, found, cand, bitmap);
   }
-
-  // 4. compaction: ascending block order, thread t owns a run of 32-bit words
-  const int wper = (nwords32 + kSelThreads - 1) / kSelThreads;
-  const int w0 = tid * wper, w1 = min(nwords32, w0 + wper);
-  uint32_t cnt = 0;
-  for (int w = w0; w < w1; w++) cnt += __popc(bitmap[w]);
-  uint32_t tot;
-  uint32_t pos = block_exclusive_scan(cnt, tmp, &tot);
-  for (int w = w0; w < w1; w++) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
-      pos++;
-    }
-  }
+  compact(bitmap, nv, k, out, tmp);
 }
 
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
@@ -711,8 +1018,18 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   if (cpw > chunks) cpw = chunks;
   pl.cpw = (int)cpw;
   pl.chunks = (int)((chunks + cpw - 1) / cpw);
-  pl.keys_bytes = (size_t)L->batch * n_q * pl.stride * sizeof(uint32_t);
-  pl.hist_bytes = (size_t)L->batch * n_q * kHistBins * sizeof(uint32_t);
+  pl.keys_bytes = (size_t)rows * pl.stride * sizeof(uint32_t);
+  pl.hist_bytes = (size_t)rows * kHistBins * sizeof(uint32_t);
+  // selection: parts of kPartKeys blocks on workgroups of their own when the
+  // rows are long and too few to fill the chip
+  bool sliced = pl.stride > kSliceMinBlocks && rows < kSliceMaxRows;
+  const char* senv = getenv("LCA_TOPK_SLICED");
+  if (senv && *senv) sliced = atoi(senv) != 0;
+  pl.slices = sliced ? (int)((pl.stride + kPartKeys - 1) / kPartKeys) : 0;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  pl.part_count_bytes = up((size_t)rows * pl.slices * sizeof(uint32_t));
+  pl.part_bits_bytes = (size_t)rows * pl.slices * kSelThreads * sizeof(uint32_t);
+  pl.part_cand_bytes = (size_t)rows * pl.slices * 2 * kCandCap * sizeof(uint32_t);
   return pl;
 }
 
@@ -748,8 +1065,19 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.keys = s.keys;
   sa.hist = s.hist;
   sa.topk = topk;
+  sa.slices = pl.slices;
+  char* part = static_cast<char*>(ws) + pl.hist_bytes + pl.keys_bytes;
+  sa.part_count = reinterpret_cast<uint32_t*>(part);
+  sa.part_bits = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes);
+  sa.part_cand = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes + pl.part_bits_bytes);
+  // one timed interval covers the selection's one or two launches
   TimedLaunch t(kKernelTopkSelect, stream);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);
+  if (pl.slices) {
+    hipLaunchKernelGGL(topk_slice_kernel, dim3(pl.slices, rows), dim3(kSelThreads), 0, stream, sa);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);
+  } else {
+    hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);
+  }
   return t.done();
 }
 

@@ -34,14 +34,18 @@ int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, c
                     const float* igate, int n, hipStream_t stream);
 
 // Indexer workspace: per-query key histograms [rows][4096] (zero between
-// calls), then scores as order-preserving uint32 keys [rows][stride].
-// rows = B * n_q.
+// calls), then scores as order-preserving uint32 keys [rows][stride], then,
+// when the selection is split over rounds, the per-(query, round) listed-key
+// counts, bitmap words and lists.  rows = B * n_q.
 struct IndexerPlan {
   int64_t stride;       // keys per score row (>= visible blocks of any query)
   int chunks;           // workgroups per score row
   int cpw;              // chunks of 1024 blocks per workgroup
+  int slices;           // selection rounds per query on their own workgroups (0: one workgroup)
   size_t keys_bytes;
   size_t hist_bytes;    // per-query histograms at the start of the workspace
+  size_t part_count_bytes, part_bits_bytes, part_cand_bytes;
+  size_t total() const { return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes; }
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,

@@ -118,6 +118,9 @@ INDEXER_CASES = [
     ("h20_two_groups", 2, [2500, 2600], 2, 20, 100, 0),
     ("h32_k2048", 1, [12000], 1, 32, 2048, 0),
     ("k_ge_visible", 2, [200, 37], 1, 8, 64, 0),
+    # more than one selection round of 32768 blocks
+    ("long_rows_h16_k512", 2, [140000, 70000], 1, 16, 512, 16),
+    ("long_nq2_h8_k256", 1, [200000], 2, 8, 256, 0),
 ]
 
 
@@ -134,12 +137,18 @@ def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed):
     return ref, lay, Q
 
 
+@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
 @pytest.mark.parametrize("case", INDEXER_CASES, ids=[c[0] for c in INDEXER_CASES])
-def test_indexer_topk_parity(case):
+def test_indexer_topk_parity(case, sliced, monkeypatch):
+    """sliced="1" forces the selection that spreads a query's rounds over
+    workgroups (taken by itself for few long rows)"""
     lca = _lca()
     name, B, lens, n_q, H_I, k, needles = case
     seed = 3000 + len(name)
-    say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed)
+    say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed,
+        "sliced", sliced)
+    if sliced:
+        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
     ref, lay, Q = _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed)
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
     torch.cuda.synchronize()
@@ -149,10 +158,10 @@ def test_indexer_topk_parity(case):
     ws = lay._ws["indexer"]
     nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
     hist_bytes = B * n_q * 4096 * 4
-    stride = (nbytes - hist_bytes) // (4 * B * n_q)
+    stride = max(64, (max(lens) // 4 + 63) // 64 * 64)
     wsh = ws[:nbytes].view(torch.int32).cpu().numpy().view(np.uint32)
     assert not wsh[: hist_bytes // 4].any()          # histograms left zeroed for the next call
-    keys = wsh[hist_bytes // 4:].reshape(B * n_q, stride)
+    keys = wsh[hist_bytes // 4: hist_bytes // 4 + B * n_q * stride].reshape(B * n_q, stride)
     for b in range(B):
         for qi in range(n_q):
             sc = oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"])
@@ -169,11 +178,15 @@ def test_indexer_topk_parity(case):
             assert set(nd) <= set(got[b, -1].tolist())
 
 
-def test_indexer_equal_scores_take_lowest_indices():
+@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
+@pytest.mark.parametrize("B,L", [(1, 4000), (2, 140000)], ids=["short", "long"])
+def test_indexer_equal_scores_take_lowest_indices(B, L, sliced, monkeypatch):
     lca = _lca()
-    say("indexer equal scores")
-    B, m, L, k = 1, 4, 4000, 50
-    ref = SL.make_layer(77, "eq", B, m, 128, 256, 1, L // m + 4, [L])
+    say("indexer equal scores", B, L, "sliced", sliced)
+    if sliced:
+        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
+    m, k = 4, 50
+    ref = SL.make_layer(77, "eq", B, m, 128, 256, 1, L // m + 4, [L] * B)
     ref["idx_code"][:] = 0x22          # every key identical
     ref["idx_scale"][:] = 127
     Q = SL.queries(77, "eq", B, 1, 16, 4)
@@ -181,15 +194,20 @@ def test_indexer_equal_scores_take_lowest_indices():
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k).cpu().numpy()
     want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
     assert np.array_equal(got, want)
-    assert list(got[0, 0]) == list(range(k))
+    for b in range(B):
+        assert list(got[b, 0]) == list(range(k))
 
 
-def test_indexer_near_equal_scores():
+@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
+@pytest.mark.parametrize("L", [48000, 140000], ids=["one_round", "two_rounds"])
+def test_indexer_near_equal_scores(L, sliced, monkeypatch):
     """Most scores share their high bits (keys differ in one byte): exercises
     the second-level candidate selection."""
     lca = _lca()
-    say("indexer near-equal scores")
-    B, m, L, k = 2, 4, 48000, 512
+    say("indexer near-equal scores", L, "sliced", sliced)
+    if sliced:
+        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
+    B, m, k = 2, 4, 512
     ref = SL.make_layer(78, "neq", B, m, 128, 256, 1, L // m + 4, [L, L - 7])
     rng = np.random.default_rng(78)
     pattern = rng.integers(0, 256, 32).astype(np.uint8)
