@@ -295,8 +295,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     float mx = x[0];
 #pragma unroll
     for (int j = 1; j < 8; j++) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = fmaxf(mx, swap_rows(mx));
+    mx = fmaxf(mx, swap_halves(mx));
     // move the reference only when the tile's maximum exceeds it by more
     // than the headroom (always on the first key seen)
     if (__any(mx > mrow + kLazyMax)) {
@@ -331,8 +331,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   }
 
   if (!active) return;
-  lrow += __shfl_xor(lrow, 16, kWave);
-  lrow += __shfl_xor(lrow, 32, kWave);
+  lrow += swap_rows(lrow);
+  lrow += swap_halves(lrow);
   if (a.splits == 1) {
     if (hq < a.H) {
       const float inv = 1.0f / lrow;

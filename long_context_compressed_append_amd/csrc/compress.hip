@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
           code = f32_e2m1(ldexpf(y, -X));
           ebyte = (uint32_t)(X + 127);
         }
-        uint32_t hi = __shfl_xor(code, 1, kWave);
+        uint32_t hi = lane_xor1(code);
         if ((lane & 1) == 0) a.idx_code[e * 32 + (lane >> 1)] = (uint8_t)(code | (hi << 4));
         if ((lane & 31) == 0) a.idx_scale[e * 2 + (lane >> 5)] = (uint8_t)ebyte;
       }

@@ -93,7 +93,7 @@ __device__ __noinline__ float score_unscaled(v8i A0, v8i A1, v8i Bm, int hgroups
                                         (hv ? q_exp[h][1] : 0) + ke1), 0.0f);
       part = __builtin_fmaf(hv ? q_w[h] : 0.0f, rl, part);
     }
-    const float upper = __shfl_xor(part, 32, kWave);
+    const float upper = swap_halves(part);
     total = (hg == 0) ? part : __fadd_rn(total, part);
     total = __fadd_rn(total, upper);
   }
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
       X = X < -127 ? -127 : (X > 127 ? 127 : X);
       code = f32_e2m1(ldexpf(x, -X));
     }
-    uint32_t hi = __shfl_xor(code, 1, kWave);
+    uint32_t hi = lane_xor1(code);
     const int h = e >> 6, el = e & 63;
     if ((el & 1) == 0) q_code[h][el >> 1] = (uint8_t)(code | (hi << 4));
     if ((el & 31) == 0) q_exp[h][el >> 5] = X;
@@ -216,14 +216,8 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   {
     // extremes of the query's 2H block exponents: lane l looks at entry l
     const int e = lane < 2 * a.H ? q_exp[lane >> 1][lane & 1] : 0;
-    int lo = lane < 2 * a.H ? e : (1 << 20), hi = lane < 2 * a.H ? e : -(1 << 20);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      lo = min(lo, __shfl_xor(lo, o, kWave));
-      hi = max(hi, __shfl_xor(hi, o, kWave));
-    }
-    qmin = lo;
-    qmax = hi;
+    qmin = wave_minmax<0>(lane < 2 * a.H ? e : (1 << 20));
+    qmax = wave_minmax<1>(lane < 2 * a.H ? e : -(1 << 20));
   }
 
   uint32_t* out = a.keys + (int64_t)srow * a.stride;
@@ -268,7 +262,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
                                        fmaxf(__fadd_rn(acc[u][2 * hl], acc[u][2 * hl + 1]), 0.0f), part[u]);
           }
 #pragma unroll
-          for (int u = 0; u < kDepth; u++) upper[u] = __shfl_xor(part[u], 32, kWave);
+          for (int u = 0; u < kDepth; u++) upper[u] = swap_halves(part[u]);
 #pragma unroll
           for (int u = 0; u < kDepth; u++) {
             total[u] = (hg == 0) ? part[u] : __fadd_rn(total[u], part[u]);
@@ -305,10 +299,13 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   }
   __syncthreads();
   uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256) {
-    const uint32_t c = lhist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
+  // every count is read before any atomic goes out
+  uint32_t hc[kHistBins / 256];
+#pragma unroll
+  for (int i = 0; i < kHistBins / 256; i++) hc[i] = lhist[tid + 256 * i];
+#pragma unroll
+  for (int i = 0; i < kHistBins / 256; i++)
+    if (hc[i]) atomicAdd(&gh[tid + 256 * i], hc[i]);
 }
 
 // ---------------------------------------------------------------------------

@@ -79,18 +79,78 @@ __device__ __forceinline__ int floor_log2(float a) {
   return (31 - __clz((int)(u & 0x7FFFFFu))) - 149;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Lane reductions on DPP moves (no LDS round trips).  A step combines each
+// lane with the lane `ctrl` names; a lane whose source lies outside its row,
+// or whose row is masked off, combines with itself.  Shifts by 1, 2, 4 and 8
+// leave in lane 15 of every 16-lane row the reduction of the row; the
+// broadcast of lane 15 into the next row (rows 1 and 3) then leaves that of
+// lanes 0-31 in lane 31 and of lanes 32-63 in lane 63, and the broadcast of
+// lane 31 into rows 2 and 3 that of the wave in lane 63.
+constexpr int kDppRowShr = 0x110, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_max(float x) {
+  const int xi = __float_as_int(x);
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, kCtrl, kRowMask, 0xf, false)));
+}
+
+template <int kOp, int kCtrl, int kRowMask>   // kOp 0: min, 1: max
+__device__ __forceinline__ int dpp_minmax(int x) {
+  const int y = __builtin_amdgcn_update_dpp(x, x, kCtrl, kRowMask, 0xf, false);
+  return kOp ? max(x, y) : min(x, y);
+}
+
+__device__ __forceinline__ float row_max_steps(float v) {
+  v = dpp_max<kDppRowShr + 1, 0xf>(v);
+  v = dpp_max<kDppRowShr + 2, 0xf>(v);
+  v = dpp_max<kDppRowShr + 4, 0xf>(v);
+  v = dpp_max<kDppRowShr + 8, 0xf>(v);
+  return dpp_max<kDppRowBcast15, 0xa>(v);
+}
+
+// max over the wave, in every lane
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max<kDppRowBcast31, 0xc>(row_max_steps(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // max over the 32-lane half of the wave that the caller is in
 __device__ __forceinline__ float half_wave_max(float v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = row_max_steps(v);
+  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return (threadIdx.x & 32) ? hi : lo;
+}
+
+// min (kOp 0) or max (kOp 1) over the wave, in every lane
+template <int kOp>
+__device__ __forceinline__ int wave_minmax(int v) {
+  v = dpp_minmax<kOp, kDppRowShr + 1, 0xf>(v);
+  v = dpp_minmax<kOp, kDppRowShr + 2, 0xf>(v);
+  v = dpp_minmax<kOp, kDppRowShr + 4, 0xf>(v);
+  v = dpp_minmax<kOp, kDppRowShr + 8, 0xf>(v);
+  v = dpp_minmax<kOp, kDppRowBcast15, 0xa>(v);
+  v = dpp_minmax<kOp, kDppRowBcast31, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// the value of lane l ^ 32 (gfx950 permlane32 swap: a VALU op)
+__device__ __forceinline__ float swap_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// the value of lane l ^ 16 (gfx950 permlane16 swap: odd rows with even rows)
+__device__ __forceinline__ float swap_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// the value of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2)
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false);
 }
 
 __device__ __forceinline__ uint32_t ord_key(float s) {
