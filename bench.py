@@ -53,6 +53,17 @@ INTERLEAVED = {
 }
 
 
+# Prefill chunk: one row with a prior context given as a cache image, then a
+# chunk of new tokens through compress_append, indexer_topk for every chunk
+# query (causal) and csa_attend.
+# name: (prior tokens, chunk, ratio, heads, indexer heads, k, window, ring)
+PREFILL = {
+    "csa_prefill_chunk": (262144, 4096, 4, 64, 16, 512, 128, 8192),
+}
+FP8_MFMA_PEAK_TFLOPS = 5000.0      # dense FP8-rate matrix peak (the scoring's FP8-rate reference)
+FP4_MFMA_PEAK_TFLOPS = 10100.0     # dense MXFP4 matrix peak
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -152,6 +163,144 @@ def interleaved_bytes(B, ctx, H_c, HI, k, H_h, W):
     csa = B * ((ctx // 4) * 34 + HI * 260 + 2 * k * 4 + k * 604 + W * 1024 + H_c * 1024 + H_c * 2048)
     hca = B * ((ctx // 128) * 604 + W * 1024 + H_h * 1024 + H_h * 2048)
     return csa, hca
+
+
+def prefill_score_flops(prior, n, m, HI):
+    """Scoring work of a chunk: every visible (query, block) pair, H_I heads x
+    64-d dot products (2 flops per multiply-add)."""
+    pairs = sum((prior + i + 1) // m for i in range(n))
+    return pairs * HI * 64 * 2, pairs
+
+
+def run_prefill(args):
+    import torch
+    import long_context_compressed_append_amd as lca
+    from synth import layers as SL
+
+    prior, n, m, H, HI, k, W, R = PREFILL[args.workload]
+    seed, tag = 1004, "prefill"
+    t = time.time()
+    ref = SL.make_layer(seed, tag, 1, m, W, R, 1, (prior + n) // m + 64, [prior])
+    tok = SL.tokens(seed, "chunk", 1, n, 1)
+    Q = SL.queries(seed, tag, 1, n, H, HI)
+    log(f"host image built in {time.time() - t:.1f}s")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    lay = lca.Layer.from_host(ref, device=dev)
+    d_tok = {kk: up(v) for kk, v in tok.items()}
+    iq, iw, q = up(Q["iq"]), up(Q["iw"]), up(Q["q"])
+    topk = torch.empty((1, n, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, n, H, 512), dtype=torch.float32, device=dev)
+    scale = float(1.0 / np.sqrt(512.0))
+
+    def reset():                      # back to the prior context (outside the timed kernels)
+        lay.seq_len.fill_(prior)
+        lay.len_min = lay.len_max = prior
+
+    def step():
+        lca.compress_append(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"])
+        lca.indexer_topk(lay, iq, iw, k, out=topk)
+        lca.csa_attend(lay, q, topk, scale, out=out)
+
+    for _ in range(args.warmup):
+        reset()
+        step()
+    torch.cuda.synchronize()
+    # whole steps between HIP events on the stream the library launches on
+    # (torch's current stream), then each kernel alone (every launch
+    # bracketed by events) over further steps
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(args.steps):
+        reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms_per_step = float(np.median(times))
+    kernels = {}
+    for name in ("compress", "indexer_score", "topk_select", "attend", "attend_combine"):
+        with lca.KernelTimer(name) as kt:
+            for _ in range(max(1, args.steps // 4)):
+                reset()
+                step()
+            torch.cuda.synchronize()
+        if kt.launches:
+            kernels[name] = round(kt.total_ms * 1e3 / kt.launches, 1)
+    flops, pairs = prefill_score_flops(prior, n, m, HI)
+    score_us = kernels.get("indexer_score", 0.0)
+    tflops = flops / (score_us * 1e-6) / 1e12 if score_us else 0.0
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = prefill_cpu_baseline(ref, tok, Q, prior, n, m, k)
+        except Exception as e:  # report, never hide
+            cpu = dict(error=repr(e))
+    res = {
+        "metric": METRIC,
+        "value": round(n / (ms_per_step / 1e3), 1),
+        "unit": "queries/s (prefill chunk tokens through compress + indexer + top-k + attention)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4 scoring (exact fp32 scores); fp8/bf16 storage; bf16/fp16 MFMA attention",
+        "data": "synthetic (seeded cache image of the prior context, N(0,1) chunk)",
+        "config": {
+            "workload": args.workload, "batch": 1, "prior_tokens": prior, "chunk": n, "ratio": m,
+            "heads": H, "indexer_heads": HI, "topk": k, "window": W, "ring": R,
+            "kernel_us": kernels,
+            "score_visible_pairs": pairs,
+            "score_flops": flops,
+            "score_fp4_peak_frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4),
+        },
+        "roofline": {
+            "kernel": "indexer_score", "bound": "mfma", "achieved": round(tflops, 1),
+            "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel_avg_us": score_us, "flops_per_launch": flops,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k):
+    """The oracle on a sample of the chunk: the whole compress_append, then
+    indexer_topk and csa_attend for 4 of the chunk's queries (each on a view
+    whose length ends at that query)."""
+    import oracle
+    nthreads = min(16, len(os.sched_getaffinity(0)))
+    scale = np.float32(1.0 / np.sqrt(512.0))
+    V = oracle.row_view(ref, 0)
+    t0 = time.perf_counter()
+    oracle.compress_append(V, tok["kv"], tok["gate"], tok["ikey"], tok["igate"])
+    t_comp = time.perf_counter() - t0
+    sample = (0, n // 3, 2 * n // 3, n - 1)
+    t0 = time.perf_counter()
+    for qi in sample:
+        Vq = dict(V)
+        Vq["seq_len"] = np.array([prior + qi + 1], np.int32)
+        tk = oracle.indexer_topk(Vq, Q["iq"][:, qi:qi + 1], Q["iw"][:, qi:qi + 1], k, nthreads=nthreads)
+        oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], tk, scale, nthreads=nthreads)
+    t_q = (time.perf_counter() - t0) / len(sample)
+    per_chunk = t_comp + t_q * n
+    return dict(value=n / per_chunk, unit="queries/s", cores=nthreads, kind="oracle",
+                sample=f"compress_append of the {n}-token chunk ({t_comp:.2f}s) plus indexer_topk + "
+                       f"csa_attend for {len(sample)} of its queries ({t_q:.2f}s each), scaled to "
+                       f"the chunk")
 
 
 def run_interleaved(args):
@@ -297,7 +446,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="csa_decode_128k",
-                    choices=sorted(WORKLOADS) + sorted(INTERLEAVED))
+                    choices=sorted(WORKLOADS) + sorted(INTERLEAVED) + sorted(PREFILL))
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -315,6 +464,10 @@ def main():
 
     if args.workload in INTERLEAVED:
         return run_interleaved(args)
+    if args.workload in PREFILL:
+        if args.steps == 200 and args.warmup == 16:     # defaults sized for decode steps
+            args.steps, args.warmup = 12, 2
+        return run_prefill(args)
 
     import torch
     import long_context_compressed_append_amd as lca

@@ -309,6 +309,287 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Scores for many queries per row (prefill chunks): a workgroup takes Qwg
+// consecutive queries of one row and a range of blocks, so every key is read
+// from memory once per Qwg queries rather than once per query.
+//
+// One 32x32x64 FP4 product per query pair (H <= 16) or per query (H <= 32)
+// and 32 blocks: row r = 8i + 4s + j of the A operand is
+//   H <= 16: query 2m + i/2 of the wavefront's set, head 8s + 4(i%2) + j
+//   H <= 32: query m, head 16(i/2) + 8s + 4(i%2) + j
+// and carries the head's whole 64-d MXFP4 vector (lanes l and l + 32 give its
+// two MX halves with their own E8M0 scales), so lane l's 16 outputs are the
+// dot products of its block (column l % 32) with the heads of head group s =
+// l / 32 of its queries.  With both halves in one product the hardware adds
+// two scaled partial sums; the result is still the exactly rounded dot when
+// every partial sum is an fp32 number: each half's products are multiples of
+// 2^(E-2) below 1152 * 2^E (E = query exponent + key exponent of the half),
+// so with |E0 - E1| <= 10 and both E in [-124, 116] every partial sum is a
+// multiple of 2^(min E - 2) below 2^(max E + 12) and needs at most 24 bits.
+// Iterations where some (row, column) leaves these bounds take the per-half
+// path (two unscaled products, scales applied exactly per output).
+// Each lane runs the head chains of its group for its queries; one permlane
+// swap brings the other group's partial, and lane l < 32 (l >= 32) finishes
+// the first (second) query of the pair.
+// ---------------------------------------------------------------------------
+
+constexpr int kTileWaves = 8;
+constexpr int kTileMinQueries = 16;                  // rows with at least this many queries
+constexpr int kTileTargetWGs = 1024;
+constexpr int kTileSets = 1;                         // query sets per workgroup
+constexpr int kTileWavesPerSet = kTileWaves / kTileSets;
+
+// max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
+// set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
+// output would first be canonicalised, a second instruction.)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+template <int kQw>   // queries per wavefront: 8 (H <= 16) or 4 (H <= 32)
+__device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, int set,
+                                                const int (*q_exp)[32][2], int ke0, int ke1) {
+  // per-half products without scales, then each output's exact value
+  const v16f zero16 = {};
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const v8i A0 = kh ? zero8 : Am, A1 = kh ? Am : zero8;
+  const v16f D0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A0, Bm, zero16, 4, 4, 0, 127, 0, 127);
+  const v16f D1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A1, Bm, zero16, 4, 4, 0, 127, 0, 127);
+  const int s = (threadIdx.x & 63) >> 5;
+  v16f d;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int q = kQw == 8 ? set * kQw + 2 * m + (i >> 1) : set * kQw + m;
+      const int h = kQw == 8 ? 8 * s + 4 * (i & 1) + j : 16 * (i >> 1) + 8 * s + 4 * (i & 1) + j;
+      d[4 * i + j] = exact_pair(D0[4 * i + j], q_exp[q][h][0] + ke0, D1[4 * i + j], q_exp[q][h][1] + ke1);
+    }
+  return d;
+}
+
+template <int kQw>
+__global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(ScoreArgs a) {
+  constexpr int kQwg = kQw * kTileSets;               // queries per workgroup
+  constexpr int kNm = 4;                              // products per iteration
+  const int brow = blockIdx.z, qg = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int set = wave / kTileWavesPerSet, wv = wave % kTileWavesPerSet;
+  const int col = lane & 31, kh = lane >> 5;
+  const int q0 = qg * kQwg;                           // first query of the workgroup (row-local)
+
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kQwg][kHistBins];
+  __shared__ __attribute__((aligned(16))) uint8_t q_code[kQwg][32][32];
+  __shared__ int q_exp[kQwg][32][2];
+  __shared__ float q_w[kQwg][32];
+
+  // block indices fit int: max_blocks <= 524288
+  const int cap = (int)(a.stride < a.max_blocks ? a.stride : a.max_blocks);
+  const int b_lo = blockIdx.x * a.cpw * kScoreBlocksPerWG;
+  const int b_hi = b_lo + a.cpw * kScoreBlocksPerWG;
+  const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
+  const uint8_t* ks = a.idx_scale + (int64_t)brow * a.max_blocks * 2;
+
+  // queries: Qwg x H x 64 fp32 values, quantised one MX block per half-wave
+  const int nqv = min(kQwg, a.n_q - q0);              // queries of this workgroup
+  const float* qsrc = a.iq + ((int64_t)brow * a.n_q + q0) * a.H * kIdx;
+  const int qvals = kQwg * a.H * kIdx;
+  for (int i = tid; i < kQwg * kHistBins / 4; i += 64 * kTileWaves)
+    reinterpret_cast<uint4*>(&lh[0][0])[i] = make_uint4(0, 0, 0, 0);
+  for (int e0 = 0; e0 < qvals; e0 += 64 * kTileWaves) {
+    const int e = e0 + tid;                           // whole MX blocks per half-wave
+    const int q = e / (a.H * kIdx), rem = e % (a.H * kIdx);
+    const float x = (e < qvals && q < nqv) ? qsrc[e] : 0.0f;
+    const float amax = half_wave_max(fabsf(x));
+    uint32_t code = 0;
+    int X = -127;
+    if (amax > 0.0f) {
+      X = floor_log2(amax) - 2;
+      X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      code = f32_e2m1(ldexpf(x, -X));
+    }
+    const uint32_t hi = lane_xor1(code);
+    const int h = rem >> 6, el = rem & 63;
+    if (e < qvals) {
+      if ((el & 1) == 0) q_code[q][h][el >> 1] = (uint8_t)(code | (hi << 4));
+      if ((el & 31) == 0) q_exp[q][h][el >> 5] = X;
+    }
+  }
+  for (int i = tid; i < kQwg * 32; i += 64 * kTileWaves) {
+    const int q = i >> 5, h = i & 31;
+    q_w[q][h] = (h < a.H && q < nqv) ? a.iw[((int64_t)brow * a.n_q + q0 + q) * a.H + h] : 0.0f;
+  }
+  __syncthreads();
+
+  // A operands (row l % 32, K-half l / 32), their scales, the lane's weights
+  const int r = col, ri = r >> 3, rs = (r >> 2) & 1, rj = r & 3;
+  v8i A[kNm];
+  int sa[kNm];
+  float wt[kNm][16];
+#pragma unroll
+  for (int m = 0; m < kNm; m++) {
+    const int q = kQw == 8 ? set * kQw + 2 * m + (ri >> 1) : set * kQw + m;
+    const int h = kQw == 8 ? 8 * rs + 4 * (ri & 1) + rj : 16 * (ri >> 1) + 8 * rs + 4 * (ri & 1) + rj;
+    const bool ok = h < a.H;
+    const int* src = reinterpret_cast<const int*>(&q_code[q][ok ? h : 0][16 * kh]);
+    A[m] = (v8i){ok ? src[0] : 0, ok ? src[1] : 0, ok ? src[2] : 0, ok ? src[3] : 0, 0, 0, 0, 0};
+    sa[m] = ok ? q_exp[q][h][kh] + 127 : 127;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int qo = kQw == 8 ? set * kQw + 2 * m + (i >> 1) : set * kQw + m;
+        const int ho = kQw == 8 ? 8 * kh + 4 * (i & 1) + j : 16 * (i >> 1) + 8 * kh + 4 * (i & 1) + j;
+        wt[m][4 * i + j] = q_w[qo][ho];       // 0 past H (the chain is unchanged)
+      }
+  }
+  // exponent bounds of this set's query halves: the exact fast path needs
+  // |(ea0 + eb0) - (ea1 + eb1)| <= 10 and every ea + eb in [-124, 116]
+  int emin = 1 << 20, emax = -(1 << 20), dmin = 1 << 20, dmax = -(1 << 20);
+  for (int i = lane; i < kQw * 32; i += 64) {
+    const int q = set * kQw + (i >> 5), h = i & 31;
+    if (h < a.H && q < nqv) {
+      const int e0 = q_exp[q][h][0], e1 = q_exp[q][h][1];
+      emin = min(emin, min(e0, e1));
+      emax = max(emax, max(e0, e1));
+      dmin = min(dmin, e0 - e1);
+      dmax = max(dmax, e0 - e1);
+    }
+  }
+  emin = wave_minmax<0>(emin);
+  emax = wave_minmax<1>(emax);
+  dmin = wave_minmax<0>(dmin);
+  dmax = wave_minmax<1>(dmax);
+
+  // visible blocks of the wavefront's queries (query q0 + set * kQw + u)
+  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+  const int len = *(const_i32p)(a.seq_len + brow);
+  int nvq[kQw];
+  int nv_hi = 0;
+#pragma unroll
+  for (int u = 0; u < kQw; u++) {
+    const int q = q0 + set * kQw + u;
+    const int p = len - a.n_q + q;
+    int nv = q < a.n_q ? (p + 1) / a.m : 0;
+    if (nv > cap) nv = cap;
+    nvq[u] = nv;
+    nv_hi = nv > nv_hi ? nv : nv_hi;
+  }
+  const int b_end = b_hi < nv_hi ? b_hi : nv_hi;
+  // lane l < 32 stores query 2m (H <= 16) or m of the pair, lane l >= 32 the other
+  uint32_t* outq[kNm];
+  int nvl[kNm];
+  uint32_t* lhq[kNm];
+#pragma unroll
+  for (int m = 0; m < kNm; m++) {
+    const int u = kQw == 8 ? 2 * m + kh : m;          // H <= 32: both halves hold query m
+    outq[m] = a.keys + ((int64_t)brow * a.n_q + q0 + set * kQw + u) * a.stride;
+    nvl[m] = (kQw == 8 || kh == 0) ? nvq[u] : 0;     // H <= 32: one store per query
+    lhq[m] = &lh[set * kQw + u][0];
+  }
+
+  const v16f zero16 = {};
+  // iteration t covers blocks b_lo + 32 (wv + t * kTileWavesPerSet) + col; the
+  // keys of kRing iterations are in flight (a block past the key row reads
+  // block 0; what is not scored is masked)
+  constexpr int kRing = 4;
+  const int n_it = b_end > b_lo ? (b_end - b_lo + 32 * kTileWavesPerSet - 1) / (32 * kTileWavesPerSet) : 0;
+  auto blk_of = [&](int t) -> int { return b_lo + 32 * (wv + t * kTileWavesPerSet) + col; };
+  int4 kr[kRing];
+  uint32_t erw[kRing];
+  auto load = [&](int t, int4& k4, uint32_t& e2) {
+    const int blk = blk_of(t);
+    const int bl = (t < n_it && blk < cap) ? blk : 0;
+    k4 = *reinterpret_cast<const int4*>(kc + bl * 32 + 16 * kh);
+    e2 = *reinterpret_cast<const uint16_t*>(ks + bl * 2);
+  };
+#pragma unroll
+  for (int u = 0; u < kRing; u++) load(u, kr[u], erw[u]);
+
+  // Guard bounds on the key's raw E8M0 bytes (b = e + 127): both bytes in
+  // [blo, bhi] and b0 - b1 in [dlo, dhi] (unsigned range compares).
+  const int blo = -124 - emin + 127, bhi = 116 - emax + 127;
+  const int dlo = -10 - dmin, dhi = 10 - dmax;
+  const bool fast_possible = blo <= bhi && dlo <= dhi;   // else every iteration takes the per-half path
+  struct Dots {
+    v16f d[kNm];
+  };
+  // the products of iteration t (matrix cores, or the per-half path)
+  auto dots = [&](int t, const int4& k4, uint32_t e2) {
+    const int blk = blk_of(t);
+    const uint32_t er = blk < b_end ? e2 : 0x7F7Fu;          // unscored blocks: unit scales
+    const int b0 = (int)(er & 0xFF), b1 = (int)(er >> 8);
+    const bool ok = fast_possible & ((uint32_t)(b0 - blo) <= (uint32_t)(bhi - blo)) &
+                    ((uint32_t)(b1 - blo) <= (uint32_t)(bhi - blo)) & ((uint32_t)(b0 - b1 - dlo) <= (uint32_t)(dhi - dlo));
+    const v8i Bm = (v8i){k4.x, k4.y, k4.z, k4.w, 0, 0, 0, 0};
+    Dots r;
+    if (__all(ok)) {
+      const int sb = kh ? b1 : b0;
+#pragma unroll
+      for (int m = 0; m < kNm; m++)
+        r.d[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[m], Bm, zero16, 4, 4, 0, sa[m], 0, sb);
+    } else {
+#pragma unroll
+      for (int m = 0; m < kNm; m++)
+        r.d[m] = tile_dots_unscaled<kQw>(A[m], Bm, kh, m, set, q_exp, b0 - 127, b1 - 127);
+    }
+    return r;
+  };
+  // head chains (groups of 8 heads), the two groups' partials meet, keys
+  auto finish = [&](int t, const Dots& D) {
+    const int blk = blk_of(t);
+#pragma unroll
+    for (int m = 0; m < kNm; m++) {
+      float p[2] = {0.0f, 0.0f};          // i = 0, 1 -> p[0]; i = 2, 3 -> p[1]
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          p[i >> 1] = __builtin_fmaf(wt[m][4 * i + j], relu_bits(D.d[m][4 * i + j]), p[i >> 1]);
+      float score;
+      if (kQw == 8) {
+        // p[0]: group s of query 2m, p[1]: group s of query 2m + 1.  After the
+        // swap lane l < 32 holds (group 0, group 1) of query 2m, lane l >= 32
+        // those of query 2m + 1.
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false,
+                                                         false);
+        score = __fadd_rn(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      } else {
+        // p[0]: group s, p[1]: group 2 + s of query m: ((g0 + g1) + g2) + g3
+        const float o0 = swap_halves(p[0]), o1 = swap_halves(p[1]);
+        score = __fadd_rn(__fadd_rn(__fadd_rn(kh ? o0 : p[0], kh ? p[0] : o0), kh ? o1 : p[1]), kh ? p[1] : o1);
+      }
+      // no -0: every chain starts at +0 and each fma result is exact-rounded
+      // from a sum that is -0 only when both terms are
+      if (blk < nvl[m]) {
+        const uint32_t key = ord_key(score);
+        outq[m][blk] = key;
+        atomicAdd(&lhq[m][key >> kHistShift], 1u);
+      }
+    }
+  };
+#pragma unroll 1
+  for (int t0 = 0; t0 < n_it; t0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; u++) {
+      const Dots D = dots(t0 + u, kr[u], erw[u]);
+      load(t0 + u + kRing, kr[u], erw[u]);
+      finish(t0 + u, D);
+    }
+  }
+  __syncthreads();
+  // flush the histograms of the workgroup's queries
+#pragma unroll 1
+  for (int q = 0; q < nqv; q++) {
+    uint32_t* gh = a.hist + ((int64_t)brow * a.n_q + q0 + q) * kHistBins;
+    uint32_t hc[kHistBins / (64 * kTileWaves)];
+#pragma unroll
+    for (int i = 0; i < kHistBins / (64 * kTileWaves); i++) hc[i] = lh[q][tid + 64 * kTileWaves * i];
+#pragma unroll
+    for (int i = 0; i < kHistBins / (64 * kTileWaves); i++)
+      if (hc[i]) atomicAdd(&gh[tid + 64 * kTileWaves * i], hc[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Exact top-k by (score desc, block asc) for one query, on workgroups of 512
 // threads.  Keys are taken in rounds of 32768 blocks; in a round, thread t
 // owns the 64 blocks 64t .. 64t+63 (two 32-bit bitmap words).
@@ -1015,6 +1296,22 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   if (cpw > chunks) cpw = chunks;
   pl.cpw = (int)cpw;
   pl.chunks = (int)((chunks + cpw - 1) / cpw);
+  // many queries per row: the tile kernel (key tiles shared by the queries)
+  pl.tile = 0;
+  pl.qgroups = 0;
+  bool tile = n_q >= kTileMinQueries && H_I <= 32;
+  const char* tenv = getenv("LCA_SCORE_TILE");
+  if (tenv && *tenv) tile = atoi(tenv) != 0 && H_I <= 32;
+  if (tile) {
+    pl.tile = H_I <= 16 ? 8 : 4;
+    pl.qgroups = (n_q + pl.tile * kTileSets - 1) / (pl.tile * kTileSets);
+    int64_t tcpw = ((int64_t)L->batch * pl.qgroups * chunks + kTileTargetWGs - 1) / kTileTargetWGs;
+    if (env && *env) tcpw = atoi(env);
+    if (tcpw < 1) tcpw = 1;
+    if (tcpw > chunks) tcpw = chunks;
+    pl.cpw = (int)tcpw;
+    pl.chunks = (int)((chunks + tcpw - 1) / tcpw);
+  }
   pl.keys_bytes = (size_t)rows * pl.stride * sizeof(uint32_t);
   pl.hist_bytes = (size_t)rows * kHistBins * sizeof(uint32_t);
   // selection: parts of kPartKeys blocks on workgroups of their own when the
@@ -1049,7 +1346,14 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.hist_bytes);
   {
     TimedLaunch t(kKernelIndexerScore, stream);
-    hipLaunchKernelGGL(indexer_score_kernel, dim3(pl.chunks, rows), dim3(256), 0, stream, s);
+    if (pl.tile == 8)
+      hipLaunchKernelGGL(indexer_score_tile_kernel<8>, dim3(pl.chunks, pl.qgroups, L->batch),
+                         dim3(64 * kTileWaves), 0, stream, s);
+    else if (pl.tile == 4)
+      hipLaunchKernelGGL(indexer_score_tile_kernel<4>, dim3(pl.chunks, pl.qgroups, L->batch),
+                         dim3(64 * kTileWaves), 0, stream, s);
+    else
+      hipLaunchKernelGGL(indexer_score_kernel, dim3(pl.chunks, rows), dim3(256), 0, stream, s);
     int rc = t.done();
     if (rc) return rc;
   }

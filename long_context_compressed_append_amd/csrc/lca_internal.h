@@ -41,7 +41,9 @@ struct IndexerPlan {
   int64_t stride;       // keys per score row (>= visible blocks of any query)
   int chunks;           // workgroups per score row
   int cpw;              // chunks of 1024 blocks per workgroup
-  int slices;           // selection rounds per query on their own workgroups (0: one workgroup)
+  int slices;           // selection parts per query on their own workgroups (0: one workgroup)
+  int tile;             // 0: one query per score workgroup; 8 or 4: queries per wavefront of the tile kernel
+  int qgroups;          // tile kernel: query groups per row
   size_t keys_bytes;
   size_t hist_bytes;    // per-query histograms at the start of the workspace
   size_t part_count_bytes, part_bits_bytes, part_cand_bytes;

@@ -121,7 +121,16 @@ INDEXER_CASES = [
     # more than one selection round of 32768 blocks
     ("long_rows_h16_k512", 2, [140000, 70000], 1, 16, 512, 16),
     ("long_nq2_h8_k256", 1, [200000], 2, 8, 256, 0),
+    # many queries per row (prefill chunks)
+    ("chunk_nq64_h16_k256", 2, [30000, 20011], 64, 16, 256, 0),
+    ("chunk_nq37_h32_k128", 1, [9000], 37, 32, 128, 0),
+    ("chunk_nq20_h5_k64", 2, [3000, 2100], 20, 5, 64, 0),
 ]
+
+# environment switches: the selection split over workgroups, the score
+# kernel that shares key tiles across a row's queries
+INDEXER_MODES = {"auto": {}, "sliced": {"LCA_TOPK_SLICED": "1"}, "tile": {"LCA_SCORE_TILE": "1"},
+                 "no_tile": {"LCA_SCORE_TILE": "0"}}
 
 
 def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed):
@@ -137,18 +146,15 @@ def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed):
     return ref, lay, Q
 
 
-@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
+@pytest.mark.parametrize("mode", list(INDEXER_MODES))
 @pytest.mark.parametrize("case", INDEXER_CASES, ids=[c[0] for c in INDEXER_CASES])
-def test_indexer_topk_parity(case, sliced, monkeypatch):
-    """sliced="1" forces the selection that spreads a query's rounds over
-    workgroups (taken by itself for few long rows)"""
+def test_indexer_topk_parity(case, mode, monkeypatch):
     lca = _lca()
     name, B, lens, n_q, H_I, k, needles = case
     seed = 3000 + len(name)
-    say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed,
-        "sliced", sliced)
-    if sliced:
-        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
+    say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed, "mode", mode)
+    for var, val in INDEXER_MODES[mode].items():
+        monkeypatch.setenv(var, val)
     ref, lay, Q = _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed)
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
     torch.cuda.synchronize()
@@ -218,6 +224,33 @@ def test_indexer_near_equal_scores(L, sliced, monkeypatch):
     lay = lca.Layer.from_host(ref)
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k).cpu().numpy()
     want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("mode", ["tile", "no_tile"])
+def test_indexer_exponent_extremes(mode, monkeypatch):
+    """Key halves with E8M0 scales up to 12 apart and query halves scaled by
+    2^20 or 2^-12: the products of the two MX halves can no longer be added
+    inside one matrix-core product without rounding, so the per-half path
+    runs.  (Exponent gaps stay below ~35 so that the oracle's double sum of
+    the two halves is itself exact.)"""
+    lca = _lca()
+    say("indexer exponent extremes", mode)
+    for var, val in INDEXER_MODES[mode].items():
+        monkeypatch.setenv(var, val)
+    B, m, L, n_q, H_I, k = 2, 4, 6000, 24, 16, 100
+    ref = SL.make_layer(79, "ext", B, m, 128, 256, 1, L // m + 4, [L, L - 3])
+    rng = np.random.default_rng(79)
+    sc = ref["idx_scale"]
+    sel = rng.random(sc.shape[:2]) < 0.3
+    sc[sel, 0] = np.clip(sc[sel, 0].astype(np.int32) + rng.integers(-12, 13, sel.sum()), 1, 254).astype(np.uint8)
+    Q = SL.queries(79, "ext", B, n_q, 16, H_I)
+    iq = Q["iq"].copy()
+    iq[:, :8, :, :32] *= np.float32(2.0 ** 20)      # the first query group: per-half path throughout
+    iq[:, 9::3, 3, 32:] *= np.float32(2.0 ** -12)
+    lay = lca.Layer.from_host(ref)
+    got = lca.indexer_topk(lay, _dev(iq), _dev(Q["iw"]), k).cpu().numpy()
+    want = oracle.indexer_topk(ref, iq, Q["iw"], k)
     assert np.array_equal(got, want)
 
 
