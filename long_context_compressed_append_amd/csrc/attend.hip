@@ -9,26 +9,32 @@
 // tokens stay at raw precision; entries are FP8 with BF16 RoPE dims.
 //
 // All query heads of a row share one 512-d key/value vector per key, so a
-// workgroup stages each key once in LDS and 8 wavefronts use it: wavefront w
-// takes heads 16(w % 4) .. +15 of its head group and channel half w / 4.
-// Every product is computed transposed, keys x heads, so that a lane owns one
-// head throughout: lane l holds head l % 16 and key / channel quarter l / 16.
-//   S^T = K Q^T   bf16 matrix cores over the wavefront's 256 channels: a
-//                 staged key holds the exact bf16 value of each e4m3 code (or
-//                 the raw bf16 window token); the per-64-dim FP8 scale
-//                 multiplies each 64-dim partial dot in fp32.  The two halves
-//                 add their partial scores through LDS.  Lane l ends with keys
-//                 4(l/16)+r and 16+4(l/16)+r of its head.
+// workgroup stages each key once in LDS and 8 compute wavefronts use it:
+// wavefront w takes heads 16(w % 4) .. +15 of its head group and channel half
+// w / 4.  Four more wavefronts only stage: while the compute wavefronts work
+// on tile t from one LDS buffer they load tile t + 2 and convert tile t + 1
+// into the other, so the loads and conversions leave the critical path.
+// A staged key is one fp16 image serving as K and as V: the exact value of
+// each e4m3 code (e4m3 values are fp16 numbers), or the bf16 RoPE / window
+// value (exact within fp16's normal range).  The query is converted to fp16
+// the same way.  Every product is computed transposed, keys x heads, so that
+// a lane owns one head throughout: lane l holds head l % 16 and key / channel
+// quarter l / 16.
+//   S^T = K Q^T   fp16 matrix cores over the wavefront's 256 channels; the
+//                 per-64-dim FP8 scale multiplies each 64-dim partial dot in
+//                 fp32.  The two halves add their partial scores through LDS.
+//                 Lane l ends with keys 4(l/16)+r and 16+4(l/16)+r of its head.
 //   softmax       online, base 2, per lane (one head) plus a max over the four
 //                 lanes that share the head; the running maximum is only
 //                 moved when it grows by more than 2^8, so rescaling is rare
-//                 and P (<= 256) stays in registers as fp16.
+//                 and P (<= 256) stays in registers.
 //   O^T = V^T P^T fp16 matrix cores: the k-slots of the product are the eight
-//                 keys the lane already holds, so P^T is the B operand as is;
-//                 the V^T operand (fp16(code * scale) or the window token,
-//                 staged [key][channel]) comes from the LDS transpose read
-//                 ds_read_b64_tr_b16.  Lane l accumulates channels
-//                 16 ct + 4(l/16) + r of its head for the 16 ct of its half.
+//                 keys the lane already holds, so P^T is the B operand; since
+//                 the tile holds code values, the B operand of a 64-dim group
+//                 is fp16(p * that group's scale of the key).  The V^T operand
+//                 comes from the LDS transpose read ds_read_b64_tr_b16.  Lane
+//                 l accumulates channels 16 ct + 4(l/16) + r of its head for
+//                 the 16 ct of its half.
 // Each workgroup covers a contiguous chunk of the key list; chunks are merged
 // by the combine kernel (or written directly when there is one chunk).
 #include "lca_device.h"
@@ -36,7 +42,6 @@
 
 namespace lca {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -45,12 +50,9 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;          // keys per tile
-// Row pitches: a K row is 1040 bytes (16 mod 256), so 16 lanes writing or
-// reading one 16-byte chunk of 16 consecutive keys hit distinct banks; a V row
-// is 1056 bytes (32 mod 256), so the 8-byte transpose reads of 8 keys x 4
+// Row pitch 1056 bytes (32 mod 256): the 8-byte transpose reads of 8 keys x 4
 // chunks by 32 lanes cover all banks once.
-constexpr int kKst = 520;          // bf16 per staged key row (512 + 8 pad)
-constexpr int kVst = 528;          // fp16 per staged value row (512 + 16 pad)
+constexpr int kVst = 528;          // fp16 per staged key row (512 + 16 pad)
 constexpr int kMaxChunk = 1024;    // keys per split workgroup (list entries staged in LDS)
 constexpr int kAttendTargetWGs = 256;
 
@@ -70,7 +72,9 @@ struct AttendArgs {
   _Float16* ws_o;
 };
 
-constexpr int kThreads = 512;
+constexpr int kComputeWaves = 8;   // 4 head wavefronts x 2 channel halves
+constexpr int kStageWaves = 4;     // wavefronts that load and convert the next tile
+constexpr int kThreads = 64 * (kComputeWaves + kStageWaves);
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running maximum
 
 // Raw data of one staged (key, 32-dim half group) slot, loaded one tile ahead.
@@ -81,31 +85,33 @@ struct StageRegs {
 };
 
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKst];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[kTile * kVst];
-  __shared__ __attribute__((aligned(16))) float sK[8 * kTile];     // [group][key]
-  __shared__ __attribute__((aligned(16))) float kbias[kTile];      // 0, or -inf for a masked key
-  __shared__ __attribute__((aligned(16))) float Sx[8 * 64 * 8];    // partial scores per wave / lane
+  // two tile buffers: the compute wavefronts read tile t from buffer t % 2
+  // while the staging wavefronts convert tile t + 1 into the other
+  __shared__ __attribute__((aligned(16))) _Float16 Ts[2][kTile * kVst];   // [key][channel]
+  __shared__ __attribute__((aligned(16))) float sK[2][8 * kTile];     // [group][key]
+  __shared__ __attribute__((aligned(16))) float kbias[2][kTile];      // 0, or -inf for a masked key
+  __shared__ __attribute__((aligned(16))) float Sx[8 * 64 * 8];       // partial scores per wave / lane
   __shared__ int klist[kMaxChunk];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hw = wave & 3, half = wave >> 2;  // head wavefront, channel half
+  const bool computes = wave < kComputeWaves;
+  const int hw = wave & 3, half = (wave >> 2) & 1;   // head wavefront, channel half (compute wavefronts)
   const int srow = blockIdx.y, split = blockIdx.x, hgrp = blockIdx.z;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
   const int h0 = hgrp * 64 + hw * 16;
-  const bool active = h0 < a.H;
+  const bool active = computes && h0 < a.H;
   const int hq = h0 + (lane & 15);            // this lane's head
   const int g = lane >> 4;                    // this lane's key / channel quarter
   const int kq = 8 * g;                       // K offset of this lane inside a 32-K step
 
-  v8bf qf[8];   // q of this lane's head, channels 256 half + 32 ks + 8 g .. +7
+  v8h qf[8];   // q of this lane's head (fp16 image of the bf16 input), channels 256 half + 32 ks + 8 g .. +7
   {
     const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv + 256 * half;
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (active && hq < a.H) v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + kq);
-      qf[ks] = __builtin_bit_cast(v8bf, v);
+      qf[ks] = bf16x8_to_f16(v);
     }
   }
 
@@ -133,14 +139,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   float mrow = -INFINITY, lrow = 0.0f;
   __syncthreads();   // klist
 
-  // staging: key sj, 64-dim group sg, 32-dim part sp; wavefront w stages
-  // group w of 32 keys (so a wavefront's slots are all of one kind)
-  const int sj = lane & 31, sg = wave, sp = lane >> 5;
+  // staging: key sj, 32-dim part sp; staging wavefront w stages the 64-dim
+  // groups w and w + 4 of the 32 keys (a wavefront's slots of one group are
+  // all of one kind)
+  const int sj = lane & 31, sp = lane >> 5, sw = wave - kComputeWaves;
   // Issue the global loads of this thread's slot of the tile at t0.  Every
   // lane issues the same four 16-byte loads (a masked slot reads a harmless
   // in-bounds address, an FP8 part reads its 32 bytes twice), so the loads
   // of one tile never wait on one another.
-  auto stage_load = [&](int t0, StageRegs& st) {
+  auto stage_load = [&](int t0, int sg, StageRegs& st) {
     const int kk = t0 + sj;
     int kind = 0;
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.ring_kv);
@@ -175,60 +182,40 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     st.s = *scp;
     st.kind = kind;
   };
-  // Convert the loaded slot into the LDS tile: K as exact bf16 values, V as
-  // fp16(value * scale), both [key][channel]; the group scale and key mask.
-  auto stage_store = [&](const StageRegs& st) {
-    uint16_t* kdst = Ks + sj * kKst + sg * 64 + sp * 32;
-    _Float16* vdst = Vs + sj * kVst + sg * 64 + sp * 32;
+  // Convert the loaded slot into the LDS tile, one fp16 image per key that
+  // serves as K and as V: an FP8 code's value exactly (e4m3 values are fp16
+  // numbers), a bf16 RoPE or window value exactly when it lies in fp16's
+  // normal range; then the group scale and the key mask.
+  auto stage_store = [&](const StageRegs& st, int sg, int buf) {
+    uint4* tdst = reinterpret_cast<uint4*>(Ts[buf] + sj * kVst + sg * 64 + sp * 32);
     if (st.kind == 1) {
 #pragma unroll
       for (int v = 0; v < 2; v++) {
         const uint32_t w4[4] = {st.d[v].x, st.d[v].y, st.d[v].z, st.d[v].w};
-        uint32_t kb4[8], vb4[8];
+        uint32_t hb[8];
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) {
-            // two codes -> exact fp32 (OCP e4m3 on gfx950), bf16 bits for K,
-            // fp16(value * scale) for V
+            // two codes -> exact fp32 (OCP e4m3 on gfx950) -> exact fp16
             const v2f f = hh ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], true)
                              : __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[q4], false);
-            kb4[q4 * 2 + hh] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
-            const v2f sv = {__fmul_rn(f[0], st.s), __fmul_rn(f[1], st.s)};
-            vb4[q4 * 2 + hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(sv, v2h));
+            hb[q4 * 2 + hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
           }
         }
-        uint4* kd = reinterpret_cast<uint4*>(kdst + v * 16);
-        kd[0] = make_uint4(kb4[0], kb4[1], kb4[2], kb4[3]);
-        kd[1] = make_uint4(kb4[4], kb4[5], kb4[6], kb4[7]);
-        uint4* vd = reinterpret_cast<uint4*>(vdst + v * 16);
-        vd[0] = make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]);
-        vd[1] = make_uint4(vb4[4], vb4[5], vb4[6], vb4[7]);
+        tdst[2 * v] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        tdst[2 * v + 1] = make_uint4(hb[4], hb[5], hb[6], hb[7]);
       }
     } else if (st.kind >= 2) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const uint4 w = st.d[v];
-        reinterpret_cast<uint4*>(kdst)[v] = w;
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        uint32_t vb4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          const v2f f = {__uint_as_float(ww[q4] << 16), __uint_as_float(ww[q4] & 0xFFFF0000u)};
-          vb4[q4] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
-        }
-        reinterpret_cast<uint4*>(vdst)[v] = make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]);
-      }
+      for (int v = 0; v < 4; v++) tdst[v] = __builtin_bit_cast(uint4, bf16x8_to_f16(st.d[v]));
     } else {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        reinterpret_cast<uint4*>(kdst)[v] = make_uint4(0, 0, 0, 0);
-        reinterpret_cast<uint4*>(vdst)[v] = make_uint4(0, 0, 0, 0);
-      }
+      for (int v = 0; v < 4; v++) tdst[v] = make_uint4(0, 0, 0, 0);
     }
-    if (sp == 0) sK[sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
+    if (sp == 0) sK[buf][sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
     // a key is valid when its first group is (every group of a key shares it)
-    if (sg == 0 && sp == 0) kbias[sj] = st.kind ? 0.0f : -INFINITY;
+    if (sg == 0 && sp == 0) kbias[buf][sj] = st.kind ? 0.0f : -INFINITY;
   };
 
   // LDS transpose-read addresses of the V^T operand: k-slot j of quarter g is
@@ -237,18 +224,51 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // 4j + i / 4, so lane L reads channels 16 ct + 4(L % 4) .. +3 of key
   // 4g + L / 4 (and of key 16 + 4g + L / 4 for the second read).
   const int Lq = lane & 15;
-  const _Float16* vrow0 = Vs + (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3) + 256 * half;
-  const _Float16* vrow1 = vrow0 + 16 * kVst;
-  float* sx_mine = Sx + (wave * 64 + lane) * 8;
-  const float* sx_other = Sx + ((wave ^ 4) * 64 + lane) * 8;
+  const int voff = (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3) + 256 * half;
+  const int koff = Lq * kVst + kq + 256 * half;
+  float* sx_mine = Sx + ((wave & 7) * 64 + lane) * 8;
+  const float* sx_other = Sx + (((wave & 7) ^ 4) * 64 + lane) * 8;
 
-  StageRegs st;
-  if (kb < ke) stage_load(kb, st);
-  for (int t0 = kb; t0 < ke; t0 += kTile) {
-    __syncthreads();                       // the previous tile is consumed
-    stage_store(st);
-    if (t0 + kTile < ke) stage_load(t0 + kTile, st);   // next tile in flight
+  // Staging wavefronts: tile 0 into buffer 0 before the loop; during tile t
+  // they store tile t + 1 (loaded a tile earlier) into the other buffer and
+  // load tile t + 2, group sw before the mid-tile barrier and group sw + 4
+  // after it.  Every wavefront passes the same two barriers per tile.
+  // (Two separate loops, so that the staging registers and the compute
+  // registers are never live at once.)
+  if (!computes) {
+    StageRegs stA, stB;
+    if (kb < ke) {
+      stage_load(kb, sw, stA);
+      stage_load(kb, sw + 4, stB);
+      stage_store(stA, sw, 0);
+      stage_store(stB, sw + 4, 0);
+      if (kb + kTile < ke) {
+        stage_load(kb + kTile, sw, stA);
+        stage_load(kb + kTile, sw + 4, stB);
+      }
+    }
     __syncthreads();
+    int cur = 0;
+    for (int t0 = kb; t0 < ke; t0 += kTile, cur ^= 1) {
+      if (t0 + kTile < ke) {
+        stage_store(stA, sw, cur ^ 1);
+        if (t0 + 2 * kTile < ke) stage_load(t0 + 2 * kTile, sw, stA);
+      }
+      __syncthreads();                     // (the compute wavefronts' partial-score exchange)
+      if (t0 + kTile < ke) {
+        stage_store(stB, sw + 4, cur ^ 1);
+        if (t0 + 2 * kTile < ke) stage_load(t0 + 2 * kTile, sw + 4, stB);
+      }
+      __syncthreads();                     // tile t + 1 staged, tile t consumed
+    }
+    return;
+  }
+  __syncthreads();                         // tile 0 staged
+  int cur = 0;
+  for (int t0 = kb; t0 < ke; t0 += kTile, cur ^= 1) {
+    const _Float16* Kc = Ts[cur] + koff;
+    const _Float16* vrow0 = Ts[cur] + voff;
+    const _Float16* vrow1 = vrow0 + 16 * kVst;
 
     // partial S^T = K Q^T over this half's channels, 32 keys x 16 heads,
     // per 64-dim group scaled in fp32
@@ -256,17 +276,17 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; nt++) {
       S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = Ks + (nt * 16 + Lq) * kKst + kq + 256 * half;
+      const _Float16* krow = Kc + nt * 16 * kVst;
 #pragma unroll
       for (int gl = 0; gl < 4; gl++) {
         v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; s2++) {
           const int ks = 2 * gl + s2;
-          const v8bf kb8 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(krow + ks * 32));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qf[ks], acc, 0, 0, 0);
+          const v8h kh8 = *reinterpret_cast<const v8h*>(krow + ks * 32);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh8, qf[ks], acc, 0, 0, 0);
         }
-        const v4f sc = *reinterpret_cast<const v4f*>(sK + (4 * half + gl) * kTile + nt * 16 + 4 * g);
+        const v4f sc = *reinterpret_cast<const v4f*>(sK[cur] + (4 * half + gl) * kTile + nt * 16 + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc[r], acc[r], S[nt][r]);
       }
@@ -284,8 +304,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       }
     }
     // online softmax (base 2) of this lane's head over its eight keys
-    const v4f kb0 = *reinterpret_cast<const v4f*>(kbias + 4 * g);
-    const v4f kb1 = *reinterpret_cast<const v4f*>(kbias + 16 + 4 * g);
+    const v4f kb0 = *reinterpret_cast<const v4f*>(kbias[cur] + 4 * g);
+    const v4f kb1 = *reinterpret_cast<const v4f*>(kbias[cur] + 16 + 4 * g);
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -311,16 +331,30 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       mrow = mnew;
     }
     const float mref = mrow == -INFINITY ? 0.0f : mrow;          // no key seen yet
-    v8h pb;
+    float pj[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const float pj = __builtin_amdgcn_exp2f(x[j] - mref);
-      lrow += pj;
-      pb[j] = (_Float16)pj;
+      pj[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+      lrow += pj[j];
+    }
+    // the tile holds code values, so each 64-dim group's FP8 scale goes into
+    // P: B operand of group gl = fp16(p_j * scale of key j's group)
+    v8h pbg[4];
+#pragma unroll
+    for (int gl = 0; gl < 4; gl++) {
+      const float* sg0 = sK[cur] + (4 * half + gl) * kTile + 4 * g;
+      const v4f s0 = *reinterpret_cast<const v4f*>(sg0);
+      const v4f s1 = *reinterpret_cast<const v4f*>(sg0 + 16);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        pbg[gl][r] = (_Float16)__fmul_rn(pj[r], s0[r]);
+        pbg[gl][4 + r] = (_Float16)__fmul_rn(pj[4 + r], s1[r]);
+      }
     }
     // O^T += V^T P^T over this half's 16 channel tiles
 #pragma unroll
     for (int c = 0; c < 16; c++) {
+      const v8h pb = pbg[c >> 2];
       typedef __attribute__((address_space(3))) v4s lds_v4s;
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
@@ -328,6 +362,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
       O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
     }
+    __syncthreads();                       // tile t + 1 staged, tile t consumed
   }
 
   if (!active) return;

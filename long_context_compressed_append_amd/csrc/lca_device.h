@@ -153,6 +153,24 @@ __device__ __forceinline__ uint32_t lane_xor1(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false);
 }
 
+// eight bf16 values (uint4) as fp16: exact for values in fp16's normal
+// range (bf16 keeps 8 significant bits, fp16 11)
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8h_t bf16x8_to_f16(uint4 w) {
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  v8h_t r;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const v2f_t f = {__uint_as_float(ww[i] << 16), __uint_as_float(ww[i] & 0xFFFF0000u)};
+    const v2h_t h = __builtin_convertvector(f, v2h_t);
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint32_t ord_key(float s) {
   uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
