@@ -169,6 +169,27 @@ int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
  * that every call leaves zero-filled again.
  */
 size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k);
+
+/*
+ * lca_indexer_layout -- where lca_indexer_topk leaves each query's scores in
+ * its workspace, for callers that inspect them (host only, enqueues nothing).
+ * Same arguments as lca_indexer_workspace; out receives 8 values:
+ *   out[0] stride S (key slots per query row), out[1] byte offset of the
+ *   uint32 keys [B * n_q][S]; a key is the score's order key (the fp32 bits,
+ *   all bits flipped for a negative score, the sign bit set otherwise).
+ *   out[2] 0: key slot b holds block b's key for every visible block b.
+ *   out[2] 1: candidate lists.  Only keys that can be among the query's top k
+ *   are kept, and the area at out[1] holds uint32 pairs (key, t) [B * n_q][S]
+ *   instead.  The query has out[5] lists; the length of list i is entry i
+ *   of the uint32 array [B * n_q][out[5]] at byte offset out[4].  With
+ *   W = out[6] and span = out[7], list i = 32 (c W + v) + col (c, v, col with
+ *   v < W, col < 32) has entry j in slot c * span + 32 v + 32 W j + col, and
+ *   that entry's t names block c * span + 32 (v + W t) + col.  Every block
+ *   whose key lies in the top-12-bit bin of the query's k-th largest key, or
+ *   above it, is in some list.  Unused entries of out are -1 or 0.
+ * Returns LCA_OK or LCA_EINVAL (NULL layer or out, n_q < 1).
+ */
+int lca_indexer_layout(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k, int64_t *out);
 int lca_indexer_topk(const lca_layer *layer, const float *iq, const float *iw, int32_t n_q,
                      int32_t H_I, int32_t k, int32_t *topk, void *ws, size_t ws_bytes,
                      hipStream_t stream);

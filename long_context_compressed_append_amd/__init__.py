@@ -65,6 +65,7 @@ def lib():
         L.lca_compress_append.argtypes = [LP, P, P, P, P, C.c_int32, P]
         L.lca_indexer_workspace.restype = C.c_size_t
         L.lca_indexer_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
+        L.lca_indexer_layout.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
         L.lca_indexer_topk.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_size_t, P]
         L.lca_attend_workspace.restype = C.c_size_t
         L.lca_attend_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
@@ -234,6 +235,18 @@ def compress_append(layer: Layer, kv, gate, ikey=None, igate=None):
 def indexer_workspace_bytes(layer: Layer, n_q, H_I, k):
     s = layer.struct()
     return lib().lca_indexer_workspace(C.byref(s), n_q, H_I, k)
+
+
+def indexer_layout(layer: Layer, n_q, H_I, k):
+    """Where the indexer's workspace holds each query's order keys: a dict
+    with stride, keys (byte offset), cand (bool) and, for candidate lists,
+    counts (byte offset), lists, waves and span."""
+    s = layer.struct()
+    out = (C.c_int64 * 8)()
+    _check(lib().lca_indexer_layout(C.byref(s), n_q, H_I, k, out))
+    v = list(out)
+    return {"stride": v[0], "keys": v[1], "cand": bool(v[2]), "counts": v[4], "lists": v[5],
+            "waves": v[6], "span": v[7]}
 
 
 def indexer_topk(layer: Layer, iq, iw, k, out=None):

@@ -142,6 +142,23 @@ size_t lca_indexer_workspace(const lca_layer* L, int32_t n_q, int32_t H_I, int32
   return pl.total();
 }
 
+int lca_indexer_layout(const lca_layer* L, int32_t n_q, int32_t H_I, int32_t k, int64_t* out) {
+  if (!L || n_q < 1 || L->ratio < 1 || L->batch < 1) return set_error(LCA_EINVAL, "invalid layer or n_q");
+  if (!out) return set_error(LCA_EINVAL, "out is NULL");
+  IndexerPlan pl = plan_indexer(L, n_q, H_I, k);
+  const int64_t lists_at = (int64_t)(pl.hist_bytes + pl.keys_bytes + pl.part_count_bytes + pl.part_bits_bytes +
+                                     pl.part_cand_bytes);
+  out[0] = pl.stride;
+  out[1] = (int64_t)pl.hist_bytes;
+  out[2] = pl.cand ? 1 : 0;
+  out[3] = -1;
+  out[4] = pl.cand ? lists_at : -1;
+  out[5] = pl.cand_lists;
+  out[6] = pl.cand_waves;
+  out[7] = pl.cand_span;
+  return LCA_OK;
+}
+
 int lca_indexer_topk(const lca_layer* L, const float* iq, const float* iw, int32_t n_q, int32_t H_I,
                      int32_t k, int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_layer(L);

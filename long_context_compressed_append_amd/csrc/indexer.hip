@@ -49,6 +49,14 @@ constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 
+// buffer resources: dword 3 of the descriptor selects the raw 32-bit data
+// format (gfx9 layout).  Accesses at or past num_records are not performed
+// (loads give 0), which stores use to drop a lane without a branch.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kDropOffset = 0x80000000u;   // past every range used here
+
 struct ScoreArgs {
   int n_q, H, m;
   int64_t max_blocks, stride;
@@ -60,6 +68,10 @@ struct ScoreArgs {
   uint32_t* keys;
   uint32_t* hist;        // [rows][kHistBins], zero on entry
   int cpw;               // chunks of 1024 blocks per workgroup
+  int k;                 // blocks selected per query
+  // candidate lists (tile kernel): keys holds (key, visit) pairs [rows][stride];
+  // list lengths [rows][chunks][kTileWaves][32]
+  uint32_t* cand_count;
 };
 
 // exact value of D0 * 2^e0 + D1 * 2^e1 rounded once to fp32, where D0, D1 are
@@ -308,6 +320,22 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
     if (hc[i]) atomicAdd(&gh[tid + 256 * i], hc[i]);
 }
 
+// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the total of row 0 (lane 15) is added to row 1, that of row 2 (lane
+// 47) to row 3, and that of rows 0-1 (lane 31) to rows 2 and 3.  Lanes whose
+// source lies outside the row read 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xc, 0xf, false);
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Scores for many queries per row (prefill chunks): a workgroup takes Qwg
 // consecutive queries of one row and a range of blocks, so every key is read
@@ -331,6 +359,19 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 // Each lane runs the head chains of its group for its queries; one permlane
 // swap brings the other group's partial, and lane l < 32 (l >= 32) finishes
 // the first (second) query of the pair.
+//
+// Candidate lists (kCand): instead of one key per block, each lane keeps
+// only the keys that can still be among its query's k largest.  From time to
+// time (after 4, 8, 16, ... iterations) wavefront w reads the running
+// histogram of query w of the workgroup and finds the highest bin b whose
+// higher bins already hold k keys; keys in bin b or below cannot reach the
+// top k of the row, since the k-th largest key of the row lies above b.
+// A lane appends every key in a higher bin, with its iteration index t, as
+// a (key, t) pair to its own list, entry j taking the slot of the j-th block
+// the lane visits (block b_lo + 32 (w + 8 j) + column; the pair array has
+// the layout of the key rows, 8 bytes a slot).  The histogram still counts
+// every key, so the selection's threshold bin tb is exact, and every key of
+// bin tb and above is in some list.
 // ---------------------------------------------------------------------------
 
 constexpr int kTileWaves = 8;
@@ -343,6 +384,35 @@ constexpr int kTileWavesPerSet = kTileWaves / kTileSets;
 // set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
 // output would first be canonicalised, a second instruction.)
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// The highest bin b such that the bins above b hold at least k keys of the
+// histogram h (-1 when there is none), found by one wavefront while other
+// wavefronts may still be adding to h: every count read was reached, so at
+// least k keys above b exist in the end, whatever the interleaving.  Lane l
+// sums bins 64 l .. 64 l + 63; the lanes whose bins all have k keys above
+// them form a prefix 0 .. F-1, and in lane F, where the count from the top
+// crosses k, each lane takes one bin (from the top down) and a wave scan
+// gives the keys above it.  Wave-uniform result.
+__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k) {
+  const int lane = threadIdx.x & 63;
+  const uint4* hv = reinterpret_cast<const uint4*>(h) + 16 * lane;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const uint4 x = hv[i];
+    s += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = wave_inclusive_scan(s);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
+  const uint64_t cross = __ballot(above < k && above + s >= k);
+  if (cross == 0) return -1;                       // fewer than k keys
+  const int F = __ffsll((long long)cross) - 1;     // lanes 0 .. F-1: every bin qualifies
+  const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
+  const uint32_t c = h[64 * F + 63 - lane];       // lane j: the j-th bin of lane F from the top
+  const uint32_t ci = wave_inclusive_scan(c);
+  const uint64_t q = __ballot(aF + ci - c >= k);   // keys above that bin reach k
+  return 64 * F + __popcll(q) - 1;
+}
 
 template <int kQw>   // queries per wavefront: 8 (H <= 16) or 4 (H <= 32)
 __device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, int set,
@@ -366,12 +436,13 @@ __device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, i
   return d;
 }
 
-template <int kQw>
+template <int kQw, bool kCand>
 __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(ScoreArgs a) {
   constexpr int kQwg = kQw * kTileSets;               // queries per workgroup
   constexpr int kNm = 4;                              // products per iteration
   const int brow = blockIdx.z, qg = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar bases
   const int set = wave / kTileWavesPerSet, wv = wave % kTileWavesPerSet;
   const int col = lane & 31, kh = lane >> 5;
   const int q0 = qg * kQwg;                           // first query of the workgroup (row-local)
@@ -380,6 +451,7 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   __shared__ __attribute__((aligned(16))) uint8_t q_code[kQwg][32][32];
   __shared__ int q_exp[kQwg][32][2];
   __shared__ float q_w[kQwg][32];
+  __shared__ int thr_s[kQwg];                         // candidate lists: running threshold bins
 
   // block indices fit int: max_blocks <= 524288
   const int cap = (int)(a.stride < a.max_blocks ? a.stride : a.max_blocks);
@@ -413,6 +485,7 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
       if ((el & 31) == 0) q_exp[q][h][el >> 5] = X;
     }
   }
+  if (kCand && tid < kQwg) thr_s[tid] = -1;
   for (int i = tid; i < kQwg * 32; i += 64 * kTileWaves) {
     const int q = i >> 5, h = i & 31;
     q_w[q][h] = (h < a.H && q < nqv) ? a.iw[((int64_t)brow * a.n_q + q0 + q) * a.H + h] : 0.0f;
@@ -478,12 +551,21 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   uint32_t* outq[kNm];
   int nvl[kNm];
   uint32_t* lhq[kNm];
+  // candidate lists: the (key, t) pairs of the set's kQw query rows as one
+  // buffer; a lane's byte offset of its next list slot, its least key kept
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      a.keys + 2 * ((int64_t)brow * a.n_q + q0 + set * kQw) * a.stride, (short)0, (int)(kQw * a.stride * 8),
+      kBufferWord3);
+  uint32_t coff[kNm], kmin[kNm];
 #pragma unroll
   for (int m = 0; m < kNm; m++) {
     const int u = kQw == 8 ? 2 * m + kh : m;          // H <= 32: both halves hold query m
-    outq[m] = a.keys + ((int64_t)brow * a.n_q + q0 + set * kQw + u) * a.stride;
+    const int64_t row = (int64_t)brow * a.n_q + q0 + set * kQw + u;
+    outq[m] = a.keys + row * a.stride;
     nvl[m] = (kQw == 8 || kh == 0) ? nvq[u] : 0;     // H <= 32: one store per query
     lhq[m] = &lh[set * kQw + u][0];
+    coff[m] = (uint32_t)((u * a.stride + b_lo + 32 * wv + col) * 8);
+    kmin[m] = 0;
   }
 
   const v16f zero16 = {};
@@ -559,20 +641,46 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
       }
       // no -0: every chain starts at +0 and each fma result is exact-rounded
       // from a sum that is -0 only when both terms are
-      if (blk < nvl[m]) {
-        const uint32_t key = ord_key(score);
-        outq[m][blk] = key;
-        atomicAdd(&lhq[m][key >> kHistShift], 1u);
+      const uint32_t key = ord_key(score);
+      if (blk < nvl[m]) atomicAdd(&lhq[m][key >> kHistShift], 1u);
+      if (!kCand) {
+        if (blk < nvl[m]) outq[m][blk] = key;
+      } else {
+        // append (key, t) to the lane's list: the slot of its next visit
+        const bool c = blk < nvl[m] && key >= kmin[m];
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){key, (uint32_t)t}, crs, (int)(c ? coff[m] : kDropOffset), 0, 0);
+        coff[m] += c ? 8u * 32u * kTileWavesPerSet : 0u;
       }
     }
   };
 #pragma unroll 1
   for (int t0 = 0; t0 < n_it; t0 += kRing) {
+    if (kCand && t0 >= kRing && (t0 & (t0 - 1)) == 0) {
+      // wavefront w refreshes the bound of query w, then every lane takes the
+      // latest bounds of its queries (another wavefront's may be older: any
+      // value it has written is valid)
+      if (wv < kQw) thr_s[set * kQw + wv] = running_threshold(&lh[set * kQw + wv][0], (uint32_t)a.k);
+      // keys above bin b: key >= (b + 1) << 20
+#pragma unroll
+      for (int m = 0; m < kNm; m++) kmin[m] = (uint32_t)(thr_s[set * kQw + (kQw == 8 ? 2 * m + kh : m)] + 1) << kHistShift;
+    }
 #pragma unroll
     for (int u = 0; u < kRing; u++) {
       const Dots D = dots(t0 + u, kr[u], erw[u]);
       load(t0 + u + kRing, kr[u], erw[u]);
       finish(t0 + u, D);
+    }
+  }
+  if (kCand) {
+    // list lengths, [rows][chunks][kTileWavesPerSet][32 columns]
+#pragma unroll
+    for (int m = 0; m < kNm; m++) {
+      const int u = kQw == 8 ? 2 * m + kh : m;
+      const int q = q0 + set * kQw + u;
+      const uint32_t first = (uint32_t)((u * a.stride + b_lo + 32 * wv + col) * 8);
+      if ((kQw == 8 || kh == 0) && q < a.n_q)
+        a.cand_count[((((int64_t)brow * a.n_q + q) * gridDim.x + blockIdx.x) * kTileWavesPerSet + wv) * 32 + col] =
+            (coff[m] - first) / (8u * 32u * kTileWavesPerSet);
     }
   }
   __syncthreads();
@@ -628,6 +736,7 @@ constexpr int kMaxParts = 64 * kMaxWords / kPartKeys;     // 32
 constexpr int kDirectRank = 128;   // lists up to this long are ranked by direct comparison
 constexpr int kSliceMaxRows = 256;   // the sliced path is taken below this many queries
 constexpr int kSliceMinBlocks = 3 * kRoundKeys / 2;   // ... and above this many blocks per row
+constexpr int kMaxCandGroups = 64;   // groups of 32 candidate lists per query (chunks x tile wavefronts)
 static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
 static_assert(kMaxParts <= 64 && kMaxParts * kSelThreads == 2 * kMaxWords, "part bookkeeping");
 static_assert(kDirectRank <= kSelThreads && kDirectRank <= 4096, "one list entry per thread, 12-bit positions");
@@ -645,23 +754,11 @@ struct SelectArgs {
   uint32_t* part_bits;
   uint32_t* part_count;
   uint32_t* part_cand;
+  // candidate lists of the tile kernel: segs = chunks x kTileWavesPerSet
+  // groups of 32 lists per query, chunk c starting at block c * span
+  const uint32_t* cand_count;
+  int segs, span;
 };
-
-// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
-// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
-// then the total of row 0 (lane 15) is added to row 1, that of row 2 (lane
-// 47) to row 3, and that of rows 0-1 (lane 31) to rows 2 and 3.  Lanes whose
-// source lies outside the row read 0.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xa, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xc, 0xf, false);
-  return x;
-}
 
 // exclusive prefix sum over the kSelThreads threads; returns the block total
 // in *total (tmp >= 32 words)
@@ -761,8 +858,6 @@ __device__ __forceinline__ void find_bin_1024(uint32_t c0, uint32_t c1, uint32_t
 // row's last 64 keys, which are masked at use.  Buffer loads keep each
 // 16-byte load whole (no re-split into overlapping pieces) and need no
 // per-round address registers; the descriptor's range is the key row.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit data format (gfx9 V# dword 3)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_row_rsrc(const uint32_t* keys, int64_t stride) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(keys), (short)0, (int)(stride * 4),
@@ -1278,6 +1373,205 @@ __global__ void __launch_bounds__(kSelThreads) topk_finish_kernel(SelectArgs a) 
   compact(bitmap, nv, k, out, tmp);
 }
 
+// ---------------------------------------------------------------------------
+// Selection from the candidate lists of the tile kernel, one workgroup per
+// query.  Step 1 as above (the histogram counts every key).  Step 2 walks the
+// lists: keys above bin tb set their bit, keys inside tb are listed in LDS in
+// no particular order.  Step 3 ranks the listed keys by (key desc, block asc)
+// -- directly for short lists, else by two radix passes over the key bits
+// and, when keys equal to the threshold key T must be split, two more over
+// the block indices of those keys.  If more than kCandCap keys share bin tb,
+// step 3 runs its passes over the lists in memory instead.  Step 4 compacts.
+// The bitmap is dynamic LDS of (stride + 31) / 32 words.
+// ---------------------------------------------------------------------------
+
+// f(ok, key, block) for every entry of the query's lists, called by all lanes
+// of a wavefront together (ok false where there is no entry).  The lists of
+// chunk c and tile wavefront v form group r = c * kTileWavesPerSet + v;
+// wavefront w takes groups w, w + 8, ...  Entry j of the list of column col
+// is the pair (key, t) in slot c * span + 32 (v + kTileWavesPerSet j) + col,
+// naming block c * span + 32 (v + kTileWavesPerSet t) + col.  Lanes l and
+// l + 32 read column l % 32 at levels j and j + 1.
+template <typename F>
+__device__ __forceinline__ void for_each_cand(const SelectArgs& a, const uint2* pairs, const uint32_t* cnt, F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  constexpr int kB = 8;
+#pragma unroll 1
+  for (int r = wave; r < a.segs; r += kSelWaves) {
+    const int c = r / kTileWavesPerSet, v = r % kTileWavesPerSet;
+    const uint32_t b0 = (uint32_t)(c * a.span + 32 * v + col);
+    const uint32_t n = cnt[32 * r + col];
+    const uint32_t nmax = (uint32_t)wave_minmax<1>((int)n);
+#pragma unroll 1
+    for (uint32_t j0 = 0; j0 < nmax; j0 += 2 * kB) {
+      uint2 e[kB];
+#pragma unroll
+      for (int u = 0; u < kB; u++) {
+        const uint32_t j = j0 + 2 * u + half;
+        e[u] = j < n ? pairs[b0 + 32u * kTileWavesPerSet * j] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; u++) {
+        const uint32_t j = j0 + 2 * u + half;
+        f(j < n, e[u].x, b0 + 32u * kTileWavesPerSet * e[u].y);
+      }
+    }
+  }
+}
+
+// Step 3 over unordered entries, all in bin tb: sets the bits of the `need`
+// largest by (key desc, block asc).  each(g) calls g(key, block) for every
+// entry, from any thread.
+template <typename Each>
+__device__ __forceinline__ void rank_unordered(Each each, uint32_t tb, uint32_t need, uint32_t* hist1024,
+                                               uint32_t* tmp, uint32_t* found, uint32_t* bitmap) {
+  const int tid = threadIdx.x;
+  // the threshold key T: bits 19..0 below the bin's 12
+  uint32_t need_k = need;
+  int shift;
+  uint32_t pfx = tb;
+  {
+    shift = 20;
+    bool exact = false;
+#pragma unroll 1
+    for (int pass = 0; pass < 2 && !exact; pass++) {
+      shift -= 10;
+      hist1024[2 * tid] = 0;
+      hist1024[2 * tid + 1] = 0;
+      if (tid == 0) found[0] = found[1] = found[2] = 0;
+      __syncthreads();
+      const int sh = shift;
+      const uint32_t pf = pfx;
+      each([&](uint32_t key, uint32_t) {
+        if ((key >> (sh + 10)) == pf) atomicAdd(&hist1024[(key >> sh) & 1023u], 1u);
+      });
+      __syncthreads();
+      find_bin_1024(hist1024[2 * tid], hist1024[2 * tid + 1], need_k, tmp, found);
+      need_k -= found[1];
+      pfx = (pfx << 10) | found[0];
+      exact = found[2] == need_k;
+      __syncthreads();
+    }
+    if (exact) {
+      each([&](uint32_t key, uint32_t blk) {
+        if ((key >> shift) >= pfx) set_bit(bitmap, blk);
+      });
+      __syncthreads();
+      return;
+    }
+  }
+  // shift is 0: pfx is T, and need_k of the keys equal to T are taken, those
+  // of the lowest blocks: the same passes over 0xFFFFF - block
+  const uint32_t T = pfx;
+  uint32_t vp = 0;
+  int vsh = 20;
+  bool vexact = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 && !vexact; pass++) {
+    vsh -= 10;
+    hist1024[2 * tid] = 0;
+    hist1024[2 * tid + 1] = 0;
+    if (tid == 0) found[0] = found[1] = found[2] = 0;
+    __syncthreads();
+    const int sh = vsh;
+    const uint32_t pf = vp;
+    each([&](uint32_t key, uint32_t blk) {
+      const uint32_t x = 0xFFFFFu - blk;
+      if (key == T && (x >> (sh + 10)) == pf) atomicAdd(&hist1024[(x >> sh) & 1023u], 1u);
+    });
+    __syncthreads();
+    find_bin_1024(hist1024[2 * tid], hist1024[2 * tid + 1], need_k, tmp, found);
+    need_k -= found[1];
+    vp = (vp << 10) | found[0];
+    vexact = found[2] == need_k;     // block indices are distinct: always true after the second pass
+    __syncthreads();
+  }
+  each([&](uint32_t key, uint32_t blk) {
+    if (key > T || (key == T && ((0xFFFFFu - blk) >> vsh) >= vp)) set_bit(bitmap, blk);
+  });
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kSelThreads) topk_cand_kernel(SelectArgs a) {
+  const int srow = blockIdx.x;
+  const int k = a.k, tid = threadIdx.x, lane = tid & 63;
+  int32_t* out = a.topk + (int64_t)srow * k;
+  const uint2* pairs = reinterpret_cast<const uint2*>(a.keys) + (int64_t)srow * a.stride;
+  const uint32_t* cnt = a.cand_count + (int64_t)srow * a.segs * 32;
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+
+  __shared__ uint32_t hist1024[1024];
+  __shared__ uint32_t tmp[64];
+  __shared__ uint32_t found[4];
+  __shared__ uint32_t nlist;
+  __shared__ uint32_t cand[2 * kCandCap];      // keys in bin tb, then their blocks
+  extern __shared__ uint32_t bitmap[];         // bit j of word w: block 32 w + j
+
+  const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
+  const int nv = visible_blocks(a, srow);
+  if (tid == 0) {
+    found[0] = found[1] = found[2] = found[3] = 0;
+    nlist = 0;
+  }
+  threshold_bin(hv0, hv1, (uint32_t)k, tmp, found, gh);
+  if (nv <= k) {
+    for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const int nwords32 = (nv + 31) >> 5;
+  for (int w = tid; w < nwords32; w += kSelThreads) bitmap[w] = 0u;
+  __syncthreads();
+  const uint32_t tb = found[0], above = found[1];
+  for_each_cand(a, pairs, cnt, [&](bool ok, uint32_t key, uint32_t blk) {
+    const uint32_t bin = key >> kHistShift;
+    if (ok && bin > tb) set_bit(bitmap, blk);
+    const bool in = ok && bin == tb;
+    const uint64_t bm = __ballot(in);
+    if (bm) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&nlist, (uint32_t)__popcll(bm));
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+      const uint32_t p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+      if (in && p < (uint32_t)kCandCap) {
+        cand[p] = key;
+        cand[kCandCap + p] = blk;
+      }
+    }
+  });
+  __syncthreads();
+  const uint32_t nc = nlist;
+  const uint32_t need = (uint32_t)k - above;
+  if (nc <= (uint32_t)kDirectRank) {
+    // short list: entry i is taken when fewer than `need` entries come before
+    // it in (key desc, block asc) order
+    if ((uint32_t)tid < nc) {
+      const uint32_t ki = cand[tid], bi = cand[kCandCap + tid];
+      uint32_t rank = 0;
+#pragma unroll 4
+      for (uint32_t j = 0; j < nc; j++) {
+        const uint32_t kj = cand[j], bj = cand[kCandCap + j];
+        rank += (kj > ki || (kj == ki && bj < bi)) ? 1u : 0u;
+      }
+      if (rank < need) set_bit(bitmap, bi);
+    }
+    __syncthreads();
+  } else if (nc <= (uint32_t)kCandCap) {
+    rank_unordered([&](auto g) {
+      for (uint32_t i = tid; i < nc; i += kSelThreads) g(cand[i], cand[kCandCap + i]);
+    }, tb, need, hist1024, tmp, found, bitmap);
+  } else {
+    // the lists in memory, keys of bin tb only
+    rank_unordered([&](auto g) {
+      for_each_cand(a, pairs, cnt, [&](bool ok, uint32_t key, uint32_t blk) {
+        if (ok && (key >> kHistShift) == tb) g(key, blk);
+      });
+    }, tb, need, hist1024, tmp, found, bitmap);
+  }
+  compact(bitmap, nv, k, out, tmp);
+}
+
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   (void)H_I;
   (void)k;
@@ -1319,11 +1613,22 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   bool sliced = pl.stride > kSliceMinBlocks && rows < kSliceMaxRows;
   const char* senv = getenv("LCA_TOPK_SLICED");
   if (senv && *senv) sliced = atoi(senv) != 0;
+  // tile kernel: candidate lists instead of full key rows, unless a row has
+  // too many lists (chunks x wavefronts) to gather
+  pl.cand = pl.tile && pl.chunks * kTileWavesPerSet <= kMaxCandGroups;
+  const char* cenv = getenv("LCA_TOPK_CAND");
+  if (cenv && *cenv) pl.cand = pl.tile && atoi(cenv) != 0;
+  if (pl.cand) sliced = false;
+  pl.cand_waves = kTileWavesPerSet;
+  pl.cand_lists = pl.cand ? pl.chunks * kTileWavesPerSet * 32 : 0;
+  pl.cand_span = pl.cpw * kScoreBlocksPerWG;
   pl.slices = sliced ? (int)((pl.stride + kPartKeys - 1) / kPartKeys) : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   pl.part_count_bytes = up((size_t)rows * pl.slices * sizeof(uint32_t));
   pl.part_bits_bytes = (size_t)rows * pl.slices * kSelThreads * sizeof(uint32_t);
   pl.part_cand_bytes = (size_t)rows * pl.slices * 2 * kCandCap * sizeof(uint32_t);
+  if (pl.cand) pl.keys_bytes *= 2;     // (key, visit) pairs
+  pl.cand_count_bytes = pl.cand ? up((size_t)rows * pl.chunks * kTileWavesPerSet * 32 * sizeof(uint32_t)) : 0;
   return pl;
 }
 
@@ -1344,14 +1649,21 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.hist = static_cast<uint32_t*>(ws);
   s.cpw = pl.cpw;
   s.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.hist_bytes);
+  s.k = k;
+  char* cand = static_cast<char*>(ws) + pl.hist_bytes + pl.keys_bytes + pl.part_count_bytes + pl.part_bits_bytes +
+               pl.part_cand_bytes;
+  s.cand_count = pl.cand ? reinterpret_cast<uint32_t*>(cand) : nullptr;
   {
     TimedLaunch t(kKernelIndexerScore, stream);
-    if (pl.tile == 8)
-      hipLaunchKernelGGL(indexer_score_tile_kernel<8>, dim3(pl.chunks, pl.qgroups, L->batch),
-                         dim3(64 * kTileWaves), 0, stream, s);
+    const dim3 tg(pl.chunks, pl.qgroups, L->batch), tb(64 * kTileWaves);
+    if (pl.tile == 8 && pl.cand)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<8, true>), tg, tb, 0, stream, s);
+    else if (pl.tile == 8)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<8, false>), tg, tb, 0, stream, s);
+    else if (pl.tile == 4 && pl.cand)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<4, true>), tg, tb, 0, stream, s);
     else if (pl.tile == 4)
-      hipLaunchKernelGGL(indexer_score_tile_kernel<4>, dim3(pl.chunks, pl.qgroups, L->batch),
-                         dim3(64 * kTileWaves), 0, stream, s);
+      hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
     else
       hipLaunchKernelGGL(indexer_score_kernel, dim3(pl.chunks, rows), dim3(256), 0, stream, s);
     int rc = t.done();
@@ -1371,9 +1683,15 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.part_count = reinterpret_cast<uint32_t*>(part);
   sa.part_bits = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes);
   sa.part_cand = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes + pl.part_bits_bytes);
+  sa.cand_count = s.cand_count;
+  sa.segs = pl.cand_lists / 32;
+  sa.span = pl.cand_span;
   // one timed interval covers the selection's one or two launches
   TimedLaunch t(kKernelTopkSelect, stream);
-  if (pl.slices) {
+  if (pl.cand) {
+    const size_t bitmap_bytes = (size_t)((pl.stride + 31) / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL(topk_cand_kernel, dim3(rows), dim3(kSelThreads), bitmap_bytes, stream, sa);
+  } else if (pl.slices) {
     hipLaunchKernelGGL(topk_slice_kernel, dim3(pl.slices, rows), dim3(kSelThreads), 0, stream, sa);
     hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);
   } else {

@@ -47,7 +47,14 @@ struct IndexerPlan {
   size_t keys_bytes;
   size_t hist_bytes;    // per-query histograms at the start of the workspace
   size_t part_count_bytes, part_bits_bytes, part_cand_bytes;
-  size_t total() const { return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes; }
+  bool cand;            // tile kernel keeps candidate lists: (key, visit) pairs, list lengths at the end
+  int cand_lists;       // lists per query: chunks x cand_waves x 32
+  int cand_waves;       // wavefronts per tile workgroup
+  int cand_span;        // blocks per chunk
+  size_t cand_count_bytes;
+  size_t total() const {
+    return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes + cand_count_bytes;
+  }
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,

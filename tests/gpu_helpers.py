@@ -110,3 +110,56 @@ def decode_keys(keys_u32):
     k = keys_u32.astype(np.uint32)
     bits = np.where(k & 0x80000000, k & 0x7FFFFFFF, ~k).astype(np.uint32)
     return bits.view(np.float32)
+
+
+def order_keys(scores_f32):
+    """fp32 scores to the indexer's uint32 order keys (sign bit set for a
+    non-negative score, every bit flipped for a negative one)"""
+    u = np.ascontiguousarray(scores_f32, np.float32).view(np.uint32)
+    return np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+
+
+def indexer_row_keys(ws, layout, row, nv):
+    """(blocks, keys) that the indexer left in its workspace (a uint8 device
+    tensor) for query row `row`: every visible block with full key rows, the
+    entries of the row's candidate lists otherwise (layout from
+    lca.indexer_layout)."""
+    import torch
+    S = layout["stride"]
+    if not layout["cand"]:
+        k0 = layout["keys"] + row * S * 4
+        keys = ws[k0:k0 + S * 4].view(torch.int32).cpu().numpy().view(np.uint32)
+        return np.arange(nv), keys[:nv]
+    k0 = layout["keys"] + row * S * 8
+    pairs = ws[k0:k0 + S * 8].view(torch.int32).cpu().numpy().view(np.uint32).reshape(S, 2)
+    lists, W, span = layout["lists"], layout["waves"], layout["span"]
+    c0 = layout["counts"] + row * lists * 4
+    cnt = ws[c0:c0 + lists * 4].view(torch.int32).cpu().numpy().astype(np.int64)
+    i = np.repeat(np.arange(lists), cnt)                       # list of each entry
+    j = np.arange(int(cnt.sum())) - np.repeat(np.cumsum(cnt) - cnt, cnt)   # its index in the list
+    g, col = np.divmod(i, 32)
+    c, v = np.divmod(g, W)
+    assert (c * span + 32 * v + 32 * W * j + col < S).all()
+    e = pairs[c * span + 32 * v + 32 * W * j + col]
+    return c * span + 32 * (v + W * e[:, 1].astype(np.int64)) + col, e[:, 0]
+
+
+def check_indexer_keys(blocks, keys, scores, k):
+    """The kept keys are the exact order keys of their blocks' oracle scores,
+    each block at most once, and every block that can be in the top k is
+    kept: all of them when there are at most k, else every block whose key's
+    top 12 bits reach those of the k-th largest key."""
+    want = order_keys(scores)
+    nv = len(want)
+    assert len(np.unique(blocks)) == len(blocks), "a block kept twice"
+    if len(blocks):
+        assert blocks.min() >= 0 and blocks.max() < nv, (blocks.min(), blocks.max(), nv)
+    bad = np.nonzero(keys != want[blocks])[0]
+    assert bad.size == 0, (blocks[bad[:5]], keys[bad[:5]], want[blocks[bad[:5]]])
+    if nv <= k:
+        need = np.arange(nv)
+    else:
+        tb = np.sort(want)[nv - k] >> 20
+        need = np.nonzero((want >> 20) >= tb)[0]
+    missing = np.setdiff1d(need, blocks)
+    assert missing.size == 0, ("blocks that can reach the top k are missing", missing[:5])

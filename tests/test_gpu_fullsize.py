@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 import oracle
 from synth import layers as SL
 
-from gpu_helpers import ATTN_TOL, attn_rel_err, compare_entries, decode_keys
+from gpu_helpers import ATTN_TOL, attn_rel_err, check_indexer_keys, compare_entries, indexer_row_keys
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 SCALE = np.float32(1.0 / np.sqrt(512.0))
@@ -51,15 +51,11 @@ def _ring_tokens(V, f, p0, n):
 
 
 def _score_keys(lay, lca, n_q, H_I, k):
-    """the order keys the indexer left in its workspace: [rows][stride] u32"""
+    """the indexer's workspace and its layout; the histograms must be zero"""
     ws = lay._ws["indexer"]
-    nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
-    rows = lay.batch * n_q
-    stride = max(64, (lay.len_max // lay.ratio + 63) // 64 * 64)
-    wsh = ws[:nbytes].view(torch.int32)
-    hist_words = rows * 4096
-    assert not wsh[:hist_words].any().item()        # histograms left zeroed
-    return wsh[hist_words: hist_words + rows * stride].view(rows, stride)
+    layout = lca.indexer_layout(lay, n_q, H_I, k)
+    assert not ws[:layout["keys"]].view(torch.int32).any().item()     # histograms left zeroed
+    return ws, layout
 
 
 def _check_finalised(got, V, r, block, m, has_idx):
@@ -103,8 +99,7 @@ def test_csa_decode_128k_fullsize():
         assert np.array_equal(got["ring_kv"][r, slot], V["ring_kv"][0, slot])
         flips += _check_finalised(got, V, r, ctx // m - 1, m, True)
         sc = oracle.indexer_scores(V, 0, 0, 1, Q["iq"][r:r + 1], Q["iw"][r:r + 1])
-        gs = decode_keys(keys[r, :len(sc)].cpu().numpy().view(np.uint32))
-        assert np.array_equal(gs.view(np.uint32), sc.view(np.uint32))
+        check_indexer_keys(*indexer_row_keys(*keys, r, len(sc)), sc, k)
         want = oracle.indexer_topk(V, Q["iq"][r:r + 1], Q["iw"][r:r + 1], k)
         assert np.array_equal(got_topk[r], want[0])
         assert set(planted[r]) <= set(got_topk[r, 0].tolist())
@@ -175,8 +170,7 @@ def test_csa_prefill_chunk_fullsize():
     for qi in (0, 1, 1234, 4094, 4095):
         say("csa_prefill query", qi)
         sc = oracle.indexer_scores(V, 0, qi, n, Q["iq"], Q["iw"])
-        gs = decode_keys(keys[qi, :len(sc)].cpu().numpy().view(np.uint32))
-        assert np.array_equal(gs.view(np.uint32), sc.view(np.uint32))
+        check_indexer_keys(*indexer_row_keys(*keys, qi, len(sc)), sc, k)
         assert np.array_equal(got_topk[0, qi], oracle.topk_select(sc, k))
         # one query alone: a view whose length ends at the query's position
         p = prior + qi

@@ -16,7 +16,7 @@ import oracle
 import synth
 from synth import layers as SL
 
-from gpu_helpers import ATTN_TOL, attn_rel_err, compare_entries, decode_keys
+from gpu_helpers import ATTN_TOL, attn_rel_err, check_indexer_keys, compare_entries, indexer_row_keys
 
 pytestmark = pytest.mark.gpu
 SCALE = np.float32(1.0 / np.sqrt(512.0))
@@ -128,9 +128,16 @@ INDEXER_CASES = [
 ]
 
 # environment switches: the selection split over workgroups, the score
-# kernel that shares key tiles across a row's queries
+# kernel that shares key tiles across a row's queries, with candidate lists
+# where a row has at most 64 of them (tile), always (tile_cand) or never
+# (tile_full)
 INDEXER_MODES = {"auto": {}, "sliced": {"LCA_TOPK_SLICED": "1"}, "tile": {"LCA_SCORE_TILE": "1"},
+                 "tile_cand": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "1"},
+                 "tile_full": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "0"},
                  "no_tile": {"LCA_SCORE_TILE": "0"}}
+
+# oracle results per case, shared by the modes
+_ORACLE = {}
 
 
 def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed):
@@ -159,23 +166,22 @@ def test_indexer_topk_parity(case, mode, monkeypatch):
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
-    want = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
-    # scores: the workspace holds one order key per visible block
+    if name not in _ORACLE:
+        _ORACLE[name] = (oracle.indexer_topk(ref, Q["iq"], Q["iw"], k),
+                         [[oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"]) for qi in range(n_q)]
+                          for b in range(B)])
+    want, scores = _ORACLE[name]
+    # scores: the workspace holds the order keys of every visible block, or
+    # of every block that can reach the top k (candidate lists)
     ws = lay._ws["indexer"]
-    nbytes = lca.indexer_workspace_bytes(lay, n_q, H_I, k)
-    hist_bytes = B * n_q * 4096 * 4
-    stride = max(64, (max(lens) // 4 + 63) // 64 * 64)
-    wsh = ws[:nbytes].view(torch.int32).cpu().numpy().view(np.uint32)
-    assert not wsh[: hist_bytes // 4].any()          # histograms left zeroed for the next call
-    keys = wsh[hist_bytes // 4: hist_bytes // 4 + B * n_q * stride].reshape(B * n_q, stride)
+    layout = lca.indexer_layout(lay, n_q, H_I, k)
+    hist_words = B * n_q * 4096
+    assert not ws[:hist_words * 4].view(torch.int32).any().item()   # histograms left zeroed for the next call
     for b in range(B):
         for qi in range(n_q):
-            sc = oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"])
-            nv = len(sc)
-            if nv:
-                gs = decode_keys(keys[b * n_q + qi, :nv])
-                bad = np.nonzero(gs.view(np.uint32) != sc.view(np.uint32))[0]
-                assert bad.size == 0, (b, qi, bad[:5], gs[bad[:5]], sc[bad[:5]])
+            sc = scores[b][qi]
+            blocks, keys = indexer_row_keys(ws, layout, b * n_q + qi, len(sc))
+            check_indexer_keys(blocks, keys, sc, k)
             assert np.array_equal(got[b, qi], want[b, qi]), (b, qi)
     if needles:
         for b in range(B):
@@ -184,13 +190,16 @@ def test_indexer_topk_parity(case, mode, monkeypatch):
             assert set(nd) <= set(got[b, -1].tolist())
 
 
-@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
+TIE_MODES = ["auto", "sliced", "tile_cand"]
+
+
+@pytest.mark.parametrize("mode", TIE_MODES)
 @pytest.mark.parametrize("B,L", [(1, 4000), (2, 140000)], ids=["short", "long"])
-def test_indexer_equal_scores_take_lowest_indices(B, L, sliced, monkeypatch):
+def test_indexer_equal_scores_take_lowest_indices(B, L, mode, monkeypatch):
     lca = _lca()
-    say("indexer equal scores", B, L, "sliced", sliced)
-    if sliced:
-        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
+    say("indexer equal scores", B, L, "mode", mode)
+    for var, val in INDEXER_MODES[mode].items():
+        monkeypatch.setenv(var, val)
     m, k = 4, 50
     ref = SL.make_layer(77, "eq", B, m, 128, 256, 1, L // m + 4, [L] * B)
     ref["idx_code"][:] = 0x22          # every key identical
@@ -204,15 +213,15 @@ def test_indexer_equal_scores_take_lowest_indices(B, L, sliced, monkeypatch):
         assert list(got[b, 0]) == list(range(k))
 
 
-@pytest.mark.parametrize("sliced", ["", "1"], ids=["auto", "sliced"])
+@pytest.mark.parametrize("mode", TIE_MODES)
 @pytest.mark.parametrize("L", [48000, 140000], ids=["one_round", "two_rounds"])
-def test_indexer_near_equal_scores(L, sliced, monkeypatch):
+def test_indexer_near_equal_scores(L, mode, monkeypatch):
     """Most scores share their high bits (keys differ in one byte): exercises
     the second-level candidate selection."""
     lca = _lca()
-    say("indexer near-equal scores", L, "sliced", sliced)
-    if sliced:
-        monkeypatch.setenv("LCA_TOPK_SLICED", sliced)
+    say("indexer near-equal scores", L, "mode", mode)
+    for var, val in INDEXER_MODES[mode].items():
+        monkeypatch.setenv(var, val)
     B, m, k = 2, 4, 512
     ref = SL.make_layer(78, "neq", B, m, 128, 256, 1, L // m + 4, [L, L - 7])
     rng = np.random.default_rng(78)
@@ -227,7 +236,7 @@ def test_indexer_near_equal_scores(L, sliced, monkeypatch):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("mode", ["tile", "no_tile"])
+@pytest.mark.parametrize("mode", ["tile", "tile_full", "no_tile"])
 def test_indexer_exponent_extremes(mode, monkeypatch):
     """Key halves with E8M0 scales up to 12 apart and query halves scaled by
     2^20 or 2^-12: the products of the two MX halves can no longer be added
