@@ -9,20 +9,20 @@
 // tokens stay at raw precision; entries are FP8 with BF16 RoPE dims.
 //
 // All query heads of a row share one 512-d key/value vector per key, so a
-// workgroup stages each key once in LDS and 8 compute wavefronts use it:
-// wavefront w takes heads 16(w % 4) .. +15 of its head group and channel half
-// w / 4.  Four more wavefronts only stage: while the compute wavefronts work
-// on tile t from one LDS buffer they load tile t + 2 and convert tile t + 1
-// into the other, so the loads and conversions leave the critical path.
+// workgroup stages each key once in LDS and 4 compute wavefronts use it, one
+// per SIMD: wavefront w takes heads 16 w .. +15 of its head group over all
+// 512 channels, so its scores need no exchange with another wavefront.  Four
+// more wavefronts only stage: while the compute wavefronts work on tile t
+// from one LDS buffer they load tile t + 2 and convert tile t + 1 into the
+// other, so the loads and conversions leave the critical path.
 // A staged key is one fp16 image serving as K and as V: the exact value of
 // each e4m3 code (e4m3 values are fp16 numbers), or the bf16 RoPE / window
 // value (exact within fp16's normal range).  The query is converted to fp16
 // the same way.  Every product is computed transposed, keys x heads, so that
 // a lane owns one head throughout: lane l holds head l % 16 and key / channel
 // quarter l / 16.
-//   S^T = K Q^T   fp16 matrix cores over the wavefront's 256 channels; the
-//                 per-64-dim FP8 scale multiplies each 64-dim partial dot in
-//                 fp32.  The two halves add their partial scores through LDS.
+//   S^T = K Q^T   fp16 matrix cores over the 512 channels; the per-64-dim
+//                 FP8 scale multiplies each 64-dim partial dot in fp32.
 //                 Lane l ends with keys 4(l/16)+r and 16+4(l/16)+r of its head.
 //   softmax       online, base 2, per lane (one head) plus a max over the four
 //                 lanes that share the head; the running maximum is only
@@ -34,7 +34,7 @@
 //                 is fp16(p * that group's scale of the key).  The V^T operand
 //                 comes from the LDS transpose read ds_read_b64_tr_b16.  Lane
 //                 l accumulates channels 16 ct + 4(l/16) + r of its head for
-//                 the 16 ct of its half.
+//                 the 32 channel tiles ct.
 // Each workgroup covers a contiguous chunk of the key list; chunks are merged
 // by the combine kernel (or written directly when there is one chunk).
 #include "lca_device.h"
@@ -72,7 +72,7 @@ struct AttendArgs {
   _Float16* ws_o;
 };
 
-constexpr int kComputeWaves = 8;   // 4 head wavefronts x 2 channel halves
+constexpr int kComputeWaves = 4;   // 4 head wavefronts of 16 heads, all channels
 constexpr int kStageWaves = 4;     // wavefronts that load and convert the next tile
 constexpr int kThreads = 64 * (kComputeWaves + kStageWaves);
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running maximum
@@ -90,12 +90,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Ts[2][kTile * kVst];   // [key][channel]
   __shared__ __attribute__((aligned(16))) float sK[2][8 * kTile];     // [group][key]
   __shared__ __attribute__((aligned(16))) float kbias[2][kTile];      // 0, or -inf for a masked key
-  __shared__ __attribute__((aligned(16))) float Sx[8 * 64 * 8];       // partial scores per wave / lane
   __shared__ int klist[kMaxChunk];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool computes = wave < kComputeWaves;
-  const int hw = wave & 3, half = (wave >> 2) & 1;   // head wavefront, channel half (compute wavefronts)
+  const int hw = wave & 3;                    // head wavefront (compute wavefronts)
   const int srow = blockIdx.y, split = blockIdx.x, hgrp = blockIdx.z;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
   const int h0 = hgrp * 64 + hw * 16;
@@ -104,11 +103,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int g = lane >> 4;                    // this lane's key / channel quarter
   const int kq = 8 * g;                       // K offset of this lane inside a 32-K step
 
-  v8h qf[8];   // q of this lane's head (fp16 image of the bf16 input), channels 256 half + 32 ks + 8 g .. +7
+  v8h qf[16];  // q of this lane's head (fp16 image of the bf16 input), channels 32 ks + 8 g .. +7
   {
-    const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv + 256 * half;
+    const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv;
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
+    for (int ks = 0; ks < 16; ks++) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (active && hq < a.H) v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + kq);
       qf[ks] = bf16x8_to_f16(v);
@@ -133,9 +132,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     }
   }
 
-  v4f O[16];
+  v4f O[32];
 #pragma unroll
-  for (int c = 0; c < 16; c++) O[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 32; c++) O[c] = (v4f){0.f, 0.f, 0.f, 0.f};
   float mrow = -INFINITY, lrow = 0.0f;
   __syncthreads();   // klist
 
@@ -224,15 +223,13 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // 4j + i / 4, so lane L reads channels 16 ct + 4(L % 4) .. +3 of key
   // 4g + L / 4 (and of key 16 + 4g + L / 4 for the second read).
   const int Lq = lane & 15;
-  const int voff = (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3) + 256 * half;
-  const int koff = Lq * kVst + kq + 256 * half;
-  float* sx_mine = Sx + ((wave & 7) * 64 + lane) * 8;
-  const float* sx_other = Sx + (((wave & 7) ^ 4) * 64 + lane) * 8;
+  const int voff = (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3);
+  const int koff = Lq * kVst + kq;
 
   // Staging wavefronts: tile 0 into buffer 0 before the loop; during tile t
   // they store tile t + 1 (loaded a tile earlier) into the other buffer and
-  // load tile t + 2, group sw before the mid-tile barrier and group sw + 4
-  // after it.  Every wavefront passes the same two barriers per tile.
+  // load tile t + 2, groups sw and sw + 4.  Every wavefront passes the same
+  // barrier once per tile.
   // (Two separate loops, so that the staging registers and the compute
   // registers are never live at once.)
   if (!computes) {
@@ -252,12 +249,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     for (int t0 = kb; t0 < ke; t0 += kTile, cur ^= 1) {
       if (t0 + kTile < ke) {
         stage_store(stA, sw, cur ^ 1);
-        if (t0 + 2 * kTile < ke) stage_load(t0 + 2 * kTile, sw, stA);
-      }
-      __syncthreads();                     // (the compute wavefronts' partial-score exchange)
-      if (t0 + kTile < ke) {
         stage_store(stB, sw + 4, cur ^ 1);
-        if (t0 + 2 * kTile < ke) stage_load(t0 + 2 * kTile, sw + 4, stB);
+        if (t0 + 2 * kTile < ke) {
+          stage_load(t0 + 2 * kTile, sw, stA);
+          stage_load(t0 + 2 * kTile, sw + 4, stB);
+        }
       }
       __syncthreads();                     // tile t + 1 staged, tile t consumed
     }
@@ -270,15 +266,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     const _Float16* vrow0 = Ts[cur] + voff;
     const _Float16* vrow1 = vrow0 + 16 * kVst;
 
-    // partial S^T = K Q^T over this half's channels, 32 keys x 16 heads,
-    // per 64-dim group scaled in fp32
+    // S^T = K Q^T over the 512 channels, 32 keys x 16 heads, per 64-dim
+    // group scaled in fp32
     v4f S[2];
 #pragma unroll
     for (int nt = 0; nt < 2; nt++) {
       S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
       const _Float16* krow = Kc + nt * 16 * kVst;
 #pragma unroll
-      for (int gl = 0; gl < 4; gl++) {
+      for (int gl = 0; gl < 8; gl++) {
         v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; s2++) {
@@ -286,21 +282,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
           const v8h kh8 = *reinterpret_cast<const v8h*>(krow + ks * 32);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh8, qf[ks], acc, 0, 0, 0);
         }
-        const v4f sc = *reinterpret_cast<const v4f*>(sK[cur] + (4 * half + gl) * kTile + nt * 16 + 4 * g);
+        const v4f sc = *reinterpret_cast<const v4f*>(sK[cur] + gl * kTile + nt * 16 + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; r++) S[nt][r] = __builtin_fmaf(sc[r], acc[r], S[nt][r]);
-      }
-    }
-    reinterpret_cast<v4f*>(sx_mine)[0] = S[0];
-    reinterpret_cast<v4f*>(sx_mine)[1] = S[1];
-    __syncthreads();
-    {
-      const v4f o0 = reinterpret_cast<const v4f*>(sx_other)[0];
-      const v4f o1 = reinterpret_cast<const v4f*>(sx_other)[1];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        S[0][r] += o0[r];   // fp32 addition commutes: both halves get the same sum
-        S[1][r] += o1[r];
       }
     }
     // online softmax (base 2) of this lane's head over its eight keys
@@ -325,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mrow - mnew);
       lrow *= alpha;
 #pragma unroll
-      for (int c = 0; c < 16; c++)
+      for (int c = 0; c < 32; c++)
 #pragma unroll
         for (int r = 0; r < 4; r++) O[c][r] *= alpha;
       mrow = mnew;
@@ -337,30 +321,30 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       pj[j] = __builtin_amdgcn_exp2f(x[j] - mref);
       lrow += pj[j];
     }
-    // the tile holds code values, so each 64-dim group's FP8 scale goes into
-    // P: B operand of group gl = fp16(p_j * scale of key j's group)
-    v8h pbg[4];
+    // O^T += V^T P^T over the 32 channel tiles.  The tile holds code values,
+    // so each 64-dim group's FP8 scale goes into P: B operand of group gl =
+    // fp16(p_j * scale of key j's group), for the group's four channel tiles.
 #pragma unroll
-    for (int gl = 0; gl < 4; gl++) {
-      const float* sg0 = sK[cur] + (4 * half + gl) * kTile + 4 * g;
+    for (int gl = 0; gl < 8; gl++) {
+      const float* sg0 = sK[cur] + gl * kTile + 4 * g;
       const v4f s0 = *reinterpret_cast<const v4f*>(sg0);
       const v4f s1 = *reinterpret_cast<const v4f*>(sg0 + 16);
+      v8h pb;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        pbg[gl][r] = (_Float16)__fmul_rn(pj[r], s0[r]);
-        pbg[gl][4 + r] = (_Float16)__fmul_rn(pj[4 + r], s1[r]);
+        pb[r] = (_Float16)__fmul_rn(pj[r], s0[r]);
+        pb[4 + r] = (_Float16)__fmul_rn(pj[4 + r], s1[r]);
       }
-    }
-    // O^T += V^T P^T over this half's 16 channel tiles
 #pragma unroll
-    for (int c = 0; c < 16; c++) {
-      const v8h pb = pbg[c >> 2];
-      typedef __attribute__((address_space(3))) v4s lds_v4s;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
-      const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
-      const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
-      O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
+      for (int c4 = 0; c4 < 4; c4++) {
+        const int c = 4 * gl + c4;
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
+        const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
+        const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
+      }
     }
     __syncthreads();                       // tile t + 1 staged, tile t consumed
   }
@@ -371,28 +355,28 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   if (a.splits == 1) {
     if (hq < a.H) {
       const float inv = 1.0f / lrow;
-      float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + hq) * kKv + 256 * half + 4 * g);
+      float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)srow * a.H + hq) * kKv + 4 * g);
 #pragma unroll
-      for (int c = 0; c < 16; c++)
+      for (int c = 0; c < 32; c++)
         dst[c * 4] = make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
     }
   } else {
     // partials: (m, l) per head, and this lane's normalised outputs in fp16:
     // value index ct * 4 + r of the head's 128 per lane, as 16 uint4 per lane
-    // interleaved across the wave; this half writes uint4 8 half .. +7
-    if (hq < a.H && g == 0 && half == 0) {
+    // interleaved across the wave
+    if (hq < a.H && g == 0) {
       const int64_t slot = ((int64_t)srow * a.splits + split) * a.H + hq;
       reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(mrow, lrow);
     }
     const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
     const int64_t rec = ((int64_t)srow * a.splits + split) * a.hwaves + (hgrp * 4 + hw);
-    uint4* dst = reinterpret_cast<uint4*>(a.ws_o + rec * 8192) + (8 * half) * 64 + lane;
+    uint4* dst = reinterpret_cast<uint4*>(a.ws_o + rec * 8192) + lane;
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
+    for (int q = 0; q < 16; q++) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int i0 = q * 8 + 2 * e;   // values i0, i0 + 1 of this half: (c, r) = (i0 / 4, i0 % 4)
+        const int i0 = q * 8 + 2 * e;   // values i0, i0 + 1: (c, r) = (i0 / 4, i0 % 4)
         const v2f f = {O[i0 >> 2][i0 & 3] * inv, O[(i0 + 1) >> 2][(i0 + 1) & 3] * inv};
         w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h));
       }

@@ -112,6 +112,51 @@ __device__ __noinline__ float score_unscaled(v8i A0, v8i A1, v8i Bm, int hgroups
   return total;
 }
 
+// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the total of row 0 (lane 15) is added to row 1, that of row 2 (lane
+// 47) to row 3, and that of rows 0-1 (lane 31) to rows 2 and 3.  Lanes whose
+// source lies outside the row read 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xc, 0xf, false);
+  return x;
+}
+
+// The highest bin b such that the bins above b hold at least k keys of the
+// histogram h (-1 when there is none), found by one wavefront while other
+// wavefronts may still be adding to h: every count read was reached, so at
+// least k keys above b exist in the end, whatever the interleaving.  Lane l
+// sums bins 64 l .. 64 l + 63; the lanes whose bins all have k keys above
+// them form a prefix 0 .. F-1, and in lane F, where the count from the top
+// crosses k, each lane takes one bin (from the top down) and a wave scan
+// gives the keys above it.  Wave-uniform result.
+__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k) {
+  const int lane = threadIdx.x & 63;
+  const uint4* hv = reinterpret_cast<const uint4*>(h) + 16 * lane;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const uint4 x = hv[i];
+    s += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = wave_inclusive_scan(s);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
+  const uint64_t cross = __ballot(above < k && above + s >= k);
+  if (cross == 0) return -1;                       // fewer than k keys
+  const int F = __ffsll((long long)cross) - 1;     // lanes 0 .. F-1: every bin qualifies
+  const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
+  const uint32_t c = h[64 * F + 63 - lane];       // lane j: the j-th bin of lane F from the top
+  const uint32_t ci = wave_inclusive_scan(c);
+  const uint64_t q = __ballot(aF + ci - c >= k);   // keys above that bin reach k
+  return 64 * F + __popcll(q) - 1;
+}
+
 __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   const int srow = blockIdx.y;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
@@ -320,22 +365,6 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
     if (hc[i]) atomicAdd(&gh[tid + 256 * i], hc[i]);
 }
 
-// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
-// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
-// then the total of row 0 (lane 15) is added to row 1, that of row 2 (lane
-// 47) to row 3, and that of rows 0-1 (lane 31) to rows 2 and 3.  Lanes whose
-// source lies outside the row read 0.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xa, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xc, 0xf, false);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
 // Scores for many queries per row (prefill chunks): a workgroup takes Qwg
 // consecutive queries of one row and a range of blocks, so every key is read
@@ -384,35 +413,6 @@ constexpr int kTileWavesPerSet = kTileWaves / kTileSets;
 // set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
 // output would first be canonicalised, a second instruction.)
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// The highest bin b such that the bins above b hold at least k keys of the
-// histogram h (-1 when there is none), found by one wavefront while other
-// wavefronts may still be adding to h: every count read was reached, so at
-// least k keys above b exist in the end, whatever the interleaving.  Lane l
-// sums bins 64 l .. 64 l + 63; the lanes whose bins all have k keys above
-// them form a prefix 0 .. F-1, and in lane F, where the count from the top
-// crosses k, each lane takes one bin (from the top down) and a wave scan
-// gives the keys above it.  Wave-uniform result.
-__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k) {
-  const int lane = threadIdx.x & 63;
-  const uint4* hv = reinterpret_cast<const uint4*>(h) + 16 * lane;
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const uint4 x = hv[i];
-    s += x.x + x.y + x.z + x.w;
-  }
-  const uint32_t incl = wave_inclusive_scan(s);
-  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
-  const uint64_t cross = __ballot(above < k && above + s >= k);
-  if (cross == 0) return -1;                       // fewer than k keys
-  const int F = __ffsll((long long)cross) - 1;     // lanes 0 .. F-1: every bin qualifies
-  const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
-  const uint32_t c = h[64 * F + 63 - lane];       // lane j: the j-th bin of lane F from the top
-  const uint32_t ci = wave_inclusive_scan(c);
-  const uint64_t q = __ballot(aF + ci - c >= k);   // keys above that bin reach k
-  return 64 * F + __popcll(q) - 1;
-}
 
 template <int kQw>   // queries per wavefront: 8 (H <= 16) or 4 (H <= 32)
 __device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, int set,
