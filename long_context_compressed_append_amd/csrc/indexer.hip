@@ -129,32 +129,39 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 }
 
 // The highest bin b such that the bins above b hold at least k keys of the
-// histogram h (-1 when there is none), found by one wavefront while other
-// wavefronts may still be adding to h: every count read was reached, so at
-// least k keys above b exist in the end, whatever the interleaving.  Lane l
-// sums bins 64 l .. 64 l + 63; the lanes whose bins all have k keys above
-// them form a prefix 0 .. F-1, and in lane F, where the count from the top
-// crosses k, each lane takes one bin (from the top down) and a wave scan
-// gives the keys above it.  Wave-uniform result.
-__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k) {
+// histogram h, found by one wavefront while other wavefronts may still be
+// adding to h: every count read was reached, so at least k keys above b
+// exist in the end, whatever the interleaving.  `from` is a bin at most one
+// above the answer (a previous answer + 1, as counts only grow; 0 at first):
+// only bins from there up are read, and from - 1 is returned when they hold
+// fewer than k keys (-1 at first).  Lane l sums its share of the range; the
+// lanes whose bins all have k keys above them form a prefix 0 .. F-1, and in
+// lane F, where the count from the top crosses k, each lane takes one bin
+// (from the top down) and a wave scan gives the keys above it.  Wave-uniform.
+__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, int from) {
   const int lane = threadIdx.x & 63;
-  const uint4* hv = reinterpret_cast<const uint4*>(h) + 16 * lane;
+  const int lo = from & ~3;                           // whole uint4 groups
+  const int n4 = (kHistBins - lo) >> 2;
+  const int per = (n4 + 63) >> 6;                     // groups per lane: <= 16
+  const int mine = max(0, min(per, n4 - per * lane));
+  const uint4* hv = reinterpret_cast<const uint4*>(h + lo) + per * lane;
   uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
+  for (int i = 0; i < mine; i++) {
     const uint4 x = hv[i];
     s += x.x + x.y + x.z + x.w;
   }
   const uint32_t incl = wave_inclusive_scan(s);
   const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
   const uint64_t cross = __ballot(above < k && above + s >= k);
-  if (cross == 0) return -1;                       // fewer than k keys
+  if (cross == 0) return from - 1;                 // fewer than k keys from `from` up
   const int F = __ffsll((long long)cross) - 1;     // lanes 0 .. F-1: every bin qualifies
   const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
-  const uint32_t c = h[64 * F + 63 - lane];       // lane j: the j-th bin of lane F from the top
+  const int base = lo + 4 * per * F;
+  const int cnt = 4 * __builtin_amdgcn_readlane(mine, F);   // lane F's bins: base .. base + cnt - 1
+  const uint32_t c = lane < cnt ? h[base + cnt - 1 - lane] : 0u;   // the lane-th from the top
   const uint32_t ci = wave_inclusive_scan(c);
-  const uint64_t q = __ballot(aF + ci - c >= k);   // keys above that bin reach k
-  return 64 * F + __popcll(q) - 1;
+  const uint64_t q = __ballot(lane < cnt && aF + ci - c >= k);   // keys above that bin reach k
+  return base + __popcll(q) - 1;
 }
 
 __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
@@ -391,7 +398,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 //
 // Candidate lists (kCand): instead of one key per block, each lane keeps
 // only the keys that can still be among its query's k largest.  From time to
-// time (after 4, 8, 16, ... iterations) wavefront w reads the running
+// time (after 4 iterations, then every 8) wavefront w reads the running
 // histogram of query w of the workgroup and finds the highest bin b whose
 // higher bins already hold k keys; keys in bin b or below cannot reach the
 // top k of the row, since the k-th largest key of the row lies above b.
@@ -655,11 +662,12 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   };
 #pragma unroll 1
   for (int t0 = 0; t0 < n_it; t0 += kRing) {
-    if (kCand && t0 >= kRing && (t0 & (t0 - 1)) == 0) {
+    if (kCand && t0 >= kRing && ((t0 & (t0 - 1)) == 0 || (t0 & 7) == 0)) {
       // wavefront w refreshes the bound of query w, then every lane takes the
       // latest bounds of its queries (another wavefront's may be older: any
       // value it has written is valid)
-      if (wv < kQw) thr_s[set * kQw + wv] = running_threshold(&lh[set * kQw + wv][0], (uint32_t)a.k);
+      if (wv < kQw)
+        thr_s[set * kQw + wv] = running_threshold(&lh[set * kQw + wv][0], (uint32_t)a.k, thr_s[set * kQw + wv] + 1);
       // keys above bin b: key >= (b + 1) << 20
 #pragma unroll
       for (int m = 0; m < kNm; m++) kmin[m] = (uint32_t)(thr_s[set * kQw + (kQw == 8 ? 2 * m + kh : m)] + 1) << kHistShift;
@@ -684,16 +692,20 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
     }
   }
   __syncthreads();
-  // flush the histograms of the workgroup's queries
+  // flush the histograms of the workgroup's queries.  With candidate lists
+  // only the bins above the query's last bound go out: the row's threshold
+  // bin lies above it, and the selection reads exact counts only at and above
+  // that bin.
 #pragma unroll 1
   for (int q = 0; q < nqv; q++) {
     uint32_t* gh = a.hist + ((int64_t)brow * a.n_q + q0 + q) * kHistBins;
+    const int bmin = kCand ? thr_s[q] : -1;
     uint32_t hc[kHistBins / (64 * kTileWaves)];
 #pragma unroll
     for (int i = 0; i < kHistBins / (64 * kTileWaves); i++) hc[i] = lh[q][tid + 64 * kTileWaves * i];
 #pragma unroll
     for (int i = 0; i < kHistBins / (64 * kTileWaves); i++)
-      if (hc[i]) atomicAdd(&gh[tid + 64 * kTileWaves * i], hc[i]);
+      if (hc[i] && tid + 64 * kTileWaves * i > bmin) atomicAdd(&gh[tid + 64 * kTileWaves * i], hc[i]);
   }
 }
 
