@@ -102,3 +102,33 @@ def test_workspace_queries_are_pure():
     assert n >= 4 * 32768
     a = L.lca_attend_workspace(C.byref(s), 1, 64, 512)
     assert a % 4 == 0
+
+
+def test_indexer_layout_matches_the_workspace():
+    """The layout query (host only): full key rows for a decode query, candidate
+    lists for a prefill chunk, every region inside the workspace size."""
+    L = _lib()
+    L.lca_indexer_workspace.restype = C.c_size_t
+    L.lca_indexer_layout.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
+    out = (C.c_int64 * 8)()
+    # decode: one query per row, full key rows
+    s = _layer(batch=4, len_min=131072, len_max=131072, max_blocks=33000, has_indexer=1)
+    assert L.lca_indexer_layout(C.byref(s), 1, 16, 512, out) == 0
+    stride, keys, cand = out[0], out[1], out[2]
+    assert stride >= 32768 and stride % 64 == 0 and cand == 0
+    assert keys == 4 * 4096 * 4                       # after the per-query histograms
+    assert keys + 4 * stride * 4 <= L.lca_indexer_workspace(C.byref(s), 1, 16, 512)
+    # prefill chunk: 4096 queries in one row, candidate lists
+    s = _layer(batch=1, len_min=266240, len_max=266240, max_blocks=66624, has_indexer=1)
+    n_q = 4096
+    assert L.lca_indexer_layout(C.byref(s), n_q, 16, 512, out) == 0
+    stride, keys, cand, counts, lists, waves, span = out[0], out[1], out[2], out[4], out[5], out[6], out[7]
+    assert cand == 1 and waves == 8 and lists % (32 * waves) == 0
+    chunks = lists // (32 * waves)
+    assert chunks * span >= 266240 // 4 and span % 1024 == 0
+    total = L.lca_indexer_workspace(C.byref(s), n_q, 16, 512)
+    assert keys + n_q * stride * 8 <= counts          # (key, visit) pairs, then the list lengths
+    assert counts + n_q * lists * 4 <= total
+    # errors
+    assert L.lca_indexer_layout(C.byref(s), 0, 16, 512, out) == -1
+    assert L.lca_indexer_layout(C.byref(s), 1, 16, 512, None) == -1
