@@ -167,6 +167,14 @@ int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
  * zero-filled before its first use, and be used by nothing but
  * lca_indexer_topk afterwards: its leading part holds per-query histograms
  * that every call leaves zero-filled again.
+ * The kernels are chosen from the shapes; for tests and tuning the choice
+ * can be forced through environment variables read at every call (keep them
+ * unchanged between the workspace query and the call, as the workspace size
+ * follows the choice): LCA_SCORE_TILE (0/1: multi-query score kernel),
+ * LCA_TOPK_CAND (0/1: candidate lists with it), LCA_TOPK_SLICED (0/1: the
+ * selection split over part workgroups), LCA_TOPK_FUSED (1: one query per
+ * row selects inside the scoring launch), LCA_SCORE_CPW (chunks of 1024
+ * blocks per scoring workgroup).
  */
 size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k);
 
@@ -210,6 +218,9 @@ int lca_indexer_topk(const lca_layer *layer, const float *iq, const float *iw, i
  *   q     uint16 [B][n_q][H][512] bf16     out float [B][n_q][H][512]
  * Needs 1 <= H <= 128, 1 <= k <= 2048, n_q <= len_min and
  * n_q + window - 1 <= ring.  ws must hold lca_attend_workspace(...) bytes.
+ * The number of key splits (and so the workspace size) follows the shapes;
+ * the environment variable LCA_ATTEND_SPLITS, read at every call, forces it
+ * for tests and tuning (keep it unchanged between the query and the call).
  */
 size_t lca_attend_workspace(const lca_layer *layer, int32_t n_q, int32_t H, int32_t k);
 int lca_csa_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32_t H,

@@ -72,6 +72,7 @@ struct ScoreArgs {
   // candidate lists (tile kernel): keys holds (key, visit) pairs [rows][stride];
   // list lengths [rows][chunks][kTileWaves][32]
   uint32_t* cand_count;
+  uint32_t* row_done;    // fused selection: workgroups of a row done, [rows], zero between calls
 };
 
 // exact value of D0 * 2^e0 + D1 * 2^e1 rounded once to fp32, where D0, D1 are
@@ -164,20 +165,68 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
   return base + __popcll(q) - 1;
 }
 
-__global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRoundKeys = 64 * kSelThreads;   // blocks per round
+constexpr int kCandCap = 4096;
+constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
+constexpr int kPartKeys = 32 * kSelThreads;   // blocks per workgroup of the sliced path
+constexpr int kMaxParts = 64 * kMaxWords / kPartKeys;     // 32
+constexpr int kDirectRank = 128;   // lists up to this long are ranked by direct comparison
+constexpr int kSliceMaxRows = 256;   // the sliced path is taken below this many queries
+constexpr int kSliceMinBlocks = 3 * kRoundKeys / 2;   // ... and above this many blocks per row
+constexpr int kMaxCandGroups = 64;   // groups of 32 candidate lists per query (chunks x tile wavefronts)
+static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
+static_assert(kMaxParts <= 64 && kMaxParts * kSelThreads == 2 * kMaxWords, "part bookkeeping");
+static_assert(kDirectRank <= kSelThreads && kDirectRank <= 4096, "one list entry per thread, 12-bit positions");
+
+struct SelectArgs {
+  int n_q, m, k;
+  int64_t stride;
+  const int32_t* seq_len;
+  const uint32_t* keys;
+  uint32_t* hist;
+  int32_t* topk;
+  // sliced path: per (query, round) bitmap words [rows][slices][1024], listed
+  // key counts [rows][slices] and lists [rows][slices][2][kCandCap]
+  int slices;
+  uint32_t* part_bits;
+  uint32_t* part_count;
+  uint32_t* part_cand;
+  // candidate lists of the tile kernel: segs = chunks x kTileWavesPerSet
+  // groups of 32 lists per query, chunk c starting at block c * span
+  const uint32_t* cand_count;
+  int segs, span;
+};
+
+template <bool kCoherent>
+__device__ void select_row(const SelectArgs& a, int srow, uint32_t* hist, uint32_t* tmp, uint32_t* found,
+                           uint32_t* cand, uint32_t* bitmap);
+
+// kFused: 512 threads, two halves of 4 wavefronts on two consecutive chunk
+// ranges of the row sharing one histogram; keys leave with agent-scope stores,
+// and the row's last workgroup to finish (a per-row counter, after every
+// thread's stores and histogram atomics have completed) runs the selection
+// for the row, reading keys and histogram with agent-scope loads.  No
+// device-scope fence is needed: nothing it reads sits only in another
+// XCD's L2.
+template <bool kFused>
+__global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(ScoreArgs a, SelectArgs sel) {
+  constexpr int kT = kFused ? 512 : 256;
   const int srow = blockIdx.y;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
   // This workgroup's chunks of 1024 blocks are [c0, c0 + cpw).  The key loads
   // are issued before the row length arrives: any block below the key row
   // capacity is readable, and blocks past the visible count are masked later.
-  const int64_t c0 = (int64_t)blockIdx.x * a.cpw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wh = wave & 3;                       // wavefront within its half
+  const int64_t c0 = ((int64_t)blockIdx.x * (kFused ? 2 : 1) + (wave >> 2)) * a.cpw;
   const int64_t cap = a.stride < a.max_blocks ? a.stride : a.max_blocks;
 
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
   __shared__ float q_w[32];
   __shared__ uint32_t lhist[kHistBins];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, kh = lane >> 5;
 
   const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
@@ -188,7 +237,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   const int n_it = a.cpw * kScoreItersPerWave;
   auto blk_of = [&](int i) -> int64_t {
     return (c0 + i / kScoreItersPerWave) * kScoreBlocksPerWG +
-           (int64_t)wave * (kScoreItersPerWave * kScoreBlocksPerIter) +
+           (int64_t)wh * (kScoreItersPerWave * kScoreBlocksPerIter) +
            (i % kScoreItersPerWave) * kScoreBlocksPerIter + r;
   };
   // Loads are unconditional (a block past the capacity reads block 0) so that
@@ -205,7 +254,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
 #pragma unroll
   for (int u = 0; u < 8; u++) {
     const int e = tid + 256 * u;
-    qv[u] = e < a.H * kIdx ? qsrc[e] : 0.0f;
+    qv[u] = (e < a.H * kIdx && tid < 256) ? qsrc[e] : 0.0f;
   }
   const float wq = tid < a.H ? a.iw[(int64_t)srow * a.H + tid] : 0.0f;
   // Key loads go out after the query's: the loads complete in issue order, so
@@ -224,12 +273,13 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   int64_t nv = (int64_t)(p + 1) / a.m;
   if (nv > cap) nv = cap;                      // defensive: never past the key row
 
-  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
-  // MXFP4 quantisation of the query, one 32-lane half-wave per MX block.
+  for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
+  // MXFP4 quantisation of the query, one 32-lane half-wave per MX block
+  // (the first 256 threads)
 #pragma unroll
   for (int u = 0; u < 8; u++) {
     const int e = tid + 256 * u;
-    if (e >= a.H * kIdx) break;
+    if (e >= a.H * kIdx || tid >= 256) break;
     const float x = qv[u];
     float amax = half_wave_max(fabsf(x));
     uint32_t code = 0;
@@ -346,7 +396,10 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
       const int64_t blk = blk_of(i0 + u);
       if (kh == 0 && i0 + u < n_it && blk < nv) {
         const uint32_t key = ord_key(__fadd_rn(total[u], 0.0f));   // -0 -> +0
-        out[blk] = key;
+        if (kFused)
+          __hip_atomic_store(&out[blk], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          out[blk] = key;
         atomicAdd(&lhist[key >> kHistShift], 1u);
       }
     }
@@ -364,12 +417,26 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a) {
   __syncthreads();
   uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
   // every count is read before any atomic goes out
-  uint32_t hc[kHistBins / 256];
+  uint32_t hc[kHistBins / kT];
 #pragma unroll
-  for (int i = 0; i < kHistBins / 256; i++) hc[i] = lhist[tid + 256 * i];
+  for (int i = 0; i < kHistBins / kT; i++) hc[i] = lhist[tid + kT * i];
 #pragma unroll
-  for (int i = 0; i < kHistBins / 256; i++)
-    if (hc[i]) atomicAdd(&gh[tid + 256 * i], hc[i]);
+  for (int i = 0; i < kHistBins / kT; i++)
+    if (hc[i]) atomicAdd(&gh[tid + kT * i], hc[i]);
+  if constexpr (kFused) {
+    __builtin_amdgcn_s_waitcnt(0);     // this thread's key stores and atomics have completed
+    __syncthreads();
+    __shared__ uint32_t last;
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(&a.row_done[srow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    if (tid == 0) __hip_atomic_store(&a.row_done[srow], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __shared__ uint32_t tmp[64], found[4];
+    __shared__ uint32_t cand[2 * kCandCap], bitmap[2 * kMaxWords];
+    select_row<true>(sel, srow, lhist, tmp, found, cand, bitmap);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -738,39 +805,6 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
 // radix passes.
 // ---------------------------------------------------------------------------
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRoundKeys = 64 * kSelThreads;   // blocks per round
-constexpr int kCandCap = 4096;
-constexpr int kMaxWords = 8192;   // bitmap words of 64 blocks: 524288 blocks
-constexpr int kPartKeys = 32 * kSelThreads;   // blocks per workgroup of the sliced path
-constexpr int kMaxParts = 64 * kMaxWords / kPartKeys;     // 32
-constexpr int kDirectRank = 128;   // lists up to this long are ranked by direct comparison
-constexpr int kSliceMaxRows = 256;   // the sliced path is taken below this many queries
-constexpr int kSliceMinBlocks = 3 * kRoundKeys / 2;   // ... and above this many blocks per row
-constexpr int kMaxCandGroups = 64;   // groups of 32 candidate lists per query (chunks x tile wavefronts)
-static_assert(2 * kCandCap >= kMaxWords, "the candidate list doubles as per-word counters");
-static_assert(kMaxParts <= 64 && kMaxParts * kSelThreads == 2 * kMaxWords, "part bookkeeping");
-static_assert(kDirectRank <= kSelThreads && kDirectRank <= 4096, "one list entry per thread, 12-bit positions");
-
-struct SelectArgs {
-  int n_q, m, k;
-  int64_t stride;
-  const int32_t* seq_len;
-  const uint32_t* keys;
-  uint32_t* hist;
-  int32_t* topk;
-  // sliced path: per (query, round) bitmap words [rows][slices][1024], listed
-  // key counts [rows][slices] and lists [rows][slices][2][kCandCap]
-  int slices;
-  uint32_t* part_bits;
-  uint32_t* part_count;
-  uint32_t* part_cand;
-  // candidate lists of the tile kernel: segs = chunks x kTileWavesPerSet
-  // groups of 32 lists per query, chunk c starting at block c * span
-  const uint32_t* cand_count;
-  int segs, span;
-};
 
 // exclusive prefix sum over the kSelThreads threads; returns the block total
 // in *total (tmp >= 32 words)
@@ -819,7 +853,16 @@ __device__ __noinline__ void find_bin(const uint32_t* hist, uint32_t nb, uint32_
 // Visit the row's keys in 64-key words from word w_start on: wave w takes
 // words w_start + w, + 16, ...; the keys of 8 words are loaded before any is
 // used, so the loads overlap.
-template <typename F>
+// A key load: plain, or (kCoherent) an agent-scope load that reads past the
+// L2 of this XCD, for keys that other workgroups of the same launch wrote
+// with agent-scope stores.
+template <bool kCoherent>
+__device__ __forceinline__ uint32_t load_key(const uint32_t* p) {
+  return kCoherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+}
+constexpr int kCoherentAux = 16;   // buffer-load cache policy: sc1 (agent coherent)
+
+template <bool kCoherent = false, typename F>
 __device__ __forceinline__ void for_each_word(const uint32_t* keys, int nv, int nwords, F f, int w_start = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kBatch = 8;
@@ -829,7 +872,7 @@ __device__ __forceinline__ void for_each_word(const uint32_t* keys, int nv, int 
 #pragma unroll
     for (int u = 0; u < kBatch; u++) {
       const int j = (wb + u * (kSelThreads / 64)) * 64 + lane;
-      kk[u] = keys[j < nv ? j : 0];      // past the count: ignored by f (j >= nv)
+      kk[u] = load_key<kCoherent>(keys + (j < nv ? j : 0));      // past the count: ignored by f (j >= nv)
     }
 #pragma unroll
     for (int u = 0; u < kBatch; u++) {
@@ -876,18 +919,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_row_rsrc(const uint32_t* k
                                            kBufferWord3);
 }
 
-template <int NV>
+template <int NV, int kAux = 0>
 __device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t row, int64_t stride, int b0, uint4 (&kv)[NV]) {
   b0 = b0 + 4 * NV <= stride ? b0 : (int)stride - 4 * NV;
 #pragma unroll
   for (int v = 0; v < NV; v++) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(row, 4 * b0 + 16 * v, 0, 0);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(row, 4 * b0 + 16 * v, 0, kAux);
     kv[v] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
+template <int kAux = 0>
 __device__ __forceinline__ void load_round(__amdgpu_buffer_rsrc_t row, int64_t stride, int r, uint4 (&kv)[16]) {
-  load_keys(row, stride, r * kRoundKeys + 64 * (int)threadIdx.x, kv);
+  load_keys<16, kAux>(row, stride, r * kRoundKeys + 64 * (int)threadIdx.x, kv);
 }
 
 // Step 1 on the histogram held as thread t's bins 8t .. 8t+7 (hv0, hv1):
@@ -1055,6 +1099,7 @@ __device__ __forceinline__ void rank_listed(const uint32_t* cand, uint32_t nc, u
 // Steps 2-3 when too many keys share bin tb: radix select over every key
 // (12 + 12 + 8 bits), then every key above the threshold T and the
 // lowest-index keys equal to T.  Writes every bitmap word of the row.
+template <bool kCoherent = false>
 __device__ __forceinline__ void select_all(const uint32_t* keys, int nv, uint32_t k, uint32_t* hist,
                                            uint32_t* tmp, uint32_t* found, uint32_t* cand, uint32_t* bitmap) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1066,7 +1111,7 @@ __device__ __forceinline__ void select_all(const uint32_t* keys, int nv, uint32_
     const uint32_t nb = 1u << width, mask = nb - 1;
     for (uint32_t j = tid; j < nb; j += kSelThreads) hist[j] = 0;
     __syncthreads();
-    for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+    for_each_word<kCoherent>(keys, nv, nwords, [&](int w, int j, uint32_t key) {
       if (j < nv && (d == 0 || (key >> (shift + width)) == pfx))
         atomicAdd(&hist[(key >> shift) & mask], 1u);
     });
@@ -1079,7 +1124,7 @@ __device__ __forceinline__ void select_all(const uint32_t* keys, int nv, uint32_
   const uint32_t T = pfx, need_eq = need;
   // equal keys per 64-block word (the candidate list doubles as the counts)
   uint32_t* eqc = cand;       // 2 * kCandCap >= kMaxWords counters
-  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+  for_each_word<kCoherent>(keys, nv, nwords, [&](int w, int j, uint32_t key) {
     const uint64_t gm = __ballot(j < nv && key > T);
     const uint64_t em = __ballot(j < nv && key == T);
     if (lane == 0) {
@@ -1101,7 +1146,7 @@ __device__ __forceinline__ void select_all(const uint32_t* keys, int nv, uint32_
     run += c;
   }
   __syncthreads();
-  for_each_word(keys, nv, nwords, [&](int w, int j, uint32_t key) {
+  for_each_word<kCoherent>(keys, nv, nwords, [&](int w, int j, uint32_t key) {
     const bool eq = j < nv && key == T;
     const uint64_t em = __ballot(eq);
     const uint32_t rank = eqc[w] + (uint32_t)__popcll(em & ((1ull << lane) - 1ull));
@@ -1163,18 +1208,19 @@ __device__ __forceinline__ int visible_blocks(const SelectArgs& a, int srow) {
   return nv;
 }
 
-__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) {
-  const int srow = blockIdx.x;
+// Steps 1-4 for query row srow on one workgroup of kSelThreads threads, with
+// the LDS arrays passed in: hist (kHistBins words), tmp (64), found (4),
+// cand (2 kCandCap), bitmap (2 kMaxWords).  kCoherent: the histogram and
+// keys were written earlier in the same launch (agent-scope stores and
+// atomics), so they are read with agent-scope loads.
+template <bool kCoherent>
+__device__ __forceinline__ void select_row(const SelectArgs& a, int srow, uint32_t* hist, uint32_t* tmp,
+                                           uint32_t* found, uint32_t* cand, uint32_t* bitmap) {
+  constexpr int kAux = kCoherent ? kCoherentAux : 0;
   const int k = a.k, tid = threadIdx.x;
   int32_t* out = a.topk + (int64_t)srow * k;
   const uint32_t* keys = a.keys + (int64_t)srow * a.stride;
   uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
-
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t tmp[64];
-  __shared__ uint32_t found[4];
-  __shared__ uint32_t cand[2 * kCandCap];      // listed keys, then their blocks (block order)
-  __shared__ uint32_t bitmap[2 * kMaxWords];   // bit j of word w: block 32 w + j
 
   // The histogram loads go out first, then the keys of rounds 0 and 1, so
   // that the histogram phase does not wait for the keys (loads complete in
@@ -1182,16 +1228,16 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
   // addressed within the key row, and the length comes through the scalar
   // cache after they are issued.  Round r + 2 is loaded while round r + 1
   // is processed (two register sets, no copies).
-  const uint4 hv0 = reinterpret_cast<const uint4*>(gh)[2 * tid];
-  const uint4 hv1 = reinterpret_cast<const uint4*>(gh)[2 * tid + 1];
+  uint4 hv[2];
+  load_keys<2, kAux>(key_row_rsrc(gh, kHistBins), kHistBins, 8 * tid, hv);
   const __amdgpu_buffer_rsrc_t krow = key_row_rsrc(keys, a.stride);
   uint4 ka[16], kb[16];
-  load_round(krow, a.stride, 0, ka);
-  load_round(krow, a.stride, 1, kb);
+  load_round<kAux>(krow, a.stride, 0, ka);
+  load_round<kAux>(krow, a.stride, 1, kb);
   const int nv = visible_blocks(a, srow);
   const int rounds = (nv + kRoundKeys - 1) / kRoundKeys;
   if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
-  threshold_bin(hv0, hv1, (uint32_t)k, tmp, found, gh);
+  threshold_bin(hv[0], hv[1], (uint32_t)k, tmp, found, gh);
   if (nv <= k) {
     for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
     return;
@@ -1217,16 +1263,25 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) 
   for (int r = 0; r < rounds; r += 2) {
     one_round(ka, r);
     if (r + 1 >= rounds) break;
-    load_round(krow, a.stride, r + 2, ka);
+    load_round<kAux>(krow, a.stride, r + 2, ka);
     one_round(kb, r + 1);
-    load_round(krow, a.stride, r + 3, kb);
+    load_round<kAux>(krow, a.stride, r + 3, kb);
   }
 
   if (nc <= (uint32_t)kCandCap)
     rank_listed(cand, nc, tb, above, (uint32_t)k, hist, tmp, found, bitmap);
   else
-    select_all(keys, nv, (uint32_t)k, hist, tmp, found, cand, bitmap);
+    select_all<kCoherent>(keys, nv, (uint32_t)k, hist, tmp, found, cand, bitmap);
   compact(bitmap, nv, k, out, tmp);
+}
+
+__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t tmp[64];
+  __shared__ uint32_t found[4];
+  __shared__ uint32_t cand[2 * kCandCap];      // listed keys, then their blocks (block order)
+  __shared__ uint32_t bitmap[2 * kMaxWords];   // bit j of word w: block 32 w + j
+  select_row<false>(a, blockIdx.x, hist, tmp, found, cand, bitmap);
 }
 
 // Step 2 of one part of kPartKeys blocks (blockIdx.x) of one query
@@ -1631,6 +1686,12 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   const char* cenv = getenv("LCA_TOPK_CAND");
   if (cenv && *cenv) pl.cand = pl.tile && atoi(cenv) != 0;
   if (pl.cand) sliced = false;
+  // opt-in: one query per row and one selection workgroup per row, the
+  // scoring's last workgroup of each row selects in the same launch (saves a
+  // launch, but measured no faster than two launches in a replayed graph)
+  pl.fused = false;
+  const char* fenv = getenv("LCA_TOPK_FUSED");
+  if (fenv && *fenv) pl.fused = !pl.tile && !sliced && atoi(fenv) != 0;
   pl.cand_waves = kTileWavesPerSet;
   pl.cand_lists = pl.cand ? pl.chunks * kTileWavesPerSet * 32 : 0;
   pl.cand_span = pl.cpw * kScoreBlocksPerWG;
@@ -1641,6 +1702,7 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   pl.part_cand_bytes = (size_t)rows * pl.slices * 2 * kCandCap * sizeof(uint32_t);
   if (pl.cand) pl.keys_bytes *= 2;     // (key, visit) pairs
   pl.cand_count_bytes = pl.cand ? up((size_t)rows * pl.chunks * kTileWavesPerSet * 32 * sizeof(uint32_t)) : 0;
+  pl.row_done_bytes = pl.fused ? up((size_t)rows * sizeof(uint32_t)) : 0;
   return pl;
 }
 
@@ -1665,22 +1727,7 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   char* cand = static_cast<char*>(ws) + pl.hist_bytes + pl.keys_bytes + pl.part_count_bytes + pl.part_bits_bytes +
                pl.part_cand_bytes;
   s.cand_count = pl.cand ? reinterpret_cast<uint32_t*>(cand) : nullptr;
-  {
-    TimedLaunch t(kKernelIndexerScore, stream);
-    const dim3 tg(pl.chunks, pl.qgroups, L->batch), tb(64 * kTileWaves);
-    if (pl.tile == 8 && pl.cand)
-      hipLaunchKernelGGL((indexer_score_tile_kernel<8, true>), tg, tb, 0, stream, s);
-    else if (pl.tile == 8)
-      hipLaunchKernelGGL((indexer_score_tile_kernel<8, false>), tg, tb, 0, stream, s);
-    else if (pl.tile == 4 && pl.cand)
-      hipLaunchKernelGGL((indexer_score_tile_kernel<4, true>), tg, tb, 0, stream, s);
-    else if (pl.tile == 4)
-      hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
-    else
-      hipLaunchKernelGGL(indexer_score_kernel, dim3(pl.chunks, rows), dim3(256), 0, stream, s);
-    int rc = t.done();
-    if (rc) return rc;
-  }
+  s.row_done = pl.fused ? reinterpret_cast<uint32_t*>(cand + pl.cand_count_bytes) : nullptr;
   SelectArgs sa;
   sa.n_q = n_q;
   sa.m = L->ratio;
@@ -1698,6 +1745,24 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.cand_count = s.cand_count;
   sa.segs = pl.cand_lists / 32;
   sa.span = pl.cand_span;
+  {
+    TimedLaunch t(kKernelIndexerScore, stream);
+    const dim3 tg(pl.chunks, pl.qgroups, L->batch), tb(64 * kTileWaves);
+    if (pl.tile == 8 && pl.cand)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<8, true>), tg, tb, 0, stream, s);
+    else if (pl.tile == 8)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<8, false>), tg, tb, 0, stream, s);
+    else if (pl.tile == 4 && pl.cand)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<4, true>), tg, tb, 0, stream, s);
+    else if (pl.tile == 4)
+      hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
+    else if (pl.fused)   // the selection runs in the same launch
+      hipLaunchKernelGGL(indexer_score_kernel<true>, dim3((pl.chunks + 1) / 2, rows), dim3(512), 0, stream, s, sa);
+    else
+      hipLaunchKernelGGL(indexer_score_kernel<false>, dim3(pl.chunks, rows), dim3(256), 0, stream, s, sa);
+    int rc = t.done();
+    if (rc || pl.fused) return rc;
+  }
   // one timed interval covers the selection's one or two launches
   TimedLaunch t(kKernelTopkSelect, stream);
   if (pl.cand) {

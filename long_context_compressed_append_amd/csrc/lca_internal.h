@@ -52,8 +52,11 @@ struct IndexerPlan {
   int cand_waves;       // wavefronts per tile workgroup
   int cand_span;        // blocks per chunk
   size_t cand_count_bytes;
+  bool fused;           // decode scoring selects in its own launch (per-row counters at the end)
+  size_t row_done_bytes;
   size_t total() const {
-    return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes + cand_count_bytes;
+    return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes + cand_count_bytes +
+           row_done_bytes;
   }
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);

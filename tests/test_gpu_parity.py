@@ -130,11 +130,13 @@ INDEXER_CASES = [
 # environment switches: the selection split over workgroups, the score
 # kernel that shares key tiles across a row's queries, with candidate lists
 # where a row has at most 64 of them (tile), always (tile_cand) or never
-# (tile_full)
+# (tile_full); with fused, one query per row selects inside the scoring
+# launch
 INDEXER_MODES = {"auto": {}, "sliced": {"LCA_TOPK_SLICED": "1"}, "tile": {"LCA_SCORE_TILE": "1"},
                  "tile_cand": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "1"},
                  "tile_full": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "0"},
-                 "no_tile": {"LCA_SCORE_TILE": "0"}}
+                 "no_tile": {"LCA_SCORE_TILE": "0"},
+                 "fused": {"LCA_TOPK_FUSED": "1", "LCA_TOPK_SLICED": "0"}}
 
 # oracle results per case, shared by the modes
 _ORACLE = {}
@@ -190,7 +192,7 @@ def test_indexer_topk_parity(case, mode, monkeypatch):
             assert set(nd) <= set(got[b, -1].tolist())
 
 
-TIE_MODES = ["auto", "sliced", "tile_cand"]
+TIE_MODES = ["auto", "sliced", "tile_cand", "fused"]
 
 
 @pytest.mark.parametrize("mode", TIE_MODES)
