@@ -172,8 +172,10 @@ __device__ __forceinline__ v8h_t bf16x8_to_f16(uint4 w) {
 }
 
 __device__ __forceinline__ uint32_t ord_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: every bit flipped; otherwise the sign bit set (one xor with
+  // the sign spread over the word, sign bit forced)
+  const uint32_t u = __float_as_uint(s);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 }  // namespace lca
