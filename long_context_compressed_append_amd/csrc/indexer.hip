@@ -31,7 +31,14 @@
 // While scoring, each workgroup histograms the top 12 bits of its order keys
 // and adds them to a per-query histogram; the selection reads that histogram
 // to find the bin that holds the k-th key, so it needs a single pass over the
-// keys plus an exact ranking of the few keys inside that bin.
+// keys plus an exact ranking of the few keys inside that bin.  For prefill
+// chunks the scoring keeps only keys above a running bound derived from its
+// own histogram (candidate lists), and the selection passes over those.
+//
+// Kernels: indexer_score_kernel (one query per row; optionally selecting in
+// the same launch), indexer_score_tile_kernel (many queries per row),
+// topk_select_kernel / topk_slice_kernel + topk_finish_kernel (selection over
+// full key rows), topk_cand_kernel (selection over candidate lists).
 #include "lca_device.h"
 #include "lca_internal.h"
 
