@@ -324,26 +324,45 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     // O^T += V^T P^T over the 32 channel tiles.  The tile holds code values,
     // so each 64-dim group's FP8 scale goes into P: B operand of group gl =
     // fp16(p_j * scale of key j's group), for the group's four channel tiles.
-#pragma unroll
-    for (int gl = 0; gl < 8; gl++) {
+    // Software-pipelined by hand: the transpose reads of tile c + 1 and the
+    // scales of the next group go out before the product of tile c, so each
+    // product waits only for reads issued a step earlier (LDS reads complete
+    // in order); scheduling barriers keep that order.
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    auto tr_pair = [&](int c, v4s& lo, v4s& hi) {
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
+    };
+    auto scales = [&](int gl, v4f& s0, v4f& s1) {
       const float* sg0 = sK[cur] + gl * kTile + 4 * g;
-      const v4f s0 = *reinterpret_cast<const v4f*>(sg0);
-      const v4f s1 = *reinterpret_cast<const v4f*>(sg0 + 16);
-      v8h pb;
+      s0 = *reinterpret_cast<const v4f*>(sg0);
+      s1 = *reinterpret_cast<const v4f*>(sg0 + 16);
+    };
+    v4s lo_c, hi_c;
+    v4f s0, s1;
+    scales(0, s0, s1);
+    tr_pair(0, lo_c, hi_c);
+    v8h pb;
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        pb[r] = (_Float16)__fmul_rn(pj[r], s0[r]);
-        pb[4 + r] = (_Float16)__fmul_rn(pj[4 + r], s1[r]);
+    for (int c = 0; c < 32; c++) {
+      if ((c & 3) == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          pb[r] = (_Float16)__fmul_rn(pj[r], s0[r]);
+          pb[4 + r] = (_Float16)__fmul_rn(pj[4 + r], s1[r]);
+        }
       }
-#pragma unroll
-      for (int c4 = 0; c4 < 4; c4++) {
-        const int c = 4 * gl + c4;
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow1 + 16 * c));
-        const v4h lo_h = __builtin_bit_cast(v4h, lo), hi_h = __builtin_bit_cast(v4h, hi);
-        const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
+      if ((c & 3) == 2 && c + 2 < 32) scales((c + 2) >> 2, s0, s1);
+      v4s lo_n, hi_n;
+      if (c + 1 < 32) tr_pair(c + 1, lo_n, hi_n);
+      __builtin_amdgcn_sched_barrier(0);
+      const v4h lo_h = __builtin_bit_cast(v4h, lo_c), hi_h = __builtin_bit_cast(v4h, hi_c);
+      const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 < 32) {
+        lo_c = lo_n;
+        hi_c = hi_n;
       }
     }
     __syncthreads();                       // tile t + 1 staged, tile t consumed
