@@ -125,6 +125,9 @@ INDEXER_CASES = [
     ("chunk_nq64_h16_k256", 2, [30000, 20011], 64, 16, 256, 0),
     ("chunk_nq37_h32_k128", 1, [9000], 37, 32, 128, 0),
     ("chunk_nq20_h5_k64", 2, [3000, 2100], 20, 5, 64, 0),
+    # a chunk right after a short prior: the first queries see at most k
+    # blocks, the later ones a few more
+    ("chunk_short_prior_k64", 1, [300], 64, 16, 64, 0),
 ]
 
 # environment switches: the selection split over workgroups, the score
