@@ -268,6 +268,32 @@ def test_indexer_exponent_extremes(mode, monkeypatch):
     assert np.array_equal(got, want)
 
 
+_MAX_CASE = {}
+
+
+@pytest.mark.parametrize("mode", ["auto", "single", "fused"])
+def test_indexer_max_blocks(mode, monkeypatch):
+    """The longest row the indexer takes: 524 288 blocks (2^21 tokens at
+    m = 4), which fills the whole selection bitmap: 16 rounds of the single
+    workgroup, 32 part workgroups of the sliced selection (taken by default
+    for one such row), or the selection inside the scoring launch."""
+    lca = _lca()
+    say("indexer max blocks", mode)
+    env = {"auto": {}, "single": {"LCA_TOPK_SLICED": "0"},
+           "fused": {"LCA_TOPK_SLICED": "0", "LCA_TOPK_FUSED": "1"}}[mode]
+    for var, val in env.items():
+        monkeypatch.setenv(var, val)
+    B, m, k, H_I, MB = 1, 4, 256, 8, 524288
+    if not _MAX_CASE:
+        ref = SL.make_layer(80, "max", B, m, 128, 256, 1, MB, [MB * m])
+        Q = SL.queries(80, "max", B, 1, 16, H_I)
+        _MAX_CASE.update(ref=ref, Q=Q, want=oracle.indexer_topk(ref, Q["iq"], Q["iw"], k))
+    ref, Q, want = _MAX_CASE["ref"], _MAX_CASE["Q"], _MAX_CASE["want"]
+    lay = lca.Layer.from_host(ref)
+    got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k).cpu().numpy()
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------------------ attention
 
 ATTEND_CASES = [
