@@ -306,6 +306,10 @@ ATTEND_CASES = [
     ("csa_h16_k64_pad", 1, 2, [300, 100], 2, 16, 64, 0),
     ("csa_h64_k512_onesplit", 1, 1, [8000], 1, 64, 512, 1),
     ("short_rows", 0, 2, [1, 3], 1, 64, 0, 0),
+    # the largest shapes the ABI takes: 128 heads (two head groups), k = 2048
+    # (more keys than one split stages)
+    ("csa_h128_k2048", 1, 1, [12000], 2, 128, 2048, 0),
+    ("hca_h128_onesplit", 0, 1, [40000], 1, 128, 0, 1),
 ]
 
 
