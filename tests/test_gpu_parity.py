@@ -128,6 +128,9 @@ INDEXER_CASES = [
     # a chunk right after a short prior: the first queries see at most k
     # blocks, the later ones a few more
     ("chunk_short_prior_k64", 1, [300], 64, 16, 64, 0),
+    # the smallest shapes: one indexer head, k = 1
+    ("h1_k1", 2, [4000, 2001], 1, 1, 1, 0),
+    ("chunk_nq16_h1_k1", 1, [3000], 16, 1, 1, 0),
 ]
 
 # environment switches: the selection split over workgroups, the score
