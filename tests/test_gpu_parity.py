@@ -405,3 +405,48 @@ def test_errors_enqueue_nothing():
         lca.indexer_topk(lay, torch.zeros((1, 1, 4, 64), device="cuda"),
                          torch.zeros((1, 1, 4), device="cuda"), 8)   # n_q > shortest row
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("kind,n_q", [("csa", 1), ("csa", 64), ("hca", 1)], ids=["csa_decode", "csa_chunk", "hca"])
+def test_graph_replay_matches_eager(kind, n_q):
+    """The selection and attention calls captured in a HIP graph and replayed
+    three times, with eager launches of the same calls between the replays:
+    every replay gives the eager results bit for bit (no memset nodes in the
+    graph; every call leaves its workspace ready for the next)."""
+    lca = _lca()
+    say("graph replay", kind, n_q)
+    csa = kind == "csa"
+    B, m, L, H, HI, k = 2, (4 if csa else 128), 20000, 64, 16, 256
+    ref = SL.make_layer(91, "graph" + kind, B, m, 128, 256, int(csa), L // m + 8, [L, L - 5])
+    Q = SL.queries(91, "graph" + kind, B, n_q, H, HI if csa else 0)
+    lay = lca.Layer.from_host(ref)
+    q = _dev(Q["q"])
+    topk = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, n_q, H, 512), dtype=torch.float32, device="cuda")
+
+    def step():
+        if csa:
+            lca.indexer_topk(lay, iq, iw, k, out=topk)
+            lca.csa_attend(lay, q, topk, float(SCALE), out=out)
+        else:
+            lca.hca_attend(lay, q, float(SCALE), out=out)
+
+    iq, iw = (_dev(Q["iq"]), _dev(Q["iw"])) if csa else (None, None)
+    step()                                  # eager: allocates the workspaces
+    torch.cuda.synchronize()
+    t_ref, o_ref = topk.clone(), out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        topk.zero_()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert (not csa or torch.equal(topk, t_ref)) and torch.equal(out, o_ref), ("replay", rep)
+        step()
+        torch.cuda.synchronize()
+        assert (not csa or torch.equal(topk, t_ref)) and torch.equal(out, o_ref), ("eager", rep)
