@@ -450,3 +450,56 @@ def test_graph_replay_matches_eager(kind, n_q):
         step()
         torch.cuda.synchronize()
         assert (not csa or torch.equal(topk, t_ref)) and torch.equal(out, o_ref), ("eager", rep)
+
+
+def test_graph_replay_with_append():
+    """A whole CSA decode step (append, selection, attention) captured once
+    with plans for the longest length it will reach, replayed six times; an
+    eager twin of the layer takes the same six steps.  After every step the
+    top-k lists, the outputs and the row lengths agree bit for bit, and so do
+    the cache planes at the end."""
+    lca = _lca()
+    B, m, L, H, HI, k, steps = 2, 4, 20001, 64, 16, 256, 6
+    say("graph replay with append", B, L, steps)
+    ref = SL.make_layer(92, "gapp", B, m, 128, 256, 1, (L + 64) // m + 8, [L, L - 6])
+    tok = SL.tokens(92, "gapp", B, 1, 1)
+    Q = SL.queries(92, "gapp", B, 1, H, HI)
+    lg, le = lca.Layer.from_host(ref), lca.Layer.from_host(ref)
+    d = {kk: _dev(v) for kk, v in tok.items()}
+    iq, iw, q = _dev(Q["iq"]), _dev(Q["iw"]), _dev(Q["q"])
+    bufs = {id(lay): (torch.empty((B, 1, k), dtype=torch.int32, device="cuda"),
+                      torch.empty((B, 1, H, 512), dtype=torch.float32, device="cuda")) for lay in (lg, le)}
+
+    def step(lay, plan_len=None):
+        lca.compress_append(lay, d["kv"], d["gate"], d["ikey"], d["igate"])
+        if plan_len is not None:
+            lay.len_max = plan_len
+        t, o = bufs[id(lay)]
+        lca.indexer_topk(lay, iq, iw, k, out=t)
+        lca.csa_attend(lay, q, t, float(SCALE), out=o)
+
+    final = L + steps + 2
+    before = (lg.len_min, lg.len_max)
+    lg.len_max = final                     # workspaces sized for the longest length
+    lg.workspace(lca.indexer_workspace_bytes(lg, 1, HI, k), "indexer")
+    lg.workspace(lca.attend_workspace_bytes(lg, 1, H, k), "attend")
+    lg.len_min, lg.len_max = before
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(lg, plan_len=final)
+    torch.cuda.synchronize()
+    lg.len_min, lg.len_max = before        # capture executes nothing
+    for r in range(steps):
+        g.replay()
+        step(le)
+        torch.cuda.synchronize()
+        (tg, og), (te, oe) = bufs[id(lg)], bufs[id(le)]
+        assert torch.equal(lg.seq_len, le.seq_len), r
+        assert torch.equal(tg, te), r
+        assert torch.equal(og, oe), r
+    a, b = lg.download(), le.download()
+    for f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv"):
+        assert np.array_equal(a[f], b[f]), f
