@@ -82,6 +82,11 @@ struct ScoreArgs {
   uint32_t* row_done;    // fused selection: workgroups of a row done, [rows], zero between calls
 };
 
+// max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
+// set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
+// output would first be canonicalised, a second instruction.)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // exact value of D0 * 2^e0 + D1 * 2^e1 rounded once to fp32, where D0, D1 are
 // multiples of 1/4 below 2^11 in magnitude
 __device__ __forceinline__ float exact_pair(float D0, int e0, float D1, int e1) {
@@ -227,8 +232,9 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   // capacity is readable, and blocks past the visible count are masked later.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wh = wave & 3;                       // wavefront within its half
-  const int64_t c0 = ((int64_t)blockIdx.x * (kFused ? 2 : 1) + (wave >> 2)) * a.cpw;
-  const int64_t cap = a.stride < a.max_blocks ? a.stride : a.max_blocks;
+  // Block indices fit 32 bits (a key row holds at most 524 288 blocks).
+  const int c0 = ((int)blockIdx.x * (kFused ? 2 : 1) + (wave >> 2)) * a.cpw;
+  const int cap = (int)(a.stride < a.max_blocks ? a.stride : a.max_blocks);
 
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
@@ -242,16 +248,16 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   // is group i % 8 of this wave's 256 blocks in chunk c0 + i / 8.  Keys are
   // loaded kDepth iterations ahead of their use.
   const int n_it = a.cpw * kScoreItersPerWave;
-  auto blk_of = [&](int i) -> int64_t {
+  auto blk_of = [&](int i) -> int {
     return (c0 + i / kScoreItersPerWave) * kScoreBlocksPerWG +
-           (int64_t)wh * (kScoreItersPerWave * kScoreBlocksPerIter) +
+           wh * (kScoreItersPerWave * kScoreBlocksPerIter) +
            (i % kScoreItersPerWave) * kScoreBlocksPerIter + r;
   };
   // Loads are unconditional (a block past the capacity reads block 0) so that
   // no load waits on another; compute() masks what they return.
   auto load = [&](int i, int4& kr, uint32_t& er) {
-    const int64_t blk = blk_of(i);
-    const int64_t b = (i < n_it && blk < cap) ? blk : 0;
+    const int blk = blk_of(i);
+    const int b = (i < n_it && blk < cap) ? blk : 0;
     kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
     er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
   };
@@ -277,7 +283,7 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   // the row length through the scalar cache, once every vector load is out
   typedef const int32_t __attribute__((address_space(4)))* const_i32p;
   const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
-  int64_t nv = (int64_t)(p + 1) / a.m;
+  int nv = (p + 1) / a.m;
   if (nv > cap) nv = cap;                      // defensive: never past the key row
 
   for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
@@ -304,15 +310,15 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   if (tid < a.H) q_w[tid] = wq;
   __syncthreads();
 
-  // A operands and their E8M0 scales: lane l feeds row l%32 with K-half l/32.
+  // A operands for the per-half products of the exact fallback (no scales):
+  // lane l feeds row l%32 with K-half l/32, row (head, half) holding only that
+  // half of the head.
   const int hgroups = (a.H + 15) >> 4;
   v8i A[2];
-  int sa[2];
-  int qmin = 1 << 20, qmax = -(1 << 20);
+  int qmin = 1 << 20, qmax = -(1 << 20), qdmin = 0, qdmax = 0;
 #pragma unroll
   for (int hg = 0; hg < 2; hg++) {
     A[hg] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-    sa[hg] = 127;
     const int G = (r & 7) >> 2, v = 4 * (r >> 3) + (r & 3);
     const int h = 16 * hg + 8 * G + (v >> 1), half = v & 1;
     if (hg < hgroups && half == kh && h < a.H) {
@@ -321,7 +327,23 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
       A[hg][1] = src[1];
       A[hg][2] = src[2];
       A[hg][3] = src[3];
-      sa[hg] = q_exp[h][kh] + 127;
+    }
+  }
+  // The same query with both MX halves of a head in one A row, for products
+  // that add the two halves in hardware: row 16 hg + 8 i + 4 s + j carries
+  // head 16 hg + 8 s + 4 i + j, so that output 8 hg + hl of a lane in set s
+  // is head 16 hg + 8 s + hl (its octet in order).
+  v8i Af = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  int saf = 127;
+  {
+    const int h = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+    if (h < a.H) {
+      const int* src = reinterpret_cast<const int*>(&q_code[h][16 * kh]);
+      Af[0] = src[0];
+      Af[1] = src[1];
+      Af[2] = src[2];
+      Af[3] = src[3];
+      saf = q_exp[h][kh] + 127;
     }
   }
   // Per-lane epilogue constants for the 8 heads of this lane's set (octet
@@ -339,7 +361,24 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
     const int e = lane < 2 * a.H ? q_exp[lane >> 1][lane & 1] : 0;
     qmin = wave_minmax<0>(lane < 2 * a.H ? e : (1 << 20));
     qmax = wave_minmax<1>(lane < 2 * a.H ? e : -(1 << 20));
+    // range of the heads' half-exponent differences: lane l looks at head l
+    const int d = lane < a.H ? q_exp[lane][0] - q_exp[lane][1] : 0;
+    qdmin = wave_minmax<0>(lane < a.H ? d : (1 << 20));
+    qdmax = wave_minmax<1>(lane < a.H ? d : -(1 << 20));
   }
+
+  // One product adding both halves gives the exactly rounded dot when every
+  // half's exponent sum E = query exponent + key exponent lies in [-124, 116]
+  // and the two sums of a head differ by at most 10: each half's products are
+  // multiples of 2^(E-2) below 1152 * 2^E, so every partial sum then needs at
+  // most 24 bits and is an exact fp32 number.  On the key's two E8M0 bytes
+  // (exponent + 127) these are the ranges byte in [3 - qmin, 243 - qmax] and
+  // byte0 - byte1 in [-10 - qdmin, 10 - qdmax], each checked as one unsigned
+  // comparison (an empty range admits nothing).
+  int byte_lo = 3 - qmin, diff_lo = -10 - qdmin;
+  uint32_t byte_span = (uint32_t)(243 - qmax - byte_lo), diff_span = (uint32_t)(10 - qdmax - diff_lo);
+  if (243 - qmax < byte_lo) byte_lo = 1 << 30, byte_span = 0;
+  if (10 - qdmax < diff_lo) diff_lo = 1 << 30, diff_span = 0;
 
   uint32_t* out = a.keys + (int64_t)srow * a.stride;
   const v16f zero16 = {};
@@ -347,31 +386,29 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   // kDepth iterations at once: their matrix-core products and head chains are
   // independent, so they interleave; one range check covers the block.
   auto compute = [&](int i0, const int4 (&kr)[kDepth], const uint32_t (&er_in)[kDepth]) {
-    int ke0[kDepth], ke1[kDepth], sb[kDepth];
-    uint32_t er[kDepth];
+    int b0[kDepth], b1[kDepth], sb[kDepth];
     bool ok = true;
 #pragma unroll
     for (int u = 0; u < kDepth; u++) {
       // a block that is not scored takes unit scales (its result is dropped)
-      er[u] = blk_of(i0 + u) < nv ? er_in[u] : 0x7F7Fu;
-      ke0[u] = (int)(er[u] & 0xFF) - 127;
-      ke1[u] = (int)(er[u] >> 8) - 127;
-      sb[u] = kh ? (ke1[u] + 127) : (ke0[u] + 127);
-      // scaled partials stay normal fp32 when every exponent sum is in range
-      ok = ok && (qmin + min(ke0[u], ke1[u]) >= -124) && (qmax + max(ke0[u], ke1[u]) <= 116);
+      const uint32_t er = blk_of(i0 + u) < nv ? er_in[u] : 0x7F7Fu;
+      b0[u] = (int)(er & 0xFF);
+      b1[u] = (int)(er >> 8);
+      sb[u] = kh ? b1[u] : b0[u];
+      ok = ok & ((uint32_t)(b0[u] - byte_lo) <= byte_span) & ((uint32_t)(b1[u] - byte_lo) <= byte_span) &
+           ((uint32_t)(b0[u] - b1[u] - diff_lo) <= diff_span);
     }
     float total[kDepth];
     if (__all(ok)) {
+      v16f acc[kDepth];
+#pragma unroll
+      for (int u = 0; u < kDepth; u++) {
+        const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Af, Bm, zero16, 4, 4, 0, saf, 0, sb[u]);
+      }
 #pragma unroll
       for (int hg = 0; hg < 2; hg++) {
         if (hg < hgroups) {
-          v16f acc[kDepth];
-#pragma unroll
-          for (int u = 0; u < kDepth; u++) {
-            const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
-            acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[hg], Bm, zero16, 4, 4, 0, sa[hg],
-                                                                     0, sb[u]);
-          }
           // both lane sets fold their octet at once; the low set adds the octets
           float part[kDepth], upper[kDepth];
 #pragma unroll
@@ -379,8 +416,7 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
             part[u] = 0.0f;
 #pragma unroll
             for (int hl = 0; hl < 8; hl++)
-              part[u] = __builtin_fmaf(wv[hg][hl],
-                                       fmaxf(__fadd_rn(acc[u][2 * hl], acc[u][2 * hl + 1]), 0.0f), part[u]);
+              part[u] = __builtin_fmaf(wv[hg][hl], relu_bits(acc[u][8 * hg + hl]), part[u]);
           }
 #pragma unroll
           for (int u = 0; u < kDepth; u++) upper[u] = swap_halves(part[u]);
@@ -395,13 +431,13 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
 #pragma unroll
       for (int u = 0; u < kDepth; u++) {
         const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
-        total[u] = score_unscaled(A[0], A[1], Bm, hgroups, a.H, kh, q_exp, q_w, ke0[u], ke1[u]);
+        total[u] = score_unscaled(A[0], A[1], Bm, hgroups, a.H, kh, q_exp, q_w, b0[u] - 127, b1[u] - 127);
       }
     }
 #pragma unroll
     for (int u = 0; u < kDepth; u++) {
-      const int64_t blk = blk_of(i0 + u);
-      if (kh == 0 && i0 + u < n_it && blk < nv) {
+      const int blk = blk_of(i0 + u);
+      if ((kh == 0) & (i0 + u < n_it) & (blk < nv)) {
         const uint32_t key = ord_key(__fadd_rn(total[u], 0.0f));   // -0 -> +0
         if (kFused)
           __hip_atomic_store(&out[blk], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -490,10 +526,6 @@ constexpr int kTileTargetWGs = 1024;
 constexpr int kTileSets = 1;                         // query sets per workgroup
 constexpr int kTileWavesPerSet = kTileWaves / kTileSets;
 
-// max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
-// set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
-// output would first be canonicalised, a second instruction.)
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 template <int kQw>   // queries per wavefront: 8 (H <= 16) or 4 (H <= 32)
 __device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, int set,
