@@ -313,6 +313,10 @@ ATTEND_CASES = [
     # (more keys than one split stages)
     ("csa_h128_k2048", 1, 1, [12000], 2, 128, 2048, 0),
     ("hca_h128_onesplit", 0, 1, [40000], 1, 128, 0, 1),
+    # many query rows of one chunk each (more workgroups than CUs), rows
+    # with a short window among them
+    ("csa_rows_nq300_h64_k64", 1, 2, [3000, 400], 300, 64, 64, 0),
+    ("csa_rows_nq200_h128_k96", 1, 1, [5000], 200, 128, 96, 0),
 ]
 
 
