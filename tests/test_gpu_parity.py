@@ -456,18 +456,22 @@ def test_graph_replay_matches_eager(kind, n_q):
         assert (not csa or torch.equal(topk, t_ref)) and torch.equal(out, o_ref), ("eager", rep)
 
 
-def test_graph_replay_with_append():
-    """A whole CSA decode step (append, selection, attention) captured once
-    with plans for the longest length it will reach, replayed six times; an
-    eager twin of the layer takes the same six steps.  After every step the
-    top-k lists, the outputs and the row lengths agree bit for bit, and so do
-    the cache planes at the end."""
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_graph_replay_with_append(kind):
+    """A whole decode step (append, then selection and attention for CSA, or
+    attention over every entry for HCA) captured once with plans for the
+    longest length it will reach, replayed six times; an eager twin of the
+    layer takes the same six steps.  After every step the top-k lists, the
+    outputs and the row lengths agree bit for bit, and so do the cache planes
+    at the end.  The HCA rows cross a 128-token block boundary on the way."""
     lca = _lca()
-    B, m, L, H, HI, k, steps = 2, 4, 20001, 64, 16, 256, 6
-    say("graph replay with append", B, L, steps)
-    ref = SL.make_layer(92, "gapp", B, m, 128, 256, 1, (L + 64) // m + 8, [L, L - 6])
-    tok = SL.tokens(92, "gapp", B, 1, 1)
-    Q = SL.queries(92, "gapp", B, 1, H, HI)
+    csa = kind == "csa"
+    B, H, HI, k, steps = 2, 64, 16, 256, 6
+    m, L = (4, 20001) if csa else (128, 128 * 40 - 3)
+    say("graph replay with append", kind, B, L, steps)
+    ref = SL.make_layer(92, "gapp" + kind, B, m, 128, 256, int(csa), (L + 64) // m + 8, [L, L - 6])
+    tok = SL.tokens(92, "gapp" + kind, B, 1, 1)
+    Q = SL.queries(92, "gapp" + kind, B, 1, H, HI)
     lg, le = lca.Layer.from_host(ref), lca.Layer.from_host(ref)
     d = {kk: _dev(v) for kk, v in tok.items()}
     iq, iw, q = _dev(Q["iq"]), _dev(Q["iw"]), _dev(Q["q"])
@@ -479,14 +483,18 @@ def test_graph_replay_with_append():
         if plan_len is not None:
             lay.len_max = plan_len
         t, o = bufs[id(lay)]
-        lca.indexer_topk(lay, iq, iw, k, out=t)
-        lca.csa_attend(lay, q, t, float(SCALE), out=o)
+        if csa:
+            lca.indexer_topk(lay, iq, iw, k, out=t)
+            lca.csa_attend(lay, q, t, float(SCALE), out=o)
+        else:
+            lca.hca_attend(lay, q, float(SCALE), out=o)
 
     final = L + steps + 2
     before = (lg.len_min, lg.len_max)
     lg.len_max = final                     # workspaces sized for the longest length
-    lg.workspace(lca.indexer_workspace_bytes(lg, 1, HI, k), "indexer")
-    lg.workspace(lca.attend_workspace_bytes(lg, 1, H, k), "attend")
+    if csa:
+        lg.workspace(lca.indexer_workspace_bytes(lg, 1, HI, k), "indexer")
+    lg.workspace(lca.attend_workspace_bytes(lg, 1, H, k if csa else 0), "attend")
     lg.len_min, lg.len_max = before
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -502,8 +510,11 @@ def test_graph_replay_with_append():
         torch.cuda.synchronize()
         (tg, og), (te, oe) = bufs[id(lg)], bufs[id(le)]
         assert torch.equal(lg.seq_len, le.seq_len), r
-        assert torch.equal(tg, te), r
+        assert not csa or torch.equal(tg, te), r
         assert torch.equal(og, oe), r
     a, b = lg.download(), le.download()
-    for f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv"):
-        assert np.array_equal(a[f], b[f]), f
+    planes = ("nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv")
+    for f in planes:
+        if f in a:
+            assert np.array_equal(a[f], b[f]), f
+    assert int(b["seq_len"][0]) // m > L // m     # a block was finalised on the way
