@@ -518,3 +518,28 @@ def test_graph_replay_with_append(kind):
         if f in a:
             assert np.array_equal(a[f], b[f]), f
     assert int(b["seq_len"][0]) // m > L // m     # a block was finalised on the way
+
+
+@pytest.mark.parametrize("n_q", [1, 20], ids=["decode", "chunk"])
+def test_ratio1_csa_and_window_only(n_q):
+    """Two layer variants on the same kernels: CSA at ratio 1 (the selection
+    runs over the raw tokens, one block per token) through the indexer and
+    the attention, and attention over the window alone (every list entry -1,
+    as in a plain sliding-window layer)."""
+    lca = _lca()
+    B, lens, H, H_I, k, W = 2, [3000, 2411], 64, 16, 256, 128
+    say("ratio-1 CSA and window-only", "n_q", n_q, "lens", lens)
+    ref = SL.make_layer(6100 + n_q, "r1", B, 1, W, 256, 1, max(lens) + 8, lens)
+    Q = SL.queries(6100 + n_q, "r1", B, n_q, H, H_I)
+    lay = lca.Layer.from_host(ref)
+    topk = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
+    torch.cuda.synchronize()
+    want_idx = oracle.indexer_topk(ref, Q["iq"], Q["iw"], k)
+    assert np.array_equal(topk.cpu().numpy(), want_idx)
+    got = lca.csa_attend(lay, _dev(Q["q"]), topk, float(SCALE))
+    torch.cuda.synchronize()
+    assert attn_rel_err(got.cpu().numpy(), oracle.csa_attend(ref, Q["q"], want_idx, SCALE)) <= ATTN_TOL
+    none = np.full((B, n_q, 64), -1, np.int32)
+    got = lca.csa_attend(lay, _dev(Q["q"]), _dev(none), float(SCALE))
+    torch.cuda.synchronize()
+    assert attn_rel_err(got.cpu().numpy(), oracle.csa_attend(ref, Q["q"], none, SCALE)) <= ATTN_TOL
