@@ -55,10 +55,12 @@ INTERLEAVED = {
 
 # Prefill chunk: one row with a prior context given as a cache image, then a
 # chunk of new tokens through compress_append, indexer_topk for every chunk
-# query (causal) and csa_attend.
+# query (causal) and csa_attend -- or, for HCA (no indexer), hca_attend over
+# every block visible to each query.
 # name: (prior tokens, chunk, ratio, heads, indexer heads, k, window, ring)
 PREFILL = {
     "csa_prefill_chunk": (262144, 4096, 4, 64, 16, 512, 128, 8192),
+    "hca_prefill_chunk": (262144, 4096, 128, 64, 0, 0, 128, 8192),
 }
 FP16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 matrix cores
 FP8_MFMA_PEAK_TFLOPS = 5000.0      # dense FP8-rate matrix peak (the scoring's FP8-rate reference)
@@ -187,10 +189,11 @@ def run_prefill(args):
     from synth import layers as SL
 
     prior, n, m, H, HI, k, W, R = PREFILL[args.workload]
+    csa = HI > 0
     seed, tag = 1004, "prefill"
     t = time.time()
-    ref = SL.make_layer(seed, tag, 1, m, W, R, 1, (prior + n) // m + 64, [prior])
-    tok = SL.tokens(seed, "chunk", 1, n, 1)
+    ref = SL.make_layer(seed, tag, 1, m, W, R, int(csa), (prior + n) // m + 64, [prior])
+    tok = SL.tokens(seed, "chunk", 1, n, int(csa))
     Q = SL.queries(seed, tag, 1, n, H, HI)
     log(f"host image built in {time.time() - t:.1f}s")
     dev = torch.device("cuda", 0)
@@ -204,8 +207,9 @@ def run_prefill(args):
 
     lay = lca.Layer.from_host(ref, device=dev)
     d_tok = {kk: up(v) for kk, v in tok.items()}
-    iq, iw, q = up(Q["iq"]), up(Q["iw"]), up(Q["q"])
-    topk = torch.empty((1, n, k), dtype=torch.int32, device=dev)
+    q = up(Q["q"])
+    iq, iw = (up(Q["iq"]), up(Q["iw"])) if csa else (None, None)
+    topk = torch.empty((1, n, max(k, 1)), dtype=torch.int32, device=dev)
     out = torch.empty((1, n, H, 512), dtype=torch.float32, device=dev)
     scale = float(1.0 / np.sqrt(512.0))
 
@@ -214,9 +218,13 @@ def run_prefill(args):
         lay.len_min = lay.len_max = prior
 
     def step():
-        lca.compress_append(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"])
-        lca.indexer_topk(lay, iq, iw, k, out=topk)
-        lca.csa_attend(lay, q, topk, scale, out=out)
+        if csa:
+            lca.compress_append(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"])
+            lca.indexer_topk(lay, iq, iw, k, out=topk)
+            lca.csa_attend(lay, q, topk, scale, out=out)
+        else:
+            lca.compress_append(lay, d_tok["kv"], d_tok["gate"])
+            lca.hca_attend(lay, q, scale, out=out)
 
     for _ in range(args.warmup):
         reset()
@@ -248,26 +256,34 @@ def run_prefill(args):
     flops, pairs = prefill_score_flops(prior, n, m, HI)
     score_us = kernels.get("indexer_score", 0.0)
     tflops = flops / (score_us * 1e-6) / 1e12 if score_us else 0.0
-    att_flops = prefill_attend_flops(prior, n, m, H, k, W)
+    # HCA attends to every visible block: a list longer than any row
+    att_flops = prefill_attend_flops(prior, n, m, H, k if csa else (prior + n) // m + 1, W)
     att_us = kernels.get("attend", 0.0)
     att_tflops = att_flops / (att_us * 1e-6) / 1e12 if att_us else 0.0
-    # the roofline object covers the scoring, the prefill target (FP4 operands,
-    # priced at the FP8 rate); the attention, the longer kernel here, is
-    # reported beside it against the fp16 peak
-    roof = {"kernel": "indexer_score", "bound": "mfma", "achieved": round(tflops, 1),
-            "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel_avg_us": score_us, "flops_per_launch": flops}
+    if csa:
+        # the roofline object covers the scoring, the prefill target (FP4
+        # operands, priced at the FP8 rate); the attention, the longer kernel
+        # here, is reported beside it against the fp16 peak
+        roof = {"kernel": "indexer_score", "bound": "mfma", "achieved": round(tflops, 1),
+                "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel_avg_us": score_us, "flops_per_launch": flops}
+    else:
+        roof = {"kernel": "attend", "bound": "mfma", "achieved": round(att_tflops, 1),
+                "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(att_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel_avg_us": att_us, "flops_per_launch": att_flops}
     cpu = None
     if not args.no_cpu_baseline:
         try:
-            cpu = prefill_cpu_baseline(ref, tok, Q, prior, n, m, k)
+            cpu = prefill_cpu_baseline(ref, tok, Q, prior, n, m, k, csa)
         except Exception as e:  # report, never hide
             cpu = dict(error=repr(e))
     res = {
         "metric": METRIC,
         "value": round(n / (ms_per_step / 1e3), 1),
-        "unit": "queries/s (prefill chunk tokens through compress + indexer + top-k + attention)",
+        "unit": ("queries/s (prefill chunk tokens through compress + indexer + top-k + attention)" if csa
+                 else "queries/s (prefill chunk tokens through compress + dense attention)"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -275,7 +291,8 @@ def run_prefill(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4 scoring (exact fp32 scores); fp8/bf16 storage; bf16/fp16 MFMA attention",
+        "dtype": ("fp4 scoring (exact fp32 scores); fp8/bf16 storage; bf16/fp16 MFMA attention" if csa
+                  else "fp8/bf16 storage; bf16/fp16 MFMA attention"),
         "data": "synthetic (seeded cache image of the prior context, N(0,1) chunk)",
         "config": {
             "workload": args.workload, "batch": 1, "prior_tokens": prior, "chunk": n, "ratio": m,
@@ -295,30 +312,36 @@ def run_prefill(args):
     print(json.dumps(res), flush=True)
 
 
-def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k):
+def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k, csa=True):
     """The oracle on a sample of the chunk: the whole compress_append, then
-    indexer_topk and csa_attend for 4 of the chunk's queries (each on a view
-    whose length ends at that query)."""
+    indexer_topk and csa_attend (HCA: hca_attend) for 4 of the chunk's queries
+    (each on a view whose length ends at that query)."""
     import oracle
     nthreads = min(16, len(os.sched_getaffinity(0)))
     scale = np.float32(1.0 / np.sqrt(512.0))
     V = oracle.row_view(ref, 0)
     t0 = time.perf_counter()
-    oracle.compress_append(V, tok["kv"], tok["gate"], tok["ikey"], tok["igate"])
+    if csa:
+        oracle.compress_append(V, tok["kv"], tok["gate"], tok["ikey"], tok["igate"])
+    else:
+        oracle.compress_append(V, tok["kv"], tok["gate"])
     t_comp = time.perf_counter() - t0
     sample = (0, n // 3, 2 * n // 3, n - 1)
     t0 = time.perf_counter()
     for qi in sample:
         Vq = dict(V)
         Vq["seq_len"] = np.array([prior + qi + 1], np.int32)
-        tk = oracle.indexer_topk(Vq, Q["iq"][:, qi:qi + 1], Q["iw"][:, qi:qi + 1], k, nthreads=nthreads)
-        oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], tk, scale, nthreads=nthreads)
+        if csa:
+            tk = oracle.indexer_topk(Vq, Q["iq"][:, qi:qi + 1], Q["iw"][:, qi:qi + 1], k, nthreads=nthreads)
+            oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], tk, scale, nthreads=nthreads)
+        else:
+            oracle.hca_attend(Vq, Q["q"][:, qi:qi + 1], scale, nthreads=nthreads)
     t_q = (time.perf_counter() - t0) / len(sample)
     per_chunk = t_comp + t_q * n
     return dict(value=n / per_chunk, unit="queries/s", cores=nthreads, kind="oracle",
-                sample=f"compress_append of the {n}-token chunk ({t_comp:.2f}s) plus indexer_topk + "
-                       f"csa_attend for {len(sample)} of its queries ({t_q:.2f}s each), scaled to "
-                       f"the chunk")
+                sample=f"compress_append of the {n}-token chunk ({t_comp:.2f}s) plus "
+                       f"{'indexer_topk + csa_attend' if csa else 'hca_attend'} for {len(sample)} of its "
+                       f"queries ({t_q:.2f}s each), scaled to the chunk")
 
 
 def run_interleaved(args):

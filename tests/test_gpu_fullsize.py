@@ -182,6 +182,41 @@ def test_csa_prefill_chunk_fullsize():
         assert err <= ATTN_TOL
 
 
+def test_hca_prefill_chunk_fullsize():
+    """One HCA row with a 262144-token prior context (2048 blocks at m = 128):
+    a 4096-token chunk goes through compress_append (32 new blocks), then its
+    4096 queries attend densely to the blocks each one sees, plus the window.
+    Sampled queries (around block boundaries and at both ends) are checked
+    against the oracle."""
+    lca = _lca()
+    prior, n, m, H, W, R = 262144, 4096, 128, 64, 128, 8192
+    seed, tag = 1005, "hprefill"
+    say("hca_prefill_chunk fullsize prior", prior, "chunk", n, "seed", seed)
+    ref = SL.make_layer(seed, tag, 1, m, W, R, 0, (prior + n) // m + 64, [prior])
+    tok = SL.tokens(seed, "chunk", 1, n, 0)
+    Q = SL.queries(seed, tag, 1, n, H)
+    lay = lca.Layer.from_host(ref)
+    lca.compress_append(lay, _dev(tok["kv"]), _dev(tok["gate"]))
+    out = lca.hca_attend(lay, _dev(Q["q"]), float(SCALE))
+    torch.cuda.synchronize()
+    got = lay.download()
+    V = oracle.row_view(ref, 0)
+    oracle.compress_append(V, tok["kv"], tok["gate"])
+    assert int(got["seq_len"][0]) == prior + n
+    flips = 0
+    for b in (prior // m, (prior + n) // m - 1):
+        flips += _check_finalised(got, V, 0, b, m, False)
+    assert flips <= 2
+    for qi in (0, 126, 127, 2047, 4095):
+        say("hca_prefill query", qi)
+        Vq = dict(V)
+        Vq["seq_len"] = np.array([prior + qi + 1], np.int32)
+        wo = oracle.hca_attend(Vq, Q["q"][:, qi:qi + 1], SCALE)
+        err = attn_rel_err(out[:, qi:qi + 1].cpu().numpy(), wo)
+        print("query", qi, "attention max rel err", err, flush=True)
+        assert err <= ATTN_TOL
+
+
 def _row_copy(L, r):
     """an independent one-row copy of row r of a layer image"""
     V = dict(L)
