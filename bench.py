@@ -298,10 +298,10 @@ def run_prefill(args):
             "workload": args.workload, "batch": 1, "prior_tokens": prior, "chunk": n, "ratio": m,
             "heads": H, "indexer_heads": HI, "topk": k, "window": W, "ring": R,
             "kernel_us": kernels,
-            "score_visible_pairs": pairs,
-            "score_flops": flops,
-            "score_fp4_peak_frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4),
-            "score_fp8_rate_frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4),
+            **({"score_visible_pairs": pairs,
+                "score_flops": flops,
+                "score_fp4_peak_frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4),
+                "score_fp8_rate_frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4)} if csa else {}),
             "attend_flops": att_flops,
             "attend_tflops": round(att_tflops, 1),
             "attend_fp16_peak_frac": round(att_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
