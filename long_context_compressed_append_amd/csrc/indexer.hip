@@ -14,17 +14,19 @@
 //   a zero score is +0.  The selection is bitwise reproducible.
 //
 // Matrix-core mapping (v_mfma_scale_f32_32x32x64_f8f6f4, both operands e2m1):
-// the 32 A rows are (head, half) pairs -- a row carries one head's 32 codes of
-// one MX half and zeros in the other half -- and the 32 B columns are 32
-// consecutive blocks.  With the 32x32 output layout (lane l holds column l%32
-// and rows 8i + 4*(l/32) + j), rows are placed so that lane l < 32 receives
-// heads 0..7 and lane l >= 32 heads 8..15 of block l%32, each as its two
-// per-half partial dot products.  The hardware applies the E8M0 scales of the
-// query half (A) and of the key half (B).  A per-half partial is a sum of 32
-// products on one power-of-two grid, below 2^11 grid steps, so it is exact;
-// one fp32 add of the two halves then rounds the exact dot once.  Blocks whose
-// scaled partials could leave the fp32 normal range take an unscaled MFMA and
-// apply the scales in fp32 (double for the far ranges), with the same result.
+// the 32 B columns are 32 consecutive blocks (lanes l and l + 32 give the two
+// MX halves of block l%32's key with their E8M0 scales); an A row carries one
+// head's whole 64-d MXFP4 query (lanes l and l + 32 give its two halves and
+// their scales).  With the 32x32 output layout (lane l holds column l%32 and
+// rows 8i + 4*(l/32) + j), heads are placed so that lane l < 32 receives heads
+// 0..7 (and 16..23) and lane l >= 32 heads 8..15 (and 24..31) of its block, in
+// order.  The hardware adds the two scaled half sums: each half's products
+// are multiples of 2^(E-2) below 1152 * 2^E (E = query + key exponent of the
+// half), so when both E lie in [-124, 116] and differ by at most 10 every
+// partial sum needs at most 24 bits and the result is the exact dot rounded
+// once.  Iterations where some block leaves these bounds take the per-half
+// layout instead (a row per (head, half), unscaled products, scales applied
+// in fp32, double for the far ranges), with the same result.
 // The head chain runs on the low lanes for heads 0..7, hops to the high lanes
 // for heads 8..15, and hops back for the next group of 16 heads.
 //
