@@ -4,9 +4,10 @@
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread -lm.
  * Floating point: the compressor follows its stated fp32 order (the FP8/FP4
  * codes it decides are taken in the same precision on both sides); the
- * indexer score is an exact dot product rounded once, then a fixed fp32 fma
- * chain (the top-k it decides is compared bit for bit); attention is computed
- * in double and rounded to fp32 once at the end.
+ * indexer score is an exact dot product per head rounded once, then one fp32
+ * fma chain over the heads in ascending order (the top-k it decides is
+ * compared bit for bit); attention is computed in double and rounded to
+ * fp32 once at the end.
  */
 #define _GNU_SOURCE
 #include "lca_oracle.h"
@@ -313,43 +314,38 @@ int orc_compress_append(orc_layer *L, const uint16_t *kv, const float *gate,
  * top-k blocks are kept.  Readings: one shared 64-d key per block; the query
  * has H heads of 64 dims, quantized to MXFP4 in the call; per-head fp32
  * weights; score = sum_h w_h * ReLU(q_h . k).  Order of evaluation (fixed so
- * that the selection can be compared bit for bit): each head's dot product is
- * the exact dot of the two dequantized MXFP4 vectors rounded once to fp32;
- * ReLU maps it to +0 unless positive; heads are folded in groups of eight
- * (heads 8g .. 8g+7): inside a group by fp32 fused multiply-adds in ascending
- * head order starting from +0, and the group partials are added in ascending
- * group order; a zero score is +0.
+ * that the selection can be compared bit for bit; the pages fix none): each
+ * head's dot product is the exact dot of the two dequantized MXFP4 vectors
+ * rounded once to fp32; ReLU maps it to +0 unless positive; the weighted sum
+ * is a single chain of fp32 fused multiply-adds over the heads in ascending
+ * order, starting from +0; a zero score is +0.
  * ====================================================================== */
 
 float orc_index_score(const uint8_t *qcode, const uint8_t *qe, const float *w,
                       int H, const uint8_t *kcode, const uint8_t *ke,
                       int *inexact) {
   float score = 0.0f;
-  for (int g = 0; g * 8 < H; g++) {
-    float part = 0.0f;
-    for (int h = 8 * g; h < H && h < 8 * g + 8; h++) {
-      double halfsum[2];
-      for (int j = 0; j < 2; j++) {
-        double d = 0.0;                    /* exact: products on a 1/4 grid, |sum| < 2^11 */
-        for (int i = 0; i < ORC_MX_BLOCK; i++) {
-          int el = j * ORC_MX_BLOCK + i;
-          uint8_t qb = qcode[h * 32 + el / 2], kb = kcode[el / 2];
-          uint8_t qn = (el & 1) ? (qb >> 4) : (qb & 15);
-          uint8_t kn = (el & 1) ? (kb >> 4) : (kb & 15);
-          d += orc_e2m1_value(qn) * orc_e2m1_value(kn);
-        }
-        halfsum[j] = ldexp(d, ((int)qe[h * 2 + j] - 127) + ((int)ke[j] - 127));
+  for (int h = 0; h < H; h++) {
+    double halfsum[2];
+    for (int j = 0; j < 2; j++) {
+      double d = 0.0;                      /* exact: products on a 1/4 grid, |sum| < 2^11 */
+      for (int i = 0; i < ORC_MX_BLOCK; i++) {
+        int el = j * ORC_MX_BLOCK + i;
+        uint8_t qb = qcode[h * 32 + el / 2], kb = kcode[el / 2];
+        uint8_t qn = (el & 1) ? (qb >> 4) : (qb & 15);
+        uint8_t kn = (el & 1) ? (kb >> 4) : (kb & 15);
+        d += orc_e2m1_value(qn) * orc_e2m1_value(kn);
       }
-      double s = halfsum[0] + halfsum[1];
-      /* exactness of the double sum (TwoSum error term must vanish) */
-      double bv = s - halfsum[0], av = s - bv;
-      double err = (halfsum[0] - av) + (halfsum[1] - bv);
-      if (err != 0.0 && inexact) *inexact = 1;
-      float dot = (float)s;                /* the single rounding to fp32 */
-      float r = dot > 0.0f ? dot : 0.0f;
-      part = fmaf(w[h], r, part);
+      halfsum[j] = ldexp(d, ((int)qe[h * 2 + j] - 127) + ((int)ke[j] - 127));
     }
-    score = (g == 0) ? part : score + part;
+    double s = halfsum[0] + halfsum[1];
+    /* exactness of the double sum (TwoSum error term must vanish) */
+    double bv = s - halfsum[0], av = s - bv;
+    double err = (halfsum[0] - av) + (halfsum[1] - bv);
+    if (err != 0.0 && inexact) *inexact = 1;
+    float dot = (float)s;                  /* the single rounding to fp32 */
+    float r = dot > 0.0f ? dot : 0.0f;     /* ReLU */
+    score = fmaf(w[h], r, score);          /* one chain, ascending heads */
   }
   if (score == 0.0f) score = 0.0f;         /* canonical +0 */
   return score;

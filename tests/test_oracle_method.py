@@ -142,25 +142,31 @@ def test_chunked_equals_token_by_token(m, has_idx):
 
 # ------------------------------------------------------------------ indexer
 
+def _exact_dot(qcode, qe, kcode, ke, h):
+    """The exact rational dot product of head h's dequantized MXFP4 query with
+    the dequantized MXFP4 key (e2m1 values from the format table times the
+    E8M0 powers of two)."""
+    dot = Fraction(0)
+    for el in range(64):
+        j = el // 32
+        qb, kb = int(qcode[h, el // 2]), int(kcode[el // 2])
+        qn = (qb >> 4) if el & 1 else (qb & 15)
+        kn = (kb >> 4) if el & 1 else (kb & 15)
+        sc = Fraction(2) ** (int(qe[h, j]) - 127 + int(ke[j]) - 127)
+        dot += E2M1[qn] * E2M1[kn] * sc
+    return dot
+
+
 def _brute_score(qcode, qe, w, kcode, ke):
-    """Exact-rational brute force of the defined evaluation order."""
+    """Exact-rational brute force of the defined evaluation order: per head
+    the exact dot rounded once to binary32, ReLU, then one chain of fused
+    multiply-adds (each rounded once) over the heads in ascending order from
+    +0."""
     score = 0.0
-    H = len(w)
-    for g in range(0, H, 8):
-        part = 0.0
-        for h in range(g, min(H, g + 8)):
-            dot = Fraction(0)
-            for el in range(64):
-                j = el // 32
-                qb, kb = int(qcode[h, el // 2]), int(kcode[el // 2])
-                qn = (qb >> 4) if el & 1 else (qb & 15)
-                kn = (kb >> 4) if el & 1 else (kb & 15)
-                sc = Fraction(2) ** (int(qe[h, j]) - 127 + int(ke[j]) - 127)
-                dot += E2M1[qn] * E2M1[kn] * sc
-            d = round_f32(dot)
-            r = d if d > 0 else 0.0
-            part = round_f32(Fraction(float(np.float32(w[h]))) * Fraction(r) + Fraction(part))
-        score = part if g == 0 else round_f32(Fraction(score) + Fraction(part))
+    for h in range(len(w)):
+        d = round_f32(_exact_dot(qcode, qe, kcode, ke, h))
+        r = d if d > 0 else 0.0
+        score = round_f32(Fraction(float(np.float32(w[h]))) * Fraction(r) + Fraction(score))
     return score + 0.0
 
 
@@ -180,22 +186,78 @@ def test_index_score_closed_form():
     assert not inexact and s == GOLD["index_score"]["score"]
 
 
+def _random_query_key(rng, H):
+    qf = rng.standard_normal((H, 64)).astype(np.float32) * 10.0 ** rng.uniform(-2, 2)
+    qcode = np.zeros((H, 32), np.uint8)
+    qe = np.zeros((H, 2), np.uint8)
+    for h in range(H):
+        qcode[h], qe[h] = oracle.make_idx(qf[h])
+    kcode = rng.integers(0, 256, 32).astype(np.uint8)
+    ke = (127 + rng.integers(-6, 6, 2)).astype(np.uint8)
+    return qcode, qe, kcode, ke
+
+
 def test_index_score_matches_exact_rational_brute_force():
     rng = np.random.default_rng(17)
-    for trial in range(40):
-        H = int(rng.integers(1, 6)) if trial < 20 else int(rng.integers(7, 21))
-        qf = rng.standard_normal((H, 64)).astype(np.float32) * 10.0 ** rng.uniform(-2, 2)
-        qcode = np.zeros((H, 32), np.uint8)
-        qe = np.zeros((H, 2), np.uint8)
-        for h in range(H):
-            qcode[h], qe[h] = oracle.make_idx(qf[h])
+    for trial in range(48):
+        H = int(rng.integers(1, 6)) if trial < 16 else int(rng.integers(7, 33))
+        qcode, qe, kcode, ke = _random_query_key(rng, H)
         w = rng.standard_normal(H).astype(np.float32)      # any sign
-        kcode = rng.integers(0, 256, 32).astype(np.uint8)
-        ke = (127 + rng.integers(-6, 6, 2)).astype(np.uint8)
         s, inexact = oracle.index_score(qcode, qe, w, kcode, ke)
         assert not inexact
         want = _brute_score(qcode, qe, w, kcode, ke)
         assert np.float32(s).view(np.uint32) == np.float32(want).view(np.uint32), (trial, s, want)
+
+
+def test_index_score_close_to_exact_weighted_sum():
+    """Order-free pin: the score is the exact sum over heads of
+    w_h * ReLU(dot_h) (dot_h the exactly rounded dot) up to the rounding of
+    H fused multiply-adds, |err| <= H u / (1 - H u) * sum_h |w_h r_h|, u = 2^-24.
+    A dropped head, a wrong weight index or a sign error breaks it."""
+    rng = np.random.default_rng(18)
+    u = 2.0 ** -24
+    for trial in range(60):
+        H = int(rng.integers(1, 33))
+        qcode, qe, kcode, ke = _random_query_key(rng, H)
+        w = rng.standard_normal(H).astype(np.float32)
+        if trial % 3 == 0:
+            w = np.abs(w)
+        elif trial % 3 == 1:
+            w = -np.abs(w)
+        s, _ = oracle.index_score(qcode, qe, w, kcode, ke)
+        terms = []
+        for h in range(H):
+            d = Fraction(round_f32(_exact_dot(qcode, qe, kcode, ke, h)))
+            terms.append(Fraction(float(w[h])) * max(d, Fraction(0)))
+        exact = sum(terms, Fraction(0))
+        bound = Fraction(H) * Fraction(u) / (1 - H * Fraction(u)) * sum(abs(t) for t in terms)
+        assert abs(Fraction(float(s)) - exact) <= bound, (trial, s, float(exact))
+        if all(t >= 0 for t in terms) or all(t <= 0 for t in terms):
+            # one-signed terms: the relative error is at most the same factor
+            assert abs(Fraction(float(s)) - exact) <= bound
+
+
+def test_index_score_negative_weights_and_zero():
+    """All-negative weights give negative (or +0) scores; a score that is
+    zero is +0 whatever the weights' signs."""
+    rng = np.random.default_rng(19)
+    for trial in range(20):
+        H = int(rng.integers(1, 17))
+        qcode, qe, kcode, ke = _random_query_key(rng, H)
+        w = -np.abs(rng.standard_normal(H).astype(np.float32))
+        s, _ = oracle.index_score(qcode, qe, w, kcode, ke)
+        assert s <= 0.0
+        if s == 0.0:
+            assert np.float32(s).view(np.uint32) == 0
+    # every dot negative -> every ReLU +0 -> score +0 even with w < 0
+    qcode = np.zeros((2, 32), np.uint8)
+    qe = np.full((2, 2), 127, np.uint8)
+    qcode[:, 0] = 0x02                       # element 0 = +1.0
+    kcode = np.zeros(32, np.uint8)
+    kcode[0] = 0x0A                          # element 0 = -1.0
+    s, _ = oracle.index_score(qcode, qe, np.array([-1.0, -2.0], np.float32), kcode,
+                              np.array([127, 127], np.uint8))
+    assert np.float32(s).view(np.uint32) == 0
 
 
 def test_topk_brute_force_ties_and_padding():
