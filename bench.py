@@ -602,7 +602,7 @@ def main():
         for lay in layers:       # size the workspaces for the planned lengths before capture
             lay.len_max = final_len
             if csa:
-                lay.workspace(lca.indexer_workspace_bytes(lay, 1, HI, k), "indexer")
+                lay.indexer_workspace(1, lca.indexer_workspace_bytes(lay, 1, HI, k))
             lay.workspace(lca.attend_workspace_bytes(lay, 1, H, k), "attend")
         for lay, (a, b) in zip(layers, lens_before):
             lay.len_min, lay.len_max = a, b

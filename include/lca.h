@@ -155,18 +155,21 @@ int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
  * p = seq_len - n_q + i), over the visible blocks b < floor((p+1)/m):
  *   q_h = MXFP4(iq[h]) (quantized in the call, same rule as the keys);
  *   dot_h = exact dot of the dequantized q_h and key b, rounded once to fp32;
- *   for each group g of eight heads (8g .. 8g+7): p_g = +0, then
- *     p_g = fmaf(iw[h], max(dot_h, 0), p_g) for h ascending;
- *   score = ((p_0 + p_1) + p_2) + ... (ascending groups), a zero score is +0;
+ *   score = +0, then score = fmaf(iw[h], max(dot_h, 0), score) for
+ *           h = 0 .. H_I-1 (one chain, ascending heads); a zero score is +0;
  *   topk = the min(k, visible) largest (score desc, block asc), written in
  *          ascending block order, padded with -1.
  *   iq    float [B][n_q][H_I][64]     iw    float [B][n_q][H_I]
  *   topk  int32 [B][n_q][k]           (output)
  * Needs a CSA layer, 1 <= H_I <= 32, 1 <= k <= 2048, n_q <= len_min and
- * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes, be
- * zero-filled before its first use, and be used by nothing but
- * lca_indexer_topk afterwards: its leading part holds per-query histograms
- * that every call leaves zero-filled again.
+ * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes and
+ * be used by nothing but lca_indexer_topk.  Its first B * n_q * 16 KiB hold
+ * one histogram per query; they must be zero when a call starts, and every
+ * call leaves them zero again.  A call writes its scores and lists after its
+ * own histograms, so a workspace that served a call with fewer queries
+ * (B * n_q) holds non-zero bytes where a call with more queries keeps its
+ * histograms: zero-fill it again before such a call (or keep one workspace
+ * per query count).  A zero-filled workspace is ready for any call.
  * The kernels are chosen from the shapes; for tests and tuning the choice
  * can be forced through environment variables read at every call (keep them
  * unchanged between the workspace query and the call, as the workspace size

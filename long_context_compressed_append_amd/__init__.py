@@ -199,8 +199,11 @@ class Layer:
 
     def workspace(self, nbytes, kind="attend"):
         """A cached, zero-initialised device workspace of at least nbytes, one
-        per kind ("indexer" keeps its histograms zeroed between calls and is
-        used by nothing else)."""
+        per kind.  The indexer's kind is ("indexer", B * n_q): its workspace
+        starts with one zeroed histogram per query, which every call leaves
+        zeroed, followed by data of that call; a call with more queries would
+        find that data where its own histograms lie, so each query count
+        keeps a workspace of its own."""
         if nbytes == 0:
             return None
         ws = self._ws.get(kind)
@@ -208,6 +211,11 @@ class Layer:
             ws = torch.zeros(int(nbytes), dtype=torch.uint8, device=self.seq_len.device)
             self._ws[kind] = ws
         return ws
+
+    def indexer_workspace(self, n_q, nbytes=0):
+        """The indexer workspace for calls with n_q queries per row."""
+        return self.workspace(nbytes, ("indexer", self.batch * int(n_q))) if nbytes else \
+            self._ws.get(("indexer", self.batch * int(n_q)))
 
 
 def abi_version():
@@ -260,7 +268,7 @@ def indexer_topk(layer: Layer, iq, iw, k, out=None):
     _dev(out, torch.int32, (B, n_q, k), "topk")
     s = layer.struct()
     nbytes = lib().lca_indexer_workspace(C.byref(s), n_q, H_I, k)
-    ws = layer.workspace(nbytes, "indexer")
+    ws = layer.indexer_workspace(n_q, nbytes)
     _check(lib().lca_indexer_topk(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _ptr(ws),
                                   nbytes, _stream()))
     return out

@@ -70,12 +70,12 @@ __device__ __forceinline__ void ring_copy(const CompressArgs& a, int row, int j,
 }
 
 // Longer blocks (m = 16 .. 128): the m logits (then weights) of this lane's
-// channel go to the wavefront's LDS slice lds[i * 64 + lane]; the loads of a
-// batch of 32 tokens are all issued before any is used.
-template <typename XF, typename ZF>
+// channel go to the wavefront's LDS slice lds[i * 64 + lane] (64 m floats);
+// the loads of a batch of NB tokens are all issued before any is used.  NB
+// divides m (16 for m = 16, 32 above), so no batch reaches past the block.
+template <int NB, typename XF, typename ZF>
 __device__ __forceinline__ float pool_long(int m, XF xval, ZF zval, const float* bias, int C, int c,
                                            float* lds, int lane) {
-  constexpr int NB = 32;
   float mx = -INFINITY;
 #pragma unroll 1
   for (int i0 = 0; i0 < m; i0 += NB) {
@@ -175,8 +175,9 @@ __device__ __forceinline__ float pool_channel(const CompressArgs& a, int row, in
       if (i < m) acc = __fadd_rn(acc, __fmul_rn(__fdiv_rn(ev[i], S), xv[i]));
     return acc;
   }
-  // m = 16 .. 128 (a power of two): a multiple of the 32-token batch above 16
-  return pool_long(m, xval, zval, bias, C, c, lds, lane);
+  // m = 16 .. 128 (a power of two): batches of 16 tokens for m = 16, else 32
+  if (m == 16) return pool_long<16>(m, xval, zval, bias, C, c, lds, lane);
+  return pool_long<32>(m, xval, zval, bias, C, c, lds, lane);
 }
 
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {

@@ -10,26 +10,32 @@
 // Score of block b for one query (H heads):
 //   dot_h  = exact dot product of MXFP4(q_h) and the block's MXFP4 key,
 //            rounded once to fp32;
-//   score  = +0, then score = fma(w_h, max(dot_h, 0), score) for h ascending;
-//   a zero score is +0.  The selection is bitwise reproducible.
+//   score  = +0, then score = fma(w_h, max(dot_h, 0), score) for h = 0 .. H-1
+//            (one chain in ascending head order); a zero score is +0.
+// The selection is bitwise reproducible.
 //
 // Matrix-core mapping (v_mfma_scale_f32_32x32x64_f8f6f4, both operands e2m1):
 // the 32 B columns are 32 consecutive blocks (lanes l and l + 32 give the two
 // MX halves of block l%32's key with their E8M0 scales); an A row carries one
 // head's whole 64-d MXFP4 query (lanes l and l + 32 give its two halves and
-// their scales).  With the 32x32 output layout (lane l holds column l%32 and
-// rows 8i + 4*(l/32) + j), heads are placed so that lane l < 32 receives heads
-// 0..7 (and 16..23) and lane l >= 32 heads 8..15 (and 24..31) of its block, in
-// order.  The hardware adds the two scaled half sums: each half's products
-// are multiples of 2^(E-2) below 1152 * 2^E (E = query + key exponent of the
+// their scales).  In the 32x32 output layout lane l holds column l%32 and
+// rows 8i + 4s + j (s = l/32, i, j < 4), i.e. 16 outputs e = 4i + j per lane.
+// The heads are placed so that a lane's outputs are all the heads of one
+// block, in order, and its chain needs no other lane:
+//   H <= 8 or H <= 16 (decode): outputs e = kHQ g + h of lane half s belong
+//     to key tile 2g + s of a group of 32/kHQ tiles.  The group's products
+//     accumulate into one output: the A operand of tile t is non-zero only
+//     in the rows that map to t, so every other row just adds 0.
+//   H <= 32: one tile per product, heads 16s + e; the chain runs over heads
+//     0..15 on the low lanes, hops to the high lanes for 16..31, and hops back.
+// The hardware adds the two scaled half sums: each half's products are
+// multiples of 2^(E-2) below 1152 * 2^E (E = query + key exponent of the
 // half), so when both E lie in [-124, 116] and differ by at most 10 every
 // partial sum needs at most 24 bits and the result is the exact dot rounded
 // once.  Iterations where some block leaves these bounds take the per-half
 // layout instead (a row per (head, half), unscaled products, scales applied
 // in fp32, double for the far ranges), with the same result.
-// The head chain runs on the low lanes for heads 0..7, hops to the high lanes
-// for heads 8..15, and hops back for the next group of 16 heads.
-//
+
 // While scoring, each workgroup histograms the top 12 bits of its order keys
 // and adds them to a per-query histogram; the selection reads that histogram
 // to find the bin that holds the k-th key, so it needs a single pass over the
@@ -101,30 +107,38 @@ __device__ __forceinline__ float exact_pair(float D0, int e0, float D1, int e1) 
   return (float)v;
 }
 
-// Score of the lane's block when some exponent sum is out of the range where
-// the scaled partials are exact fp32 normals: unscaled MFMA, scales in fp32
-// (double beyond that range).  Rare; kept out of line.
+// Score of the lane's block (column l % 32) when some exponent sum is out of
+// the range where the scaled partials are exact fp32 normals: unscaled MFMA,
+// scales in fp32 (double beyond that range).  Rows carry (head, half) pairs:
+// lane half s holds heads 16 hg + 8 s .. + 7 of head group hg.  The chain
+// extends on the half that holds the next heads and hops across after every
+// eight, so it visits the heads in ascending order; the score ends in the
+// low half.  Rare; kept out of line.
 __device__ __noinline__ float score_unscaled(v8i A0, v8i A1, v8i Bm, int hgroups, int H, int kh,
                                              const int (*q_exp)[2], const float* q_w, int ke0, int ke1) {
   const v16f zero16 = {};
-  float total = 0.0f;
+  float c = 0.0f;
   for (int hg = 0; hg < hgroups; hg++) {
     const v16f acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(hg ? A1 : A0, Bm, zero16, 4, 4, 0,
                                                                      127, 0, 127);
-    float part = 0.0f;
+    float rl[8], wl[8];
 #pragma unroll
     for (int hl = 0; hl < 8; hl++) {
       const int h = 16 * hg + 8 * kh + hl;
       const bool hv = h < H;
-      const float rl = fmaxf(exact_pair(acc[2 * hl], (hv ? q_exp[h][0] : 0) + ke0, acc[2 * hl + 1],
-                                        (hv ? q_exp[h][1] : 0) + ke1), 0.0f);
-      part = __builtin_fmaf(hv ? q_w[h] : 0.0f, rl, part);
+      rl[hl] = fmaxf(exact_pair(acc[2 * hl], (hv ? q_exp[h][0] : 0) + ke0, acc[2 * hl + 1],
+                                (hv ? q_exp[h][1] : 0) + ke1), 0.0f);
+      wl[hl] = hv ? q_w[h] : 0.0f;
     }
-    const float upper = swap_halves(part);
-    total = (hg == 0) ? part : __fadd_rn(total, part);
-    total = __fadd_rn(total, upper);
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      // the half that holds heads 16 hg + 8 s .. extends the chain, then it hops
+#pragma unroll
+      for (int hl = 0; hl < 8; hl++) c = __builtin_fmaf(wl[hl], rl[hl], c);
+      c = swap_halves(c);
+    }
   }
-  return total;
+  return c;
 }
 
 // inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
@@ -224,9 +238,13 @@ __device__ void select_row(const SelectArgs& a, int srow, uint32_t* hist, uint32
 // for the row, reading keys and histogram with agent-scope loads.  No
 // device-scope fence is needed: nothing it reads sits only in another
 // XCD's L2.
-template <bool kFused>
+// kHQ: heads per chain slot (8, 16 or 32 >= H); kTPA key tiles share one
+// matrix-core output (4, 2 or 1).
+template <bool kFused, int kHQ>
 __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(ScoreArgs a, SelectArgs sel) {
   constexpr int kT = kFused ? 512 : 256;
+  constexpr int kTPA = kHQ == 32 ? 1 : 32 / kHQ;
+  static_assert(kDepth % kTPA == 0, "a set of loaded iterations holds whole tile groups");
   const int srow = blockIdx.y;
   const int brow = srow / a.n_q, qi = srow % a.n_q;
   // This workgroup's chunks of 1024 blocks are [c0, c0 + cpw).  The key loads
@@ -332,32 +350,35 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
     }
   }
   // The same query with both MX halves of a head in one A row, for products
-  // that add the two halves in hardware: row 16 hg + 8 i + 4 s + j carries
-  // head 16 hg + 8 s + 4 i + j, so that output 8 hg + hl of a lane in set s
-  // is head 16 hg + 8 s + hl (its octet in order).
-  v8i Af = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-  int saf = 127;
+  // that add the two halves in hardware.  Row r = 8 i + 4 s + j is output
+  // e = 4 i + j of lane half s.  kHQ <= 16: output e is head e % kHQ of tile
+  // 2 (e / kHQ) + s of a group of kTPA tiles, and Af[t] holds only the rows
+  // of tile t (zero elsewhere); kHQ = 32: one tile, row r carries head 16 s + e.
+  v8i Af[kTPA];
+  int saf[kTPA];
   {
-    const int h = 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
-    if (h < a.H) {
-      const int* src = reinterpret_cast<const int*>(&q_code[h][16 * kh]);
-      Af[0] = src[0];
-      Af[1] = src[1];
-      Af[2] = src[2];
-      Af[3] = src[3];
-      saf = q_exp[h][kh] + 127;
+    const int s_r = (r >> 2) & 1, e_r = 4 * (r >> 3) + (r & 3);
+    const int h = kHQ == 32 ? 16 * s_r + e_r : e_r % kHQ;
+    const int t_r = kHQ == 32 ? 0 : 2 * (e_r / kHQ) + s_r;
+    const bool hv = h < a.H;
+    const int* src = reinterpret_cast<const int*>(&q_code[hv ? h : 0][16 * kh]);
+    const int c0 = hv ? src[0] : 0, c1 = hv ? src[1] : 0, c2 = hv ? src[2] : 0, c3 = hv ? src[3] : 0;
+    const int sc = hv ? q_exp[h][kh] + 127 : 127;
+#pragma unroll
+    for (int t = 0; t < kTPA; t++) {
+      const bool mine = t_r == t;
+      Af[t] = (v8i){mine ? c0 : 0, mine ? c1 : 0, mine ? c2 : 0, mine ? c3 : 0, 0, 0, 0, 0};
+      saf[t] = mine ? sc : 127;
     }
   }
-  // Per-lane epilogue constants for the 8 heads of this lane's set (octet
-  // 2*hg + kh); heads past H get weight 0, which leaves the chain unchanged.
-  float wv[2][8];
+  // weights of the lane's chain, head order; past H a weight is 0, which
+  // leaves the chain unchanged
+  float wv[kHQ == 32 ? 16 : kHQ];
 #pragma unroll
-  for (int hg = 0; hg < 2; hg++)
-#pragma unroll
-    for (int hl = 0; hl < 8; hl++) {
-      const int h = 16 * hg + 8 * kh + hl;
-      wv[hg][hl] = h < a.H ? q_w[h] : 0.0f;
-    }
+  for (int e = 0; e < (kHQ == 32 ? 16 : kHQ); e++) {
+    const int h = kHQ == 32 ? 16 * kh + e : e;
+    wv[e] = h < a.H ? q_w[h] : 0.0f;
+  }
   {
     // extremes of the query's 2H block exponents: lane l looks at entry l
     const int e = lane < 2 * a.H ? q_exp[lane >> 1][lane & 1] : 0;
@@ -387,6 +408,13 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
 
   // kDepth iterations at once: their matrix-core products and head chains are
   // independent, so they interleave; one range check covers the block.
+  // Lane key kk of the set belongs to iteration it_of(kk) (and column r).
+  constexpr int kKeys = kHQ == 32 ? kDepth : kDepth / 2;   // keys per lane per set
+  auto it_of = [&](int kk) -> int {
+    if (kHQ == 32) return kk;
+    const int grp = kk / (kTPA / 2), g = kk % (kTPA / 2);
+    return grp * kTPA + 2 * g + kh;
+  };
   auto compute = [&](int i0, const int4 (&kr)[kDepth], const uint32_t (&er_in)[kDepth]) {
     int b0[kDepth], b1[kDepth], sb[kDepth];
     bool ok = true;
@@ -400,47 +428,77 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
       ok = ok & ((uint32_t)(b0[u] - byte_lo) <= byte_span) & ((uint32_t)(b1[u] - byte_lo) <= byte_span) &
            ((uint32_t)(b0[u] - b1[u] - diff_lo) <= diff_span);
     }
-    float total[kDepth];
+    float total[kKeys];
     if (__all(ok)) {
-      v16f acc[kDepth];
+      if constexpr (kHQ == 32) {
+        v16f acc[kDepth];
 #pragma unroll
-      for (int u = 0; u < kDepth; u++) {
-        const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
-        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Af, Bm, zero16, 4, 4, 0, saf, 0, sb[u]);
-      }
+        for (int u = 0; u < kDepth; u++) {
+          const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
+          acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Af[0], Bm, zero16, 4, 4, 0, saf[0], 0, sb[u]);
+        }
+        // heads 0..15 on the low lanes, then 16..31 on the high lanes from
+        // there; the score hops back to the low lanes
+        float c[kDepth];
 #pragma unroll
-      for (int hg = 0; hg < 2; hg++) {
-        if (hg < hgroups) {
-          // both lane sets fold their octet at once; the low set adds the octets
-          float part[kDepth], upper[kDepth];
+        for (int u = 0; u < kDepth; u++) {
+          c[u] = 0.0f;
 #pragma unroll
-          for (int u = 0; u < kDepth; u++) {
-            part[u] = 0.0f;
+          for (int e = 0; e < 16; e++) c[u] = __builtin_fmaf(wv[e], relu_bits(acc[u][e]), c[u]);
+        }
 #pragma unroll
-            for (int hl = 0; hl < 8; hl++)
-              part[u] = __builtin_fmaf(wv[hg][hl], relu_bits(acc[u][8 * hg + hl]), part[u]);
+        for (int u = 0; u < kDepth; u++) c[u] = swap_halves(c[u]);
+#pragma unroll
+        for (int u = 0; u < kDepth; u++) {
+#pragma unroll
+          for (int e = 0; e < 16; e++) c[u] = __builtin_fmaf(wv[e], relu_bits(acc[u][e]), c[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kDepth; u++) total[u] = swap_halves(c[u]);
+      } else {
+#pragma unroll
+        for (int grp = 0; grp < kDepth / kTPA; grp++) {
+          v16f acc = zero16;
+#pragma unroll
+          for (int t = 0; t < kTPA; t++) {
+            const int u = grp * kTPA + t;
+            const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Af[t], Bm, acc, 4, 4, 0, saf[t], 0, sb[u]);
           }
 #pragma unroll
-          for (int u = 0; u < kDepth; u++) upper[u] = swap_halves(part[u]);
+          for (int g = 0; g < kTPA / 2; g++) {
+            float c = 0.0f;
 #pragma unroll
-          for (int u = 0; u < kDepth; u++) {
-            total[u] = (hg == 0) ? part[u] : __fadd_rn(total[u], part[u]);
-            total[u] = __fadd_rn(total[u], upper[u]);
+            for (int e = 0; e < kHQ; e++) c = __builtin_fmaf(wv[e], relu_bits(acc[kHQ * g + e]), c);
+            total[grp * (kTPA / 2) + g] = c;
           }
         }
       }
     } else {
+      float ts[kDepth];
 #pragma unroll
       for (int u = 0; u < kDepth; u++) {
         const v8i Bm = (v8i){kr[u].x, kr[u].y, kr[u].z, kr[u].w, 0, 0, 0, 0};
-        total[u] = score_unscaled(A[0], A[1], Bm, hgroups, a.H, kh, q_exp, q_w, b0[u] - 127, b1[u] - 127);
+        ts[u] = score_unscaled(A[0], A[1], Bm, hgroups, a.H, kh, q_exp, q_w, b0[u] - 127, b1[u] - 127);
+      }
+      // score of tile u in the low lanes; lane key kk takes iteration it_of(kk)
+#pragma unroll
+      for (int kk = 0; kk < kKeys; kk++) {
+        if (kHQ == 32) {
+          total[kk] = ts[kk];
+        } else {
+          const int grp = kk / (kTPA / 2), g = kk % (kTPA / 2);
+          const float hi = swap_halves(ts[grp * kTPA + 2 * g + 1]);
+          total[kk] = kh ? hi : ts[grp * kTPA + 2 * g];
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kDepth; u++) {
+    for (int kk = 0; kk < kKeys; kk++) {
+      const int u = it_of(kk);
       const int blk = blk_of(i0 + u);
-      if ((kh == 0) & (i0 + u < n_it) & (blk < nv)) {
-        const uint32_t key = ord_key(__fadd_rn(total[u], 0.0f));   // -0 -> +0
+      if ((kHQ != 32 || kh == 0) & (i0 + u < n_it) & (blk < nv)) {
+        const uint32_t key = ord_key(__fadd_rn(total[kk], 0.0f));   // -0 -> +0
         if (kFused)
           __hip_atomic_store(&out[blk], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -491,12 +549,12 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
 //
 // One 32x32x64 FP4 product per query pair (H <= 16) or per query (H <= 32)
 // and 32 blocks: row r = 8i + 4s + j of the A operand is
-//   H <= 16: query 2m + i/2 of the wavefront's set, head 8s + 4(i%2) + j
-//   H <= 32: query m, head 16(i/2) + 8s + 4(i%2) + j
+//   H <= 16: query 2m + s of the wavefront's set, head 4i + j
+//   H <= 32: query m, head 16s + 4i + j
 // and carries the head's whole 64-d MXFP4 vector (lanes l and l + 32 give its
 // two MX halves with their own E8M0 scales), so lane l's 16 outputs are the
-// dot products of its block (column l % 32) with the heads of head group s =
-// l / 32 of its queries.  With both halves in one product the hardware adds
+// dot products of its block (column l % 32) with heads 0..15 (16s .. 16s+15)
+// of its query, in order.  With both halves in one product the hardware adds
 // two scaled partial sums; the result is still the exactly rounded dot when
 // every partial sum is an fp32 number: each half's products are multiples of
 // 2^(E-2) below 1152 * 2^E (E = query exponent + key exponent of the half),
@@ -504,9 +562,9 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
 // multiple of 2^(min E - 2) below 2^(max E + 12) and needs at most 24 bits.
 // Iterations where some (row, column) leaves these bounds take the per-half
 // path (two unscaled products, scales applied exactly per output).
-// Each lane runs the head chains of its group for its queries; one permlane
-// swap brings the other group's partial, and lane l < 32 (l >= 32) finishes
-// the first (second) query of the pair.
+// Each lane runs the head chain of its query in ascending head order; for
+// H > 16 the chain runs over heads 0..15 on the low lanes, continues over
+// 16..31 on the high lanes and the score hops back (lane l < 32 stores it).
 //
 // Candidate lists (kCand): instead of one key per block, each lane keeps
 // only the keys that can still be among its query's k largest.  From time to
@@ -539,15 +597,13 @@ __device__ __noinline__ v16f tile_dots_unscaled(v8i Am, v8i Bm, int kh, int m, i
   const v16f D0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A0, Bm, zero16, 4, 4, 0, 127, 0, 127);
   const v16f D1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A1, Bm, zero16, 4, 4, 0, 127, 0, 127);
   const int s = (threadIdx.x & 63) >> 5;
+  const int q = kQw == 8 ? set * kQw + 2 * m + s : set * kQw + m;
   v16f d;
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int q = kQw == 8 ? set * kQw + 2 * m + (i >> 1) : set * kQw + m;
-      const int h = kQw == 8 ? 8 * s + 4 * (i & 1) + j : 16 * (i >> 1) + 8 * s + 4 * (i & 1) + j;
-      d[4 * i + j] = exact_pair(D0[4 * i + j], q_exp[q][h][0] + ke0, D1[4 * i + j], q_exp[q][h][1] + ke1);
-    }
+  for (int e = 0; e < 16; e++) {
+    const int h = kQw == 8 ? e : 16 * s + e;
+    d[e] = exact_pair(D0[e], q_exp[q][h][0] + ke0, D1[e], q_exp[q][h][1] + ke1);
+  }
   return d;
 }
 
@@ -614,20 +670,15 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   float wt[kNm][16];
 #pragma unroll
   for (int m = 0; m < kNm; m++) {
-    const int q = kQw == 8 ? set * kQw + 2 * m + (ri >> 1) : set * kQw + m;
-    const int h = kQw == 8 ? 8 * rs + 4 * (ri & 1) + rj : 16 * (ri >> 1) + 8 * rs + 4 * (ri & 1) + rj;
+    const int q = kQw == 8 ? set * kQw + 2 * m + rs : set * kQw + m;
+    const int h = kQw == 8 ? 4 * ri + rj : 16 * rs + 4 * ri + rj;
     const bool ok = h < a.H;
     const int* src = reinterpret_cast<const int*>(&q_code[q][ok ? h : 0][16 * kh]);
     A[m] = (v8i){ok ? src[0] : 0, ok ? src[1] : 0, ok ? src[2] : 0, ok ? src[3] : 0, 0, 0, 0, 0};
     sa[m] = ok ? q_exp[q][h][kh] + 127 : 127;
+    const int qo = kQw == 8 ? set * kQw + 2 * m + kh : set * kQw + m;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int qo = kQw == 8 ? set * kQw + 2 * m + (i >> 1) : set * kQw + m;
-        const int ho = kQw == 8 ? 8 * kh + 4 * (i & 1) + j : 16 * (i >> 1) + 8 * kh + 4 * (i & 1) + j;
-        wt[m][4 * i + j] = q_w[qo][ho];       // 0 past H (the chain is unchanged)
-      }
+    for (int e = 0; e < 16; e++) wt[m][e] = q_w[qo][kQw == 8 ? e : 16 * kh + e];   // 0 past H
   }
   // exponent bounds of this set's query halves: the exact fast path needs
   // |(ea0 + eb0) - (ea1 + eb1)| <= 10 and every ea + eb in [-124, 116]
@@ -730,29 +781,21 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
     }
     return r;
   };
-  // head chains (groups of 8 heads), the two groups' partials meet, keys
+  // head chains in ascending head order, keys
   auto finish = [&](int t, const Dots& D) {
     const int blk = blk_of(t);
 #pragma unroll
     for (int m = 0; m < kNm; m++) {
-      float p[2] = {0.0f, 0.0f};          // i = 0, 1 -> p[0]; i = 2, 3 -> p[1]
+      float score = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int e = 0; e < 16; e++) score = __builtin_fmaf(wt[m][e], relu_bits(D.d[m][e]), score);
+      if (kQw == 4) {
+        // heads 16..31 continue the chain of 0..15 on the high lanes; the
+        // score hops back to the low lanes
+        float c = swap_halves(score);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          p[i >> 1] = __builtin_fmaf(wt[m][4 * i + j], relu_bits(D.d[m][4 * i + j]), p[i >> 1]);
-      float score;
-      if (kQw == 8) {
-        // p[0]: group s of query 2m, p[1]: group s of query 2m + 1.  After the
-        // swap lane l < 32 holds (group 0, group 1) of query 2m, lane l >= 32
-        // those of query 2m + 1.
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false,
-                                                         false);
-        score = __fadd_rn(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      } else {
-        // p[0]: group s, p[1]: group 2 + s of query m: ((g0 + g1) + g2) + g3
-        const float o0 = swap_halves(p[0]), o1 = swap_halves(p[1]);
-        score = __fadd_rn(__fadd_rn(__fadd_rn(kh ? o0 : p[0], kh ? p[0] : o0), kh ? o1 : p[1]), kh ? p[1] : o1);
+        for (int e = 0; e < 16; e++) c = __builtin_fmaf(wt[m][e], relu_bits(D.d[m][e]), c);
+        score = swap_halves(c);
       }
       // no -0: every chain starts at +0 and each fma result is exact-rounded
       // from a sum that is -0 only when both terms are
@@ -1797,10 +1840,23 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
       hipLaunchKernelGGL((indexer_score_tile_kernel<4, true>), tg, tb, 0, stream, s);
     else if (pl.tile == 4)
       hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
-    else if (pl.fused)   // the selection runs in the same launch
-      hipLaunchKernelGGL(indexer_score_kernel<true>, dim3((pl.chunks + 1) / 2, rows), dim3(512), 0, stream, s, sa);
-    else
-      hipLaunchKernelGGL(indexer_score_kernel<false>, dim3(pl.chunks, rows), dim3(256), 0, stream, s, sa);
+    else if (pl.fused) {   // the selection runs in the same launch
+      const dim3 g((pl.chunks + 1) / 2, rows), b(512);
+      if (H_I <= 8)
+        hipLaunchKernelGGL((indexer_score_kernel<true, 8>), g, b, 0, stream, s, sa);
+      else if (H_I <= 16)
+        hipLaunchKernelGGL((indexer_score_kernel<true, 16>), g, b, 0, stream, s, sa);
+      else
+        hipLaunchKernelGGL((indexer_score_kernel<true, 32>), g, b, 0, stream, s, sa);
+    } else {
+      const dim3 g(pl.chunks, rows), b(256);
+      if (H_I <= 8)
+        hipLaunchKernelGGL((indexer_score_kernel<false, 8>), g, b, 0, stream, s, sa);
+      else if (H_I <= 16)
+        hipLaunchKernelGGL((indexer_score_kernel<false, 16>), g, b, 0, stream, s, sa);
+      else
+        hipLaunchKernelGGL((indexer_score_kernel<false, 32>), g, b, 0, stream, s, sa);
+    }
     int rc = t.done();
     if (rc || pl.fused) return rc;
   }

@@ -21,7 +21,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (bf16_bits, bf16_to_f32, abs_normal_f32, bf16_normal, distinct_choice, e2m1_code_image,
-               e4m3_code_image, e8m0_image, fp8_scale_image, normal_f32)
+               e4m3_code_image, e8m0_image, fp8_scale_image, key, normal_f32, randbytes)
 
 KV, NOPE, ROPE, IDX = 512, 448, 64, 64
 
@@ -100,6 +100,18 @@ def queries(seed, tag, batch, n_q, H, H_I=0, step=0):
         q["iq"] = normal_f32(seed, "iq", (batch, n_q, H_I, IDX), tag, step)
         q["iw"] = abs_normal_f32(seed, "iw", (batch, n_q, H_I), tag, step)
     return q
+
+
+def signed_weights(seed, tag, iw, mode):
+    """Indexer weights of another sign pattern, from |N(0,1)| weights iw:
+    "abs" leaves them, "neg" negates them all, "mixed" flips a seeded random
+    half of them."""
+    if mode == "abs":
+        return iw
+    if mode == "neg":
+        return (-iw).astype(np.float32)
+    flip = (randbytes(key(seed, "iw_sign", tag), iw.size) & 1).reshape(iw.shape).astype(bool)
+    return np.where(flip, -iw, iw).astype(np.float32)
 
 
 def plant_needles(L, seed, tag, row, count, iq_row, iw_row, q_row):

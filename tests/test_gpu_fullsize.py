@@ -19,7 +19,8 @@ torch = pytest.importorskip("torch")
 import oracle
 from synth import layers as SL
 
-from gpu_helpers import ATTN_TOL, attn_rel_err, check_indexer_keys, compare_entries, indexer_row_keys
+from gpu_helpers import (ATTN_TOL, attn_rel_err, check_indexer_keys, check_topk, compare_entries,
+                         indexer_row_keys)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 SCALE = np.float32(1.0 / np.sqrt(512.0))
@@ -52,7 +53,7 @@ def _ring_tokens(V, f, p0, n):
 
 def _score_keys(lay, lca, n_q, H_I, k):
     """the indexer's workspace and its layout; the histograms must be zero"""
-    ws = lay._ws["indexer"]
+    ws = lay.indexer_workspace(n_q)
     layout = lca.indexer_layout(lay, n_q, H_I, k)
     assert not ws[:layout["keys"]].view(torch.int32).any().item()     # histograms left zeroed
     return ws, layout
@@ -101,7 +102,7 @@ def test_csa_decode_128k_fullsize():
         sc = oracle.indexer_scores(V, 0, 0, 1, Q["iq"][r:r + 1], Q["iw"][r:r + 1])
         check_indexer_keys(*indexer_row_keys(*keys, r, len(sc)), sc, k)
         want = oracle.indexer_topk(V, Q["iq"][r:r + 1], Q["iw"][r:r + 1], k)
-        assert np.array_equal(got_topk[r], want[0])
+        check_topk(got_topk[r, 0], want[0, 0], sc, k)
         assert set(planted[r]) <= set(got_topk[r, 0].tolist())
         wo = oracle.csa_attend(V, Q["q"][r:r + 1], got_topk[r:r + 1], SCALE)
         err = attn_rel_err(got_out[r:r + 1], wo)
@@ -171,7 +172,7 @@ def test_csa_prefill_chunk_fullsize():
         say("csa_prefill query", qi)
         sc = oracle.indexer_scores(V, 0, qi, n, Q["iq"], Q["iw"])
         check_indexer_keys(*indexer_row_keys(*keys, qi, len(sc)), sc, k)
-        assert np.array_equal(got_topk[0, qi], oracle.topk_select(sc, k))
+        check_topk(got_topk[0, qi], oracle.topk_select(sc, k), sc, k)
         # one query alone: a view whose length ends at the query's position
         p = prior + qi
         Vq = dict(V)
@@ -297,7 +298,8 @@ def test_interleaved_1m_fullsize():
         for b in (ctx // 4 - 1, ctx // 4):
             flips += _check_finalised(dev_row, V, 0, b, 4, True)
         want = oracle.indexer_topk(V, qc["iq"][r:r + 1], qc["iw"][r:r + 1], k)
-        assert np.array_equal(got_topk[r], want[0])
+        check_topk(got_topk[r, 0], want[0, 0],
+                   oracle.indexer_scores(V, 0, 0, 1, qc["iq"][r:r + 1], qc["iw"][r:r + 1]), k)
         wo = oracle.csa_attend(V, qc["q"][r:r + 1], got_topk[r:r + 1], SCALE)
         err = attn_rel_err(got_c[r:r + 1], wo)
         print("csa row", r, "attention max rel err", err, flush=True)
