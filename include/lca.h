@@ -206,6 +206,26 @@ int lca_indexer_topk(const lca_layer *layer, const float *iq, const float *iw, i
                      hipStream_t stream);
 
 /*
+ * lca_indexer_topk_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops or harnesses that forbid
+ * hipMalloc): lca_indexer_topk with the same arguments except the workspace,
+ * which is a static device array inside the library of
+ * LCA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held until the process ends.
+ * Calls whose workspace (lca_indexer_workspace) exceeds that size fail with
+ * LCA_EWORKSPACE before anything is enqueued (decode steps fit: 128K context
+ * at B = 32 needs about 5 MB; a 4096-query prefill chunk does not).  The
+ * call clears the array's histogram part with a fill kernel first, so any
+ * sequence of shapes is valid.  All calls on one GPU share the array: calls
+ * that may overlap on one GPU (different streams without ordering) race.
+ * Results are those of lca_indexer_topk.  Errors: as lca_indexer_topk, plus
+ * EWORKSPACE for a call too large for the array and EHIP if the array's
+ * address cannot be found.
+ */
+#define LCA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lca_indexer_topk_noalloc(const lca_layer *layer, const float *iq, const float *iw, int32_t n_q,
+                             int32_t H_I, int32_t k, int32_t *topk, hipStream_t stream);
+
+/*
  * lca_csa_attend -- [ARCH] 2.1 (one attention over the sliding-window KV and
  * the top-k selected compressed KV); [AGENT] hybrid-attention section (recent
  * tokens at raw precision).

@@ -67,6 +67,7 @@ def lib():
         L.lca_indexer_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
         L.lca_indexer_layout.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
         L.lca_indexer_topk.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_size_t, P]
+        L.lca_indexer_topk_noalloc.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P]
         L.lca_attend_workspace.restype = C.c_size_t
         L.lca_attend_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
         L.lca_csa_attend.argtypes = [LP, P, C.c_int32, C.c_int32, P, C.c_int32, C.c_float, P, P,
@@ -271,6 +272,20 @@ def indexer_topk(layer: Layer, iq, iw, k, out=None):
     ws = layer.indexer_workspace(n_q, nbytes)
     _check(lib().lca_indexer_topk(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _ptr(ws),
                                   nbytes, _stream()))
+    return out
+
+
+def indexer_topk_noalloc(layer: Layer, iq, iw, k, out=None):
+    """indexer_topk with the library's static scratch array as workspace
+    (lca_indexer_topk_noalloc): no workspace is allocated for the call."""
+    B, n_q, H_I = iw.shape
+    _dev(iq, torch.float32, (B, n_q, H_I, IDX), "iq")
+    _dev(iw, torch.float32, (B, n_q, H_I), "iw")
+    if out is None:
+        out = torch.empty((B, n_q, k), dtype=torch.int32, device=iq.device)
+    _dev(out, torch.int32, (B, n_q, k), "topk")
+    s = layer.struct()
+    _check(lib().lca_indexer_topk_noalloc(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _stream()))
     return out
 
 

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblca.so")
-SOURCES = ["api.hip", "compress.hip", "indexer.hip", "attend.hip"]
+SOURCES = ["api.hip", "compress.hip", "indexer.hip", "attend.hip", "noalloc.hip"]
 # keep MFMA accumulators in arch VGPRs where the kernel rescales them with VALU
 EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

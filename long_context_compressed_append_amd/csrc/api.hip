@@ -102,6 +102,24 @@ static int check_ptr(const void* p, const char* name) {
   return LCA_OK;
 }
 
+int indexer_validate(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
+                     const int32_t* topk) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!L->has_indexer) return set_error(LCA_EINVAL, "lca_indexer_topk needs an indexer (CSA) layer");
+  if (n_q < 1) return set_error(LCA_EINVAL, "n_q must be >= 1 (got %d)", n_q);
+  if (H_I < 1 || H_I > 32) return set_error(LCA_EUNSUPPORTED, "H_I must be in 1..32 (got %d)", H_I);
+  if (k < 1 || k > 2048) return set_error(LCA_EUNSUPPORTED, "k must be in 1..2048 (got %d)", k);
+  if (n_q > L->len_min)
+    return set_error(LCA_EINVAL, "n_q (%d) exceeds the shortest row (%lld tokens)", n_q,
+                     (long long)L->len_min);
+  if (L->max_blocks > 524288) return set_error(LCA_EUNSUPPORTED, "max_blocks above 524288");
+  if ((int64_t)L->batch * n_q > 0x7FFFFFFF / 2) return set_error(LCA_EUNSUPPORTED, "too many queries");
+  if ((rc = check_ptr(iq, "iq")) || (rc = check_ptr(iw, "iw")) || (rc = check_ptr(topk, "topk")))
+    return rc;
+  return LCA_OK;
+}
+
 }  // namespace lca
 
 using namespace lca;
@@ -161,19 +179,8 @@ int lca_indexer_layout(const lca_layer* L, int32_t n_q, int32_t H_I, int32_t k, 
 
 int lca_indexer_topk(const lca_layer* L, const float* iq, const float* iw, int32_t n_q, int32_t H_I,
                      int32_t k, int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_layer(L);
+  int rc = indexer_validate(L, iq, iw, n_q, H_I, k, topk);
   if (rc) return rc;
-  if (!L->has_indexer) return set_error(LCA_EINVAL, "lca_indexer_topk needs an indexer (CSA) layer");
-  if (n_q < 1) return set_error(LCA_EINVAL, "n_q must be >= 1 (got %d)", n_q);
-  if (H_I < 1 || H_I > 32) return set_error(LCA_EUNSUPPORTED, "H_I must be in 1..32 (got %d)", H_I);
-  if (k < 1 || k > 2048) return set_error(LCA_EUNSUPPORTED, "k must be in 1..2048 (got %d)", k);
-  if (n_q > L->len_min)
-    return set_error(LCA_EINVAL, "n_q (%d) exceeds the shortest row (%lld tokens)", n_q,
-                     (long long)L->len_min);
-  if (L->max_blocks > 524288) return set_error(LCA_EUNSUPPORTED, "max_blocks above 524288");
-  if ((int64_t)L->batch * n_q > 0x7FFFFFFF / 2) return set_error(LCA_EUNSUPPORTED, "too many queries");
-  if ((rc = check_ptr(iq, "iq")) || (rc = check_ptr(iw, "iw")) || (rc = check_ptr(topk, "topk")))
-    return rc;
   IndexerPlan pl = plan_indexer(L, n_q, H_I, k);
   const size_t need = pl.total();
   if (!ws || ws_bytes < need)

@@ -60,6 +60,9 @@ struct IndexerPlan {
   }
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
+// argument checks of lca_indexer_topk (everything but the workspace)
+int indexer_validate(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
+                     const int32_t* topk);
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
                    int32_t* topk, void* ws, const IndexerPlan& plan, hipStream_t stream);
 
