@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 1
+#define LCA_ABI_VERSION 2
 
 enum {
   LCA_OK = 0,
@@ -163,21 +163,24 @@ int lca_compress_append(lca_layer *layer, const uint16_t *kv, const float *gate,
  *   topk  int32 [B][n_q][k]           (output)
  * Needs a CSA layer, 1 <= H_I <= 32, 1 <= k <= 2048, n_q <= len_min and
  * max_blocks <= 524288.  ws must hold lca_indexer_workspace(...) bytes and
- * be used by nothing but lca_indexer_topk.  Its first B * n_q * 16 KiB hold
- * one histogram per query; they must be zero when a call starts, and every
- * call leaves them zero again.  A call writes its scores and lists after its
- * own histograms, so a workspace that served a call with fewer queries
- * (B * n_q) holds non-zero bytes where a call with more queries keeps its
- * histograms: zero-fill it again before such a call (or keep one workspace
- * per query count).  A zero-filled workspace is ready for any call.
+ * be used by nothing but lca_indexer_topk.  Its first bytes (out[3] of
+ * lca_indexer_layout: per-row counters and one histogram per query) must be
+ * zero when a call starts, and every call leaves them zero again.  A call
+ * writes its scores and lists after them, so a workspace that served a call
+ * with fewer queries (B * n_q) holds non-zero bytes where a call with more
+ * queries keeps its counters and histograms: zero-fill it again before such
+ * a call (or keep one workspace per query count).  A zero-filled workspace
+ * is ready for any call.
+ * One query per row and H_I <= 16 (decode): the selection runs in the
+ * scoring launch (the row's last scoring workgroup selects from candidates
+ * the others kept); LCA_TOPK_FUSED = 0 runs it as a launch of its own.
  * The kernels are chosen from the shapes; for tests and tuning the choice
- * can be forced through environment variables read at every call (keep them
- * unchanged between the workspace query and the call, as the workspace size
- * follows the choice): LCA_SCORE_TILE (0/1: multi-query score kernel),
- * LCA_TOPK_CAND (0/1: candidate lists with it), LCA_TOPK_SLICED (0/1: the
- * selection split over part workgroups), LCA_TOPK_FUSED (1: one query per
- * row selects inside the scoring launch), LCA_SCORE_CPW (chunks of 1024
- * blocks per scoring workgroup).
+ * can be forced with lca_set_tuning (keep it unchanged between the workspace
+ * query and the call, as the workspace size follows the choice):
+ * LCA_SCORE_TILE (0/1: multi-query score kernel), LCA_TOPK_CAND (0/1:
+ * candidate lists with it), LCA_TOPK_SLICED (0/1: the selection split over
+ * part workgroups), LCA_TOPK_FUSED (0/1: decode selection inside the scoring
+ * launch), LCA_SCORE_CPW (chunks of 1024 blocks per scoring workgroup).
  */
 size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k);
 
@@ -185,19 +188,28 @@ size_t lca_indexer_workspace(const lca_layer *layer, int32_t n_q, int32_t H_I, i
  * lca_indexer_layout -- where lca_indexer_topk leaves each query's scores in
  * its workspace, for callers that inspect them (host only, enqueues nothing).
  * Same arguments as lca_indexer_workspace; out receives 8 values:
- *   out[0] stride S (key slots per query row), out[1] byte offset of the
- *   uint32 keys [B * n_q][S]; a key is the score's order key (the fp32 bits,
+ *   out[0] stride S (key slots per query row); out[1] byte offset of the
+ *   scores; out[3] bytes at the start of the workspace that must be zero
+ *   when a call starts (per-row counters and per-query histograms; every
+ *   call leaves them zero).  A key is the score's order key (the fp32 bits,
  *   all bits flipped for a negative score, the sign bit set otherwise).
- *   out[2] 0: key slot b holds block b's key for every visible block b.
- *   out[2] 1: candidate lists.  Only keys that can be among the query's top k
- *   are kept, and the area at out[1] holds uint32 pairs (key, t) [B * n_q][S]
- *   instead.  The query has out[5] lists; the length of list i is entry i
- *   of the uint32 array [B * n_q][out[5]] at byte offset out[4].  With
- *   W = out[6] and span = out[7], list i = 32 (c W + v) + col (c, v, col with
- *   v < W, col < 32) has entry j in slot c * span + 32 v + 32 W j + col, and
- *   that entry's t names block c * span + 32 (v + W t) + col.  Every block
- *   whose key lies in the top-12-bit bin of the query's k-th largest key, or
- *   above it, is in some list.  Unused entries of out are -1 or 0.
+ *   out[2] = 0: uint32 keys [B * n_q][S]; slot b holds block b's key for
+ *     every visible block b.
+ *   out[2] = 1 (candidate lists of multi-query rows): uint32 pairs (key, t)
+ *     [B * n_q][S].  The query has out[5] lists; the length of list i is
+ *     entry i of the uint32 array [B * n_q][out[5]] at byte offset out[4].
+ *     With W = out[6] and span = out[7], list i = 32 (c W + v) + col (c, v,
+ *     col with v < W, col < 32) has entry j in slot c * span + 32 v + 32 W j
+ *     + col, and that entry's t names block c * span + 32 (v + W t) + col.
+ *   out[2] = 2 (candidate segments of one-query rows, the selection inside
+ *     the scoring launch): uint32 pairs (key, block) [B * n_q][S]; the query
+ *     has out[5] segments of out[7] blocks; segment s holds, from slot
+ *     s * out[7] on, count pairs for blocks of its own range in ascending
+ *     order, count being entry s of the uint32 array [B * n_q][out[5]] at
+ *     byte offset out[4].
+ *   For kinds 1 and 2 every block whose key lies in the top-12-bit bin of
+ *   the query's k-th largest key, or above it, is kept.  Unused entries of
+ *   out are -1 or 0.
  * Returns LCA_OK or LCA_EINVAL (NULL layer or out, n_q < 1).
  */
 int lca_indexer_layout(const lca_layer *layer, int32_t n_q, int32_t H_I, int32_t k, int64_t *out);
@@ -242,8 +254,8 @@ int lca_indexer_topk_noalloc(const lca_layer *layer, const float *iq, const floa
  * Needs 1 <= H <= 128, 1 <= k <= 2048, n_q <= len_min and
  * n_q + window - 1 <= ring.  ws must hold lca_attend_workspace(...) bytes.
  * The number of key splits (and so the workspace size) follows the shapes;
- * the environment variable LCA_ATTEND_SPLITS, read at every call, forces it
- * for tests and tuning (keep it unchanged between the query and the call).
+ * lca_set_tuning("LCA_ATTEND_SPLITS", n) forces it for tests and tuning
+ * (keep it unchanged between the query and the call).
  */
 size_t lca_attend_workspace(const lca_layer *layer, int32_t n_q, int32_t H, int32_t k);
 int lca_csa_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32_t H,
@@ -261,6 +273,16 @@ int lca_csa_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32
  */
 int lca_hca_attend(const lca_layer *layer, const uint16_t *q, int32_t n_q, int32_t H,
                    float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lca_set_tuning -- force a kernel choice (names above: LCA_SCORE_TILE,
+ * LCA_TOPK_CAND, LCA_TOPK_SLICED, LCA_TOPK_FUSED, LCA_SCORE_CPW,
+ * LCA_ATTEND_SPLITS); value < 0 restores the automatic choice.  The initial
+ * values come from environment variables of the same names, read once when
+ * the library is loaded.  Process-wide; not meant to change while calls are
+ * being made on other threads.  Errors: EINVAL (NULL or unknown name).
+ */
+int lca_set_tuning(const char *name, int32_t value);
 
 /* Library version and last error (thread-local, never NULL). */
 int lca_abi_version(void);

@@ -73,6 +73,7 @@ def lib():
         L.lca_csa_attend.argtypes = [LP, P, C.c_int32, C.c_int32, P, C.c_int32, C.c_float, P, P,
                                      C.c_size_t, P]
         L.lca_hca_attend.argtypes = [LP, P, C.c_int32, C.c_int32, C.c_float, P, P, C.c_size_t, P]
+        L.lca_set_tuning.argtypes = [C.c_char_p, C.c_int32]
         L.lca_timing_begin.argtypes = [C.c_char_p]
         L.lca_timing_end.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
         _lib = L
@@ -223,6 +224,16 @@ def abi_version():
     return lib().lca_abi_version()
 
 
+def set_tuning(name, value=None):
+    """Force a kernel choice (lca_set_tuning); None or a negative value
+    restores the automatic choice."""
+    _check(lib().lca_set_tuning(name.encode(), -1 if value is None else int(value)))
+
+
+TUNING_NAMES = ("LCA_SCORE_TILE", "LCA_TOPK_CAND", "LCA_TOPK_SLICED", "LCA_TOPK_FUSED", "LCA_SCORE_CPW",
+                "LCA_ATTEND_SPLITS")
+
+
 def compress_append(layer: Layer, kv, gate, ikey=None, igate=None):
     """Append n tokens to every row.  kv int16/bf16 bits [B][n][512], gate fp32
     [B][n][512], ikey/igate fp32 [B][n][64] (indexer layers)."""
@@ -248,14 +259,16 @@ def indexer_workspace_bytes(layer: Layer, n_q, H_I, k):
 
 def indexer_layout(layer: Layer, n_q, H_I, k):
     """Where the indexer's workspace holds each query's order keys: a dict
-    with stride, keys (byte offset), cand (bool) and, for candidate lists,
-    counts (byte offset), lists, waves and span."""
+    with stride, keys (byte offset), kind (0 full key rows, 1 candidate lists,
+    2 per-workgroup candidate segments), zero (bytes at the start that are
+    zero between calls) and, for kinds 1 and 2, counts (byte offset), lists
+    (lists or segments per query), waves and span."""
     s = layer.struct()
     out = (C.c_int64 * 8)()
     _check(lib().lca_indexer_layout(C.byref(s), n_q, H_I, k, out))
     v = list(out)
-    return {"stride": v[0], "keys": v[1], "cand": bool(v[2]), "counts": v[4], "lists": v[5],
-            "waves": v[6], "span": v[7]}
+    return {"stride": v[0], "keys": v[1], "kind": v[2], "cand": v[2] == 1, "zero": v[3], "counts": v[4],
+            "lists": v[5], "waves": v[6], "span": v[7]}
 
 
 def indexer_topk(layer: Layer, iq, iw, k, out=None):

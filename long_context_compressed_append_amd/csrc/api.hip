@@ -4,7 +4,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
+#include <stdlib.h>
 #include <vector>
 
 #include "lca_internal.h"
@@ -21,10 +23,31 @@ int set_error(int code, const char* fmt, ...) {
   return code;
 }
 
+// ------------------------------------------------------------------ tuning
+// Kernel-choice overrides: read once from the environment when the library
+// is loaded, changed afterwards only through lca_set_tuning.  -1: automatic.
+namespace {
+const char* kTuneNames[kTuneCount] = {"LCA_SCORE_TILE", "LCA_TOPK_CAND", "LCA_TOPK_SLICED",
+                                      "LCA_TOPK_FUSED", "LCA_SCORE_CPW", "LCA_ATTEND_SPLITS"};
+struct Tuning {
+  std::atomic<int> v[kTuneCount];
+  Tuning() {
+    for (int i = 0; i < kTuneCount; i++) {
+      const char* e = getenv(kTuneNames[i]);
+      v[i].store((e && *e) ? atoi(e) : -1, std::memory_order_relaxed);
+    }
+  }
+};
+Tuning g_tuning;
+}  // namespace
+
+int tuning(TuneId id) { return g_tuning.v[id].load(std::memory_order_relaxed); }
+
 // ------------------------------------------------------------------ timing
 namespace {
 struct Timing {
   std::mutex mu;
+  std::atomic<int> open{0};   // a session is open: launches take the lock
   int kernel = kKernelNone;
   int used = 0;
   std::vector<hipEvent_t> start, stop;
@@ -36,6 +59,7 @@ const char* kKernelNames[kKernelCount] = {"indexer_score", "topk_select", "atten
 }  // namespace
 
 TimedLaunch::TimedLaunch(KernelId id, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_timing.open.load(std::memory_order_acquire)) return;   // no session: no lock, no events
   std::lock_guard<std::mutex> g(g_timing.mu);
   if (g_timing.kernel != id || g_timing.used >= kMaxTimed) return;
   slot = g_timing.used++;
@@ -164,16 +188,14 @@ int lca_indexer_layout(const lca_layer* L, int32_t n_q, int32_t H_I, int32_t k, 
   if (!L || n_q < 1 || L->ratio < 1 || L->batch < 1) return set_error(LCA_EINVAL, "invalid layer or n_q");
   if (!out) return set_error(LCA_EINVAL, "out is NULL");
   IndexerPlan pl = plan_indexer(L, n_q, H_I, k);
-  const int64_t lists_at = (int64_t)(pl.hist_bytes + pl.keys_bytes + pl.part_count_bytes + pl.part_bits_bytes +
-                                     pl.part_cand_bytes);
   out[0] = pl.stride;
-  out[1] = (int64_t)pl.hist_bytes;
-  out[2] = pl.cand ? 1 : 0;
-  out[3] = -1;
-  out[4] = pl.cand ? lists_at : -1;
-  out[5] = pl.cand_lists;
-  out[6] = pl.cand_waves;
-  out[7] = pl.cand_span;
+  out[1] = (int64_t)pl.off_keys;
+  out[2] = pl.fused ? 2 : (pl.cand ? 1 : 0);
+  out[3] = (int64_t)pl.zero_bytes;
+  out[4] = (pl.cand || pl.fused) ? (int64_t)pl.off_cand_count : -1;
+  out[5] = pl.fused ? pl.fused_wgs : pl.cand_lists;
+  out[6] = pl.cand ? pl.cand_waves : 0;
+  out[7] = pl.fused ? pl.fused_span : pl.cand_span;
   return LCA_OK;
 }
 
@@ -245,6 +267,7 @@ int lca_timing_begin(const char* kernel) {
   if (g_timing.kernel != kKernelNone) return set_error(LCA_EINVAL, "a timing session is already open");
   g_timing.kernel = id;
   g_timing.used = 0;
+  g_timing.open.store(1, std::memory_order_release);
   return LCA_OK;
 }
 
@@ -264,7 +287,18 @@ int lca_timing_end(double* total_ms, int64_t* launches) {
   if (launches) *launches = g_timing.used;
   g_timing.kernel = kKernelNone;
   g_timing.used = 0;
+  g_timing.open.store(0, std::memory_order_release);
   return LCA_OK;
+}
+
+int lca_set_tuning(const char* name, int32_t value) {
+  if (!name) return set_error(LCA_EINVAL, "tuning name is NULL");
+  for (int i = 0; i < kTuneCount; i++)
+    if (!strcmp(name, kTuneNames[i])) {
+      g_tuning.v[i].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+      return LCA_OK;
+    }
+  return set_error(LCA_EINVAL, "unknown tuning name '%s'", name);
 }
 
 }  // extern "C"

@@ -469,11 +469,6 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(CombineArgs a) {
   *reinterpret_cast<float4*>(dst + 16) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
 }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
-
 AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   AttendPlan pl;
   const int64_t nvmax = L->len_max / L->ratio;
@@ -482,7 +477,7 @@ AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   const int64_t rows = (int64_t)L->batch * n_q;
   const int64_t max_tiles = (pl.max_keys + kTile - 1) / kTile;
   int64_t s = (kAttendTargetWGs + rows * pl.head_groups - 1) / (rows * pl.head_groups);
-  const int forced = env_int("LCA_ATTEND_SPLITS", 0);
+  const int forced = tuning(kTuneAttendSplits);
   if (forced > 0) s = forced;
   if (s > max_tiles) s = max_tiles;
   if (s < 1) s = 1;

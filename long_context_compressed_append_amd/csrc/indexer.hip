@@ -88,6 +88,7 @@ struct ScoreArgs {
   // list lengths [rows][chunks][kTileWaves][32]
   uint32_t* cand_count;
   uint32_t* row_done;    // fused selection: workgroups of a row done, [rows], zero between calls
+  int fused_span;        // fused selection: blocks per scoring workgroup (its candidate segment)
 };
 
 // max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
@@ -167,6 +168,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // lanes whose bins all have k keys above them form a prefix 0 .. F-1, and in
 // lane F, where the count from the top crosses k, each lane takes one bin
 // (from the top down) and a wave scan gives the keys above it.  Wave-uniform.
+// kCoherent: h is a histogram in global memory that other workgroups are
+// adding to; it is read with agent-scope loads (past this XCD's L2).
+template <bool kCoherent = false>
 __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, int from) {
   const int lane = threadIdx.x & 63;
   const int lo = from & ~3;                           // whole uint4 groups
@@ -175,9 +179,19 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
   const int mine = max(0, min(per, n4 - per * lane));
   const uint4* hv = reinterpret_cast<const uint4*>(h + lo) + per * lane;
   uint32_t s = 0;
-  for (int i = 0; i < mine; i++) {
-    const uint4 x = hv[i];
-    s += x.x + x.y + x.z + x.w;
+  if (kCoherent) {
+    // 16-byte loads that read past this XCD's L2 (buffer cache policy sc1)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(h), (short)0,
+                                                                        kHistBins * 4, kBufferWord3);
+    for (int i = 0; i < mine; i++) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * lo + 16 * (per * lane + i), 0, 16);
+      s += x.x + x.y + x.z + x.w;
+    }
+  } else {
+    for (int i = 0; i < mine; i++) {
+      const uint4 x = hv[i];
+      s += x.x + x.y + x.z + x.w;
+    }
   }
   const uint32_t incl = wave_inclusive_scan(s);
   const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
@@ -187,7 +201,10 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
   const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
   const int base = lo + 4 * per * F;
   const int cnt = 4 * __builtin_amdgcn_readlane(mine, F);   // lane F's bins: base .. base + cnt - 1
-  const uint32_t c = lane < cnt ? h[base + cnt - 1 - lane] : 0u;   // the lane-th from the top
+  const uint32_t c = lane < cnt ? (kCoherent ? __hip_atomic_load(h + base + cnt - 1 - lane, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT)
+                                              : h[base + cnt - 1 - lane])
+                                 : 0u;   // the lane-th from the top
   const uint32_t ci = wave_inclusive_scan(c);
   const uint64_t q = __ballot(lane < cnt && aF + ci - c >= k);   // keys above that bin reach k
   return base + __popcll(q) - 1;
@@ -231,18 +248,23 @@ template <bool kCoherent>
 __device__ void select_row(const SelectArgs& a, int srow, uint32_t* hist, uint32_t* tmp, uint32_t* found,
                            uint32_t* cand, uint32_t* bitmap);
 
-// kFused: 512 threads, two halves of 4 wavefronts on two consecutive chunk
-// ranges of the row sharing one histogram; keys leave with agent-scope stores,
-// and the row's last workgroup to finish (a per-row counter, after every
-// thread's stores and histogram atomics have completed) runs the selection
-// for the row, reading keys and histogram with agent-scope loads.  No
-// device-scope fence is needed: nothing it reads sits only in another
-// XCD's L2.
+// The decode scoring with the selection in the same launch (kFused).
+__device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, int nv, uint32_t* lhist,
+                           uint32_t* dyn, int wg_b0);
+
+// kFused: the keys stay in LDS; from its own histogram and the row's
+// histogram as it stands the workgroup derives a bin below the row's
+// threshold bin and writes only its keys above that bin (candidates, in
+// block order) to its segment of the workspace, with agent-scope stores.
+// The row's last workgroup to finish (a per-row counter, after every
+// thread's stores and histogram atomics have completed) selects from the
+// candidates, reading them with agent-scope loads.  No device-scope fence is
+// needed: nothing it reads sits only in another XCD's L2.
 // kHQ: heads per chain slot (8, 16 or 32 >= H); kTPA key tiles share one
 // matrix-core output (4, 2 or 1).
 template <bool kFused, int kHQ>
-__global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(ScoreArgs a, SelectArgs sel) {
-  constexpr int kT = kFused ? 512 : 256;
+__global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectArgs sel) {
+  constexpr int kT = 256;
   constexpr int kTPA = kHQ == 32 ? 1 : 32 / kHQ;
   static_assert(kDepth % kTPA == 0, "a set of loaded iterations holds whole tile groups");
   const int srow = blockIdx.y;
@@ -251,15 +273,18 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
   // are issued before the row length arrives: any block below the key row
   // capacity is readable, and blocks past the visible count are masked later.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wh = wave & 3;                       // wavefront within its half
+  const int wh = wave;                           // wavefront of the workgroup
   // Block indices fit 32 bits (a key row holds at most 524 288 blocks).
-  const int c0 = ((int)blockIdx.x * (kFused ? 2 : 1) + (wave >> 2)) * a.cpw;
+  const int c0 = (int)blockIdx.x * a.cpw;
   const int cap = (int)(a.stride < a.max_blocks ? a.stride : a.max_blocks);
 
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
   __shared__ float q_w[32];
   __shared__ uint32_t lhist[kHistBins];
+  // kFused: the workgroup's keys by block offset (later the selection bitmap)
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
+  const int wg_b0 = (int)blockIdx.x * a.cpw * kScoreBlocksPerWG;   // kFused: first block of the workgroup
   const int r = lane & 31, kh = lane >> 5;
 
   const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
@@ -362,12 +387,12 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
     const int t_r = kHQ == 32 ? 0 : 2 * (e_r / kHQ) + s_r;
     const bool hv = h < a.H;
     const int* src = reinterpret_cast<const int*>(&q_code[hv ? h : 0][16 * kh]);
-    const int c0 = hv ? src[0] : 0, c1 = hv ? src[1] : 0, c2 = hv ? src[2] : 0, c3 = hv ? src[3] : 0;
+    const int d0 = hv ? src[0] : 0, d1 = hv ? src[1] : 0, d2 = hv ? src[2] : 0, d3 = hv ? src[3] : 0;
     const int sc = hv ? q_exp[h][kh] + 127 : 127;
 #pragma unroll
     for (int t = 0; t < kTPA; t++) {
       const bool mine = t_r == t;
-      Af[t] = (v8i){mine ? c0 : 0, mine ? c1 : 0, mine ? c2 : 0, mine ? c3 : 0, 0, 0, 0, 0};
+      Af[t] = (v8i){mine ? d0 : 0, mine ? d1 : 0, mine ? d2 : 0, mine ? d3 : 0, 0, 0, 0, 0};
       saf[t] = mine ? sc : 127;
     }
   }
@@ -500,7 +525,7 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
       if ((kHQ != 32 || kh == 0) & (i0 + u < n_it) & (blk < nv)) {
         const uint32_t key = ord_key(__fadd_rn(total[kk], 0.0f));   // -0 -> +0
         if (kFused)
-          __hip_atomic_store(&out[blk], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          dyn_lds[blk - wg_b0] = key;
         else
           out[blk] = key;
         atomicAdd(&lhist[key >> kHistShift], 1u);
@@ -518,27 +543,17 @@ __global__ void __launch_bounds__(kFused ? 512 : 256) indexer_score_kernel(Score
     for (int u = 0; u < kDepth; u++) load(i0 + 3 * kDepth + u, kB[u], eB[u]);
   }
   __syncthreads();
-  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
-  // every count is read before any atomic goes out
-  uint32_t hc[kHistBins / kT];
-#pragma unroll
-  for (int i = 0; i < kHistBins / kT; i++) hc[i] = lhist[tid + kT * i];
-#pragma unroll
-  for (int i = 0; i < kHistBins / kT; i++)
-    if (hc[i]) atomicAdd(&gh[tid + kT * i], hc[i]);
   if constexpr (kFused) {
-    __builtin_amdgcn_s_waitcnt(0);     // this thread's key stores and atomics have completed
-    __syncthreads();
-    __shared__ uint32_t last;
-    if (tid == 0)
-      last = __hip_atomic_fetch_add(&a.row_done[srow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             gridDim.x - 1;
-    __syncthreads();
-    if (!last) return;
-    if (tid == 0) __hip_atomic_store(&a.row_done[srow], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __shared__ uint32_t tmp[64], found[4];
-    __shared__ uint32_t cand[2 * kCandCap], bitmap[2 * kMaxWords];
-    select_row<true>(sel, srow, lhist, tmp, found, cand, bitmap);
+    fused_tail(a, sel, srow, nv, lhist, dyn_lds, wg_b0);
+  } else {
+    uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+    // every count is read before any atomic goes out
+    uint32_t hc[kHistBins / kT];
+#pragma unroll
+    for (int i = 0; i < kHistBins / kT; i++) hc[i] = lhist[tid + kT * i];
+#pragma unroll
+    for (int i = 0; i < kHistBins / kT; i++)
+      if (hc[i]) atomicAdd(&gh[tid + kT * i], hc[i]);
   }
 }
 
@@ -890,8 +905,9 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
 // ---------------------------------------------------------------------------
 
 
-// exclusive prefix sum over the kSelThreads threads; returns the block total
-// in *total (tmp >= 32 words)
+// exclusive prefix sum over the kT threads of the workgroup; returns the
+// block total in *total (tmp >= kT / 64 words)
+template <int kT = kSelThreads>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t x = wave_inclusive_scan(v);
@@ -899,7 +915,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   __syncthreads();
   uint32_t before_wave = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; w++) {
+  for (int w = 0; w < kT / 64; w++) {
     const uint32_t t = tmp[w];
     before_wave += w < wave ? t : 0u;
     all += t;
@@ -1723,8 +1739,398 @@ __global__ void __launch_bounds__(kSelThreads) topk_cand_kernel(SelectArgs a) {
   compact(bitmap, nv, k, out, tmp);
 }
 
+// ---------------------------------------------------------------------------
+// The selection inside the decode scoring launch (kFused; workgroups of 256
+// threads, as the scoring without it).
+//
+// Each scoring workgroup holds the keys of its blocks in LDS (dyn) and their
+// histogram (lhist).  The highest bin b whose higher bins hold at least k of
+// its own keys lies below the row's threshold bin tb (the row's counts are at
+// least the workgroup's), so only its bins above b go to the row's histogram
+// and only its keys above b can be among the row's top k.  The row's
+// histogram as it stands (other workgroups' flushes, each count at most its
+// final value) often gives a higher such bin; either is valid.  The
+// workgroup writes its keys above the bound as (key, block) pairs, in block
+// order, to its segment (slot wg_b0 of the row's pair array; capacity: its
+// blocks), the count to cand_count[row][workgroup], and arrives at the row's
+// counter.  The row's last workgroup to arrive selects:
+//   1. the final row histogram gives tb and the count of keys above it (and
+//      is zeroed for the next call); the segment counts give the offset of
+//      every segment in the row's candidate sequence;
+//   2. one pass over the candidates: those above bin tb set their bit in an
+//      LDS bitmap of the row's blocks, those inside it go to an LDS list;
+//   3. the list is ranked by (key desc, block asc): a histogram of key bits
+//      19..10, built during the pass, gives the sub-bin of the last key
+//      taken; entries above it are taken and those inside it ranked by
+//      direct comparison (more than kFusedTies entries in bin tb: radix
+//      passes over the candidates in memory);
+//   4. the bitmap is compacted into ascending block indices.
+// ---------------------------------------------------------------------------
+
+constexpr int kFT = 256;              // threads of a fused scoring workgroup
+constexpr int kFusedTies = 2048;      // bin-tb candidates the selecting workgroup ranks in LDS
+constexpr int kMaxFusedSegs = 256;    // scoring workgroups per row
+constexpr int kMaxFusedCpw = 4;       // chunks per scoring workgroup: <= 4096 keys in LDS
+constexpr int kFusedDirect = 2 * kFT; // bin-tb lists up to this long are ranked directly
+
+// Over the 1024-bin LDS histogram h (thread t holds bins P t .. P t + P - 1,
+// P = 1024 / kT): the bin where the count from the top reaches `need`:
+// found[0] = bin, found[1] = keys in higher bins, found[2] = keys in the bin.
+// found[] must be preset; unchanged when h holds fewer than `need` keys.
+template <int kT>
+__device__ __forceinline__ void find_bin_1024_t(const uint32_t* h, uint32_t need, uint32_t* tmp, uint32_t* found) {
+  constexpr int P = 1024 / kT;
+  const int tid = threadIdx.x;
+  uint32_t c[P], local = 0;
+#pragma unroll
+  for (int i = 0; i < P; i++) {
+    c[i] = h[P * tid + i];
+    local += c[i];
+  }
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan<kT>(local, tmp, &total);
+  uint32_t run = total - below - local;           // keys in bins above this thread's
+#pragma unroll
+  for (int i = P - 1; i >= 0; i--) {
+    if (run < need && run + c[i] >= need) {
+      found[0] = (uint32_t)(P * tid + i);
+      found[1] = run;
+      found[2] = c[i];
+    }
+    run += c[i];
+  }
+  __syncthreads();
+}
+
+// The `need` largest by (key desc, block asc) of n list entries that all lie
+// in bin tb (bits 31..20 of the key); entry j is get(j) = (key, block) and
+// mark(j) is called for each one taken.  Direct comparison up to
+// kFusedDirect entries, else radix passes of 10 bits over the key's low 20
+// bits and, for entries equal to the threshold key, over 0xFFFFF - block.
+template <int kT, typename Get, typename Mark>
+__device__ __forceinline__ void rank_bin_list(int n, Get get, uint32_t tb, uint32_t need, uint32_t* hist1024,
+                                              uint32_t* tmp, uint32_t* found, Mark mark) {
+  const int tid = threadIdx.x;
+  if (n <= kFusedDirect) {
+#pragma unroll
+    for (int r = 0; r < kFusedDirect / kT; r++) {
+      const int i = tid + r * kT;
+      if (i < n) {
+        const uint2 ei = get(i);
+        uint32_t rank = 0;
+        for (int j = 0; j < n; j++) {
+          const uint2 ej = get(j);
+          rank += (ej.x > ei.x || (ej.x == ei.x && ej.y < ei.y)) ? 1u : 0u;
+        }
+        if (rank < need) mark(i);
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  // threshold key T among the entries: bits 19..10, then 9..0
+  uint32_t need_k = need, pfx = tb;
+  int shift = 20;
+  bool exact = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 && !exact; pass++) {
+    shift -= 10;
+    for (int i = tid; i < 1024; i += kT) hist1024[i] = 0;
+    if (tid == 0) found[0] = found[1] = found[2] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kT) {
+      const uint32_t key = get(i).x;
+      if ((key >> (shift + 10)) == pfx) atomicAdd(&hist1024[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin_1024_t<kT>(hist1024, need_k, tmp, found);
+    need_k -= found[1];
+    pfx = (pfx << 10) | found[0];
+    exact = found[2] == need_k;
+    __syncthreads();
+  }
+  if (exact) {
+    for (int i = tid; i < n; i += kT)
+      if ((get(i).x >> shift) >= pfx) mark(i);
+    __syncthreads();
+    return;
+  }
+  // shift is 0: pfx is the threshold key T; need_k of the entries equal to
+  // it are taken, those of the lowest blocks
+  const uint32_t T = pfx;
+  uint32_t vp = 0;
+  int vsh = 20;
+  bool vexact = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 && !vexact; pass++) {
+    vsh -= 10;
+    for (int i = tid; i < 1024; i += kT) hist1024[i] = 0;
+    if (tid == 0) found[0] = found[1] = found[2] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kT) {
+      const uint2 e = get(i);
+      const uint32_t x = 0xFFFFFu - e.y;
+      if (e.x == T && (x >> (vsh + 10)) == vp) atomicAdd(&hist1024[(x >> vsh) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin_1024_t<kT>(hist1024, need_k, tmp, found);
+    need_k -= found[1];
+    vp = (vp << 10) | found[0];
+    vexact = found[2] == need_k;     // blocks are distinct: true after the second pass
+    __syncthreads();
+  }
+  for (int i = tid; i < n; i += kT) {
+    const uint2 e = get(i);
+    if (e.x > T || (e.x == T && ((0xFFFFFu - e.y) >> vsh) >= vp)) mark(i);
+  }
+  __syncthreads();
+}
+
+// The selecting (last) workgroup of row srow.  lhist: 4096 words of LDS
+// (free; it takes the sub-bin list); dyn: the dynamic LDS: the row's bitmap
+// (nv bits), then up to kFusedTies bin-tb candidates (keys, blocks) and a
+// 1024-bin histogram.
+__device__ __forceinline__ void fused_select(const ScoreArgs& a, const SelectArgs& sel, int srow, int nv,
+                                          uint32_t* lhist, uint32_t* dyn, uint32_t* tmp, uint32_t* found) {
+  constexpr int kT = kFT;
+  const int k = a.k, tid = threadIdx.x;
+  const int nseg = (int)gridDim.x, span = a.fused_span;
+  int32_t* out = sel.topk + (int64_t)srow * k;
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+  const uint64_t* row_pairs = reinterpret_cast<const uint64_t*>(a.keys) + (int64_t)srow * a.stride;
+  __shared__ uint32_t soff[kMaxFusedSegs + 1];
+  __shared__ uint32_t ntie;
+
+  // 1. the row's histogram (16 bins per thread) and segment counts, read
+  //    past the caches
+  uint4 hv[4];
+  load_keys<4, kCoherentAux>(key_row_rsrc(gh, kHistBins), kHistBins, 16 * tid, hv);
+  const uint32_t my_count =
+      tid < nseg ? __hip_atomic_load(&a.cand_count[(int64_t)srow * nseg + tid], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT)
+                 : 0u;
+  if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;
+  {
+    const uint32_t cs[16] = {hv[3].w, hv[3].z, hv[3].y, hv[3].x, hv[2].w, hv[2].z, hv[2].y, hv[2].x,
+                             hv[1].w, hv[1].z, hv[1].y, hv[1].x, hv[0].w, hv[0].z, hv[0].y, hv[0].x};
+    uint32_t c16 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) c16 += cs[i];
+    uint32_t total;
+    const uint32_t below = block_exclusive_scan<kT>(c16, tmp, &total);
+#pragma unroll
+    for (int v = 0; v < 4; v++) reinterpret_cast<uint4*>(gh)[4 * tid + v] = make_uint4(0, 0, 0, 0);   // next call
+    uint32_t run = total - below - c16;              // keys in bins above this thread's 16
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if (run < (uint32_t)k && run + cs[i] >= (uint32_t)k) {
+        found[0] = (uint32_t)(16 * tid + 15 - i);
+        found[1] = run;
+      }
+      run += cs[i];
+    }
+  }
+  uint32_t ctot;
+  const uint32_t cbase = block_exclusive_scan<kT>(my_count, tmp, &ctot);   // nseg <= kT
+  if (tid < nseg) soff[tid] = cbase;
+  if (tid == 0) {
+    soff[nseg] = ctot;
+    ntie = 0;
+  }
+  if (nv <= k) {
+    for (int j = tid; j < k; j += kT) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const int nwords32 = (nv + 31) >> 5;
+  uint32_t* bitmap = dyn;
+  uint32_t* tkey = dyn + nwords32;
+  uint32_t* tblk = tkey + kFusedTies;
+  uint32_t* hist1024 = tblk + kFusedTies;
+  for (int w = tid; w < nwords32; w += kT) bitmap[w] = 0u;
+  for (int i = tid; i < 1024; i += kT) hist1024[i] = 0u;
+  __syncthreads();
+  const uint32_t tb = found[0], need = (uint32_t)k - found[1];
+  const uint32_t C = ctot;
+  // 2. one pass over the candidates, kPer per thread in flight: above bin tb
+  //    -> bit; inside it -> the LDS list and a histogram of key bits 19..10
+  constexpr int kPer = 16;
+#pragma unroll 1
+  for (uint32_t c0 = 0; c0 < C; c0 += kPer * kT) {
+    uint64_t e[kPer];
+    int sg = 0;                                       // segment of i: soff[sg] <= i < soff[sg + 1]
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const uint32_t i = c0 + (uint32_t)(u * kT + tid);
+      if (i < C)
+        while (soff[sg + 1] <= i) sg++;
+      e[u] = i < C ? __hip_atomic_load(row_pairs + (int64_t)sg * span + (i - soff[sg]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const uint32_t i = c0 + (uint32_t)(u * kT + tid);
+      if (i < C) {
+        const uint32_t key = (uint32_t)e[u], blk = (uint32_t)(e[u] >> 32);
+        const uint32_t bin = key >> kHistShift;
+        if (bin > tb) set_bit(bitmap, blk);
+        if (bin == tb) {
+          atomicAdd(&hist1024[(key >> 10) & 1023u], 1u);
+          const uint32_t t = atomicAdd(&ntie, 1u);
+          if (t < (uint32_t)kFusedTies) {
+            tkey[t] = key;
+            tblk[t] = blk;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // 3. the bin-tb candidates ranked: from the LDS list, or (more than
+  //    kFusedTies of them) from memory, every candidate below bin tb read as
+  //    key 0 (below every key of a bin tb > 0; none exist when tb = 0) and
+  //    those above it (already set) possibly marked again
+  const uint32_t nt = ntie;
+  if (nt <= (uint32_t)kFusedTies) {
+    // the sub-bin sb of key bits 19..10 that holds the last key taken: list
+    // entries above it are taken; those inside it are ranked directly when
+    // they do not all fit (few: one 1024th of the bin)
+    if (tid == 0) found[0] = found[1] = found[2] = 0;
+    __syncthreads();
+    find_bin_1024_t<kT>(hist1024, need, tmp, found);
+    const uint32_t sb = (tb << 10) | found[0], need2 = need - found[1];
+    const bool all_in = found[2] == need2;
+    uint32_t* sub = lhist;                            // list positions of the sub-bin's entries (<= nt)
+    if (tid == 0) found[3] = 0;
+    __syncthreads();
+    for (uint32_t j = tid; j < nt; j += kT) {
+      const uint32_t kp = tkey[j] >> 10;
+      if (kp > sb || (all_in && kp == sb)) set_bit(bitmap, tblk[j]);
+      else if (kp == sb) sub[atomicAdd(&found[3], 1u)] = j;
+    }
+    __syncthreads();
+    if (!all_in) {
+      const uint32_t ns = found[3];
+      for (uint32_t i = tid; i < ns; i += kT) {
+        const uint32_t ji = sub[i];
+        const uint64_t vi = ((uint64_t)tkey[ji] << 32) | (0xFFFFFFFFu - tblk[ji]);
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (uint32_t q = 0; q < ns; q++) {
+          const uint32_t jq = sub[q];
+          const uint64_t vq = ((uint64_t)tkey[jq] << 32) | (0xFFFFFFFFu - tblk[jq]);
+          rank += vq > vi ? 1u : 0u;
+        }
+        if (rank < need2) set_bit(bitmap, tblk[ji]);
+      }
+    }
+    __syncthreads();
+  } else {
+    auto pair_at = [&](int i) -> uint64_t {
+      int lo = 0, hi = nseg;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (soff[mid] <= (uint32_t)i) lo = mid; else hi = mid;
+      }
+      return __hip_atomic_load(row_pairs + (int64_t)lo * span + ((uint32_t)i - soff[lo]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    };
+    rank_bin_list<kT>((int)C, [&](int i) {
+      const uint64_t v = pair_at(i);
+      const uint32_t key = (uint32_t)v;
+      return make_uint2((key >> kHistShift) < tb ? 0u : key, (uint32_t)(v >> 32));
+    }, tb, need, hist1024, tmp, found, [&](int i) { set_bit(bitmap, (uint32_t)(pair_at(i) >> 32)); });
+  }
+  // 4. compaction: thread t counts the bits of words t * wq .. t * wq + wq - 1,
+  //    a scan gives its first output position
+  const int wq = (nwords32 + kT - 1) / kT;
+  const int w0 = wq * tid;
+  uint32_t cnt = 0;
+  for (int w = w0; w < w0 + wq && w < nwords32; w++) cnt += (uint32_t)__popc(bitmap[w]);
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan<kT>(cnt, tmp, &tot);
+  for (int w = w0; w < w0 + wq && w < nwords32; w++) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
+      pos++;
+    }
+  }
+}
+
+__device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, int nv, uint32_t* lhist,
+                           uint32_t* dyn, int wg_b0) {
+  constexpr int kT = kFT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int span = a.fused_span;
+  uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
+  __shared__ int bnd;
+  __shared__ uint32_t tmp[64], found[4];
+  __shared__ uint32_t last;
+  // 1. the bound from the workgroup's own keys
+  if (wave == 0) {
+    const int b = running_threshold(lhist, (uint32_t)a.k, 0);
+    if (lane == 0) bnd = b;
+  }
+  __syncthreads();
+  const int b_loc = bnd;
+  // 2. its counts of the bins above it go to the row's histogram
+  for (int i = tid; i < kHistBins; i += kT) {
+    const uint32_t c = lhist[i];
+    if (c && i > b_loc) atomicAdd(&gh[i], c);
+  }
+  // 3. a higher bound from the row's histogram as it stands (the flushes of
+  //    the workgroups that are done), if it has one
+  if (wave == 0) {
+    const int b = running_threshold<true>(gh, (uint32_t)a.k, b_loc + 1);
+    if (lane == 0) bnd = max(b, b_loc);
+  }
+  __syncthreads();
+  const uint32_t kmin = (uint32_t)(bnd + 1) << kHistShift;   // bnd <= 4094
+  // 4. the keys above the bound, in block order: thread t takes the blocks
+  //    t * per .. t * per + per - 1 of the workgroup
+  const int nmine = min(span, nv - wg_b0);
+  const int per = span / kT;                                  // <= 16
+  constexpr int kMaxPer = kMaxFusedCpw * kScoreBlocksPerWG / kT;
+  uint32_t ck[kMaxPer];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; i++) {
+    const int j = tid * per + i;
+    const bool ok = i < per && j < nmine;
+    ck[i] = ok ? dyn[j] : 0u;
+    cnt += (ok && ck[i] >= kmin) ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t o = block_exclusive_scan<kT>(cnt, tmp, &tot);
+  uint64_t* seg = reinterpret_cast<uint64_t*>(a.keys) + (int64_t)srow * a.stride + wg_b0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; i++) {
+    const int j = tid * per + i;
+    if (i < per && j < nmine && ck[i] >= kmin) {
+      __hip_atomic_store(seg + o, ((uint64_t)(uint32_t)(wg_b0 + j) << 32) | ck[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      o++;
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.cand_count[(int64_t)srow * gridDim.x + blockIdx.x], tot, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  // 5. arrival: this thread's stores and atomics have completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&a.row_done[srow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  if (tid == 0) __hip_atomic_store(&a.row_done[srow], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  fused_select(a, sel, srow, nv, lhist, dyn, tmp, found);
+}
+
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
-  (void)H_I;
   (void)k;
   IndexerPlan pl;
   const int64_t nvmax = L->len_max / L->ratio;   // visible blocks of the last query
@@ -1735,8 +2141,8 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   // about kScoreTargetWGs workgroups in all, each with >= 1 chunk of one query
   const int64_t rows = (int64_t)L->batch * n_q;
   int64_t cpw = (rows * chunks + kScoreTargetWGs - 1) / kScoreTargetWGs;
-  const char* env = getenv("LCA_SCORE_CPW");
-  if (env && *env) cpw = atoi(env);
+  const int force_cpw = tuning(kTuneScoreCpw);
+  if (force_cpw > 0) cpw = force_cpw;
   if (cpw < 1) cpw = 1;
   if (cpw > chunks) cpw = chunks;
   pl.cpw = (int)cpw;
@@ -1745,54 +2151,81 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   pl.tile = 0;
   pl.qgroups = 0;
   bool tile = n_q >= kTileMinQueries && H_I <= 32;
-  const char* tenv = getenv("LCA_SCORE_TILE");
-  if (tenv && *tenv) tile = atoi(tenv) != 0 && H_I <= 32;
+  if (tuning(kTuneScoreTile) >= 0) tile = tuning(kTuneScoreTile) != 0 && H_I <= 32;
   if (tile) {
     pl.tile = H_I <= 16 ? 8 : 4;
     pl.qgroups = (n_q + pl.tile * kTileSets - 1) / (pl.tile * kTileSets);
     int64_t tcpw = ((int64_t)L->batch * pl.qgroups * chunks + kTileTargetWGs - 1) / kTileTargetWGs;
-    if (env && *env) tcpw = atoi(env);
+    if (force_cpw > 0) tcpw = force_cpw;
     if (tcpw < 1) tcpw = 1;
     if (tcpw > chunks) tcpw = chunks;
     pl.cpw = (int)tcpw;
     pl.chunks = (int)((chunks + tcpw - 1) / tcpw);
   }
-  pl.keys_bytes = (size_t)rows * pl.stride * sizeof(uint32_t);
-  pl.hist_bytes = (size_t)rows * kHistBins * sizeof(uint32_t);
   // selection: parts of kPartKeys blocks on workgroups of their own when the
   // rows are long and too few to fill the chip
   bool sliced = pl.stride > kSliceMinBlocks && rows < kSliceMaxRows;
-  const char* senv = getenv("LCA_TOPK_SLICED");
-  if (senv && *senv) sliced = atoi(senv) != 0;
+  const int force_sliced = tuning(kTuneTopkSliced);
+  if (force_sliced >= 0) sliced = force_sliced != 0;
   // tile kernel: candidate lists instead of full key rows, unless a row has
   // too many lists (chunks x wavefronts) to gather
   pl.cand = pl.tile && pl.chunks * kTileWavesPerSet <= kMaxCandGroups;
-  const char* cenv = getenv("LCA_TOPK_CAND");
-  if (cenv && *cenv) pl.cand = pl.tile && atoi(cenv) != 0;
+  if (tuning(kTuneTopkCand) >= 0) pl.cand = pl.tile && tuning(kTuneTopkCand) != 0;
   if (pl.cand) sliced = false;
-  // opt-in: one query per row and one selection workgroup per row, the
-  // scoring's last workgroup of each row selects in the same launch (saves a
-  // launch, but measured no faster than two launches in a replayed graph)
-  pl.fused = false;
-  const char* fenv = getenv("LCA_TOPK_FUSED");
-  if (fenv && *fenv) pl.fused = !pl.tile && !sliced && atoi(fenv) != 0;
+  // decode (one query per score workgroup, H <= 16): the selection runs in
+  // the scoring launch from per-workgroup candidates, unless the sliced or
+  // separate selection is asked for
+  pl.fused = !pl.tile && H_I <= 16 && force_sliced != 1;
+  if (tuning(kTuneTopkFused) >= 0) pl.fused = pl.fused && tuning(kTuneTopkFused) != 0;
+  pl.fused_wgs = pl.fused_span = 0;
+  pl.fused_lds = 0;
+  if (pl.fused) {
+    sliced = false;
+    int64_t fc = pl.cpw;                             // chunks per workgroup
+    const int64_t min_fc = (chunks + kMaxFusedSegs - 1) / kMaxFusedSegs;
+    if (fc < min_fc) fc = min_fc;
+    if (fc > kMaxFusedCpw) fc = kMaxFusedCpw;        // chunks <= 512: min_fc <= 2
+    pl.cpw = (int)fc;
+    pl.fused_wgs = (int)((chunks + fc - 1) / fc);
+    pl.fused_span = (int)(fc * kScoreBlocksPerWG);
+    // dynamic LDS: the workgroup's keys; then, in the selecting workgroup,
+    // the row's bitmap, the bin-tb list and a 1024-bin histogram
+    size_t words = (size_t)pl.fused_span;
+    const size_t sel_words = (size_t)((pl.stride + 31) / 32) + 2 * kFusedTies + 1024;
+    if (words < sel_words) words = sel_words;
+    pl.fused_lds = 4 * words;
+  }
   pl.cand_waves = kTileWavesPerSet;
   pl.cand_lists = pl.cand ? pl.chunks * kTileWavesPerSet * 32 : 0;
   pl.cand_span = pl.cpw * kScoreBlocksPerWG;
   pl.slices = sliced ? (int)((pl.stride + kPartKeys - 1) / kPartKeys) : 0;
+  // workspace layout
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  pl.part_count_bytes = up((size_t)rows * pl.slices * sizeof(uint32_t));
-  pl.part_bits_bytes = (size_t)rows * pl.slices * kSelThreads * sizeof(uint32_t);
-  pl.part_cand_bytes = (size_t)rows * pl.slices * 2 * kCandCap * sizeof(uint32_t);
-  if (pl.cand) pl.keys_bytes *= 2;     // (key, visit) pairs
-  pl.cand_count_bytes = pl.cand ? up((size_t)rows * pl.chunks * kTileWavesPerSet * 32 * sizeof(uint32_t)) : 0;
-  pl.row_done_bytes = pl.fused ? up((size_t)rows * sizeof(uint32_t)) : 0;
+  size_t o = 0;
+  pl.off_done = o;
+  o += up(pl.fused ? (size_t)rows * sizeof(uint32_t) : 0);
+  pl.off_hist = o;
+  o += (size_t)rows * kHistBins * sizeof(uint32_t);
+  pl.zero_bytes = o;
+  pl.off_keys = o;
+  o += up((size_t)rows * pl.stride * ((pl.cand || pl.fused) ? 8 : 4));   // keys, or (key, x) pairs
+  pl.off_part_count = o;
+  o += up((size_t)rows * pl.slices * sizeof(uint32_t));
+  pl.off_part_bits = o;
+  o += (size_t)rows * pl.slices * kSelThreads * sizeof(uint32_t);
+  pl.off_part_cand = o;
+  o += (size_t)rows * pl.slices * 2 * kCandCap * sizeof(uint32_t);
+  pl.off_cand_count = o;
+  if (pl.cand) o += up((size_t)rows * pl.chunks * kTileWavesPerSet * 32 * sizeof(uint32_t));
+  if (pl.fused) o += up((size_t)rows * pl.fused_wgs * sizeof(uint32_t));
+  pl.total_bytes = o;
   return pl;
 }
 
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
                    int32_t* topk, void* ws, const IndexerPlan& pl, hipStream_t stream) {
   const int rows = L->batch * n_q;
+  char* base = static_cast<char*>(ws);
   ScoreArgs s;
   s.n_q = n_q;
   s.H = H_I;
@@ -1804,14 +2237,13 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.idx_scale = L->idx_scale;
   s.iq = iq;
   s.iw = iw;
-  s.hist = static_cast<uint32_t*>(ws);
+  s.hist = reinterpret_cast<uint32_t*>(base + pl.off_hist);
   s.cpw = pl.cpw;
-  s.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.hist_bytes);
+  s.keys = reinterpret_cast<uint32_t*>(base + pl.off_keys);
   s.k = k;
-  char* cand = static_cast<char*>(ws) + pl.hist_bytes + pl.keys_bytes + pl.part_count_bytes + pl.part_bits_bytes +
-               pl.part_cand_bytes;
-  s.cand_count = pl.cand ? reinterpret_cast<uint32_t*>(cand) : nullptr;
-  s.row_done = pl.fused ? reinterpret_cast<uint32_t*>(cand + pl.cand_count_bytes) : nullptr;
+  s.cand_count = (pl.cand || pl.fused) ? reinterpret_cast<uint32_t*>(base + pl.off_cand_count) : nullptr;
+  s.row_done = pl.fused ? reinterpret_cast<uint32_t*>(base + pl.off_done) : nullptr;
+  s.fused_span = pl.fused_span;
   SelectArgs sa;
   sa.n_q = n_q;
   sa.m = L->ratio;
@@ -1822,10 +2254,9 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.hist = s.hist;
   sa.topk = topk;
   sa.slices = pl.slices;
-  char* part = static_cast<char*>(ws) + pl.hist_bytes + pl.keys_bytes;
-  sa.part_count = reinterpret_cast<uint32_t*>(part);
-  sa.part_bits = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes);
-  sa.part_cand = reinterpret_cast<uint32_t*>(part + pl.part_count_bytes + pl.part_bits_bytes);
+  sa.part_count = reinterpret_cast<uint32_t*>(base + pl.off_part_count);
+  sa.part_bits = reinterpret_cast<uint32_t*>(base + pl.off_part_bits);
+  sa.part_cand = reinterpret_cast<uint32_t*>(base + pl.off_part_cand);
   sa.cand_count = s.cand_count;
   sa.segs = pl.cand_lists / 32;
   sa.span = pl.cand_span;
@@ -1841,13 +2272,11 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
     else if (pl.tile == 4)
       hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
     else if (pl.fused) {   // the selection runs in the same launch
-      const dim3 g((pl.chunks + 1) / 2, rows), b(512);
+      const dim3 g(pl.fused_wgs, rows), b(kFT);
       if (H_I <= 8)
-        hipLaunchKernelGGL((indexer_score_kernel<true, 8>), g, b, 0, stream, s, sa);
-      else if (H_I <= 16)
-        hipLaunchKernelGGL((indexer_score_kernel<true, 16>), g, b, 0, stream, s, sa);
+        hipLaunchKernelGGL((indexer_score_kernel<true, 8>), g, b, pl.fused_lds, stream, s, sa);
       else
-        hipLaunchKernelGGL((indexer_score_kernel<true, 32>), g, b, 0, stream, s, sa);
+        hipLaunchKernelGGL((indexer_score_kernel<true, 16>), g, b, pl.fused_lds, stream, s, sa);
     } else {
       const dim3 g(pl.chunks, rows), b(256);
       if (H_I <= 8)

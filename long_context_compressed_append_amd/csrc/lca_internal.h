@@ -20,6 +20,19 @@ enum KernelId {
   kKernelCount = 5
 };
 
+// Kernel-choice overrides (lca_set_tuning / the LCA_* environment at load);
+// tuning(id) < 0 means automatic.
+enum TuneId {
+  kTuneScoreTile = 0,
+  kTuneTopkCand,
+  kTuneTopkSliced,
+  kTuneTopkFused,
+  kTuneScoreCpw,
+  kTuneAttendSplits,
+  kTuneCount
+};
+int tuning(TuneId id);
+
 // Records HIP events around one launch when a timing session for `id` is open.
 struct TimedLaunch {
   TimedLaunch(KernelId id, hipStream_t s);
@@ -33,31 +46,32 @@ int set_error(int code, const char* fmt, ...);
 int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
                     const float* igate, int n, hipStream_t stream);
 
-// Indexer workspace: per-query key histograms [rows][4096] (zero between
-// calls), then scores as order-preserving uint32 keys [rows][stride], then,
-// when the selection is split over rounds, the per-(query, round) listed-key
-// counts, bitmap words and lists.  rows = B * n_q.
+// Indexer workspace (byte offsets in the plan): the fused selection's per-row
+// arrival counters and the per-query key histograms [rows][4096] first --
+// [0, zero_bytes) is zero on entry and on return -- then the scores: order
+// keys [rows][stride], or (key, t) / (key, block) pairs [rows][stride] for
+// candidate lists; then, when the selection is split over parts, the
+// per-(query, part) listed-key counts, bitmap words and lists; then the
+// candidate list lengths.  rows = B * n_q.
 struct IndexerPlan {
-  int64_t stride;       // keys per score row (>= visible blocks of any query)
-  int chunks;           // workgroups per score row
-  int cpw;              // chunks of 1024 blocks per workgroup
+  int64_t stride;       // key slots per score row (>= visible blocks of any query)
+  int chunks;           // score workgroups per row (non-fused decode kernel, tile kernel)
+  int cpw;              // chunks of 1024 blocks per workgroup (per half-workgroup when fused)
   int slices;           // selection parts per query on their own workgroups (0: one workgroup)
   int tile;             // 0: one query per score workgroup; 8 or 4: queries per wavefront of the tile kernel
   int qgroups;          // tile kernel: query groups per row
-  size_t keys_bytes;
-  size_t hist_bytes;    // per-query histograms at the start of the workspace
-  size_t part_count_bytes, part_bits_bytes, part_cand_bytes;
-  bool cand;            // tile kernel keeps candidate lists: (key, visit) pairs, list lengths at the end
+  bool cand;            // tile kernel keeps candidate lists: (key, visit) pairs
   int cand_lists;       // lists per query: chunks x cand_waves x 32
   int cand_waves;       // wavefronts per tile workgroup
   int cand_span;        // blocks per chunk
-  size_t cand_count_bytes;
-  bool fused;           // decode scoring selects in its own launch (per-row counters at the end)
-  size_t row_done_bytes;
-  size_t total() const {
-    return hist_bytes + keys_bytes + part_count_bytes + part_bits_bytes + part_cand_bytes + cand_count_bytes +
-           row_done_bytes;
-  }
+  bool fused;           // decode scoring selects in its own launch from per-workgroup candidates
+  int fused_wgs;        // fused: scoring workgroups per row (candidate segments)
+  int fused_span;       // fused: blocks per scoring workgroup
+  size_t fused_lds;     // fused: dynamic LDS bytes (keys, then the selection bitmap)
+  size_t off_done, off_hist, off_keys, off_part_count, off_part_bits, off_part_cand, off_cand_count;
+  size_t zero_bytes;    // [0, zero_bytes): counters and histograms, zero between calls
+  size_t total_bytes;
+  size_t total() const { return total_bytes; }
 };
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
 // argument checks of lca_indexer_topk (everything but the workspace)

@@ -8,8 +8,8 @@
 // ends; its address is looked up once per device (hipGetSymbolAddress, with
 // that device current) and passed to the kernels as a pointer.  Every call
 // on a GPU shares that copy, so calls that overlap on one GPU race; the
-// histograms are cleared by a fill kernel at the start of every call (a
-// kernel, not a memset, so the call stays capturable).
+// counters and histograms are cleared by a fill kernel at the start of every
+// call (a kernel, not a memset, so the call stays capturable).
 #include <mutex>
 
 #include "lca_device.h"
@@ -66,8 +66,9 @@ extern "C" int lca_indexer_topk_noalloc(const lca_layer* L, const float* iq, con
   if (rc) return rc;
   rc = indexer_validate(L, iq, iw, n_q, H_I, k, topk);
   if (rc) return rc;
-  // histograms start at zero: clear the first hist_bytes (a multiple of 16)
-  const int64_t n16 = (int64_t)(pl.hist_bytes / 16);
+  // counters and histograms start at zero: clear the first zero_bytes (a
+  // multiple of 16)
+  const int64_t n16 = (int64_t)(pl.zero_bytes / 16);
   const int blocks = (int)(n16 / 256 < 1024 ? (n16 + 255) / 256 : 1024);
   hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
                      static_cast<uint4*>(ws), n16);

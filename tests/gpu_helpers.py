@@ -148,10 +148,26 @@ def indexer_row_keys(ws, layout, row, nv):
     lca.indexer_layout)."""
     import torch
     S = layout["stride"]
-    if not layout["cand"]:
+    if layout["kind"] == 0:
         k0 = layout["keys"] + row * S * 4
         keys = ws[k0:k0 + S * 4].view(torch.int32).cpu().numpy().view(np.uint32)
         return np.arange(nv), keys[:nv]
+    if layout["kind"] == 2:
+        # per-workgroup segments of (key, block) pairs: segment s at slot s * span
+        k0 = layout["keys"] + row * S * 8
+        pairs = ws[k0:k0 + S * 8].view(torch.int32).cpu().numpy().view(np.uint32).reshape(S, 2)
+        segs, span = layout["lists"], layout["span"]
+        c0 = layout["counts"] + row * segs * 4
+        cnt = ws[c0:c0 + segs * 4].view(torch.int32).cpu().numpy().astype(np.int64)
+        assert (cnt <= span).all()
+        idx = np.concatenate([s_ * span + np.arange(c) for s_, c in enumerate(cnt)]).astype(np.int64) \
+            if cnt.sum() else np.zeros(0, np.int64)
+        e = pairs[idx]
+        blocks = e[:, 1].astype(np.int64)
+        # each segment holds blocks of its own range, in ascending order
+        seg_of = np.repeat(np.arange(segs), cnt)
+        assert ((blocks // span) == seg_of).all()
+        return blocks, e[:, 0]
     k0 = layout["keys"] + row * S * 8
     pairs = ws[k0:k0 + S * 8].view(torch.int32).cpu().numpy().view(np.uint32).reshape(S, 2)
     lists, W, span = layout["lists"], layout["waves"], layout["span"]

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version():
     L = _lib()
-    assert L.lca_abi_version() == 1
+    assert L.lca_abi_version() == 2
 
 
 def _layer(**kw):
@@ -105,19 +105,33 @@ def test_workspace_queries_are_pure():
 
 
 def test_indexer_layout_matches_the_workspace():
-    """The layout query (host only): full key rows for a decode query, candidate
-    lists for a prefill chunk, every region inside the workspace size."""
+    """The layout query (host only): candidate segments for a decode query
+    (the selection in the scoring launch), full key rows when the separate
+    selection is forced, candidate lists for a prefill chunk, every region
+    inside the workspace size."""
     L = _lib()
     L.lca_indexer_workspace.restype = C.c_size_t
     L.lca_indexer_layout.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
+    L.lca_set_tuning.argtypes = [C.c_char_p, C.c_int32]
     out = (C.c_int64 * 8)()
-    # decode: one query per row, full key rows
+    # decode: one query per row, per-workgroup candidate segments
     s = _layer(batch=4, len_min=131072, len_max=131072, max_blocks=33000, has_indexer=1)
     assert L.lca_indexer_layout(C.byref(s), 1, 16, 512, out) == 0
-    stride, keys, cand = out[0], out[1], out[2]
-    assert stride >= 32768 and stride % 64 == 0 and cand == 0
-    assert keys == 4 * 4096 * 4                       # after the per-query histograms
-    assert keys + 4 * stride * 4 <= L.lca_indexer_workspace(C.byref(s), 1, 16, 512)
+    stride, keys, kind, zero, counts, segs, span = out[0], out[1], out[2], out[3], out[4], out[5], out[7]
+    assert stride >= 32768 and stride % 64 == 0 and kind == 2
+    assert zero == keys and zero >= 4 * 4096 * 4 + 4 * 4  # row counters, then the histograms
+    assert segs * span >= 32768 and span % 1024 == 0
+    total = L.lca_indexer_workspace(C.byref(s), 1, 16, 512)
+    assert keys + 4 * stride * 8 <= counts and counts + 4 * segs * 4 <= total
+    # the same with the separate selection: full key rows after the histograms
+    assert L.lca_set_tuning(b"LCA_TOPK_FUSED", 0) == 0
+    try:
+        assert L.lca_indexer_layout(C.byref(s), 1, 16, 512, out) == 0
+        stride, keys, kind, zero = out[0], out[1], out[2], out[3]
+        assert kind == 0 and keys == zero == 4 * 4096 * 4
+        assert keys + 4 * stride * 4 <= L.lca_indexer_workspace(C.byref(s), 1, 16, 512)
+    finally:
+        L.lca_set_tuning(b"LCA_TOPK_FUSED", -1)
     # prefill chunk: 4096 queries in one row, candidate lists
     s = _layer(batch=1, len_min=266240, len_max=266240, max_blocks=66624, has_indexer=1)
     n_q = 4096
@@ -132,3 +146,16 @@ def test_indexer_layout_matches_the_workspace():
     # errors
     assert L.lca_indexer_layout(C.byref(s), 0, 16, 512, out) == -1
     assert L.lca_indexer_layout(C.byref(s), 1, 16, 512, None) == -1
+
+
+def test_set_tuning_names():
+    L = _lib()
+    L.lca_set_tuning.argtypes = [C.c_char_p, C.c_int32]
+    L.lca_last_error.restype = C.c_char_p
+    for name in ("LCA_SCORE_TILE", "LCA_TOPK_CAND", "LCA_TOPK_SLICED", "LCA_TOPK_FUSED", "LCA_SCORE_CPW",
+                 "LCA_ATTEND_SPLITS"):
+        assert L.lca_set_tuning(name.encode(), 1) == 0
+        assert L.lca_set_tuning(name.encode(), -1) == 0       # back to automatic
+    assert L.lca_set_tuning(b"LCA_NO_SUCH_KNOB", 1) == -1
+    assert b"unknown" in L.lca_last_error()
+    assert L.lca_set_tuning(None, 1) == -1

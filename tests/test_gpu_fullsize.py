@@ -55,7 +55,7 @@ def _score_keys(lay, lca, n_q, H_I, k):
     """the indexer's workspace and its layout; the histograms must be zero"""
     ws = lay.indexer_workspace(n_q)
     layout = lca.indexer_layout(lay, n_q, H_I, k)
-    assert not ws[:layout["keys"]].view(torch.int32).any().item()     # histograms left zeroed
+    assert not ws[:layout["zero"]].view(torch.int32).any().item()     # counters, histograms left zeroed
     return ws, layout
 
 

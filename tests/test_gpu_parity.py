@@ -159,7 +159,7 @@ INDEXER_MODES = {"auto": {}, "sliced": {"LCA_TOPK_SLICED": "1"}, "tile": {"LCA_S
                  "tile_cand": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "1"},
                  "tile_full": {"LCA_SCORE_TILE": "1", "LCA_TOPK_CAND": "0"},
                  "no_tile": {"LCA_SCORE_TILE": "0"},
-                 "fused": {"LCA_TOPK_FUSED": "1", "LCA_TOPK_SLICED": "0"}}
+                 "separate": {"LCA_TOPK_FUSED": "0", "LCA_TOPK_SLICED": "0"}}
 
 # oracle results per case, shared by the modes
 _ORACLE = {}
@@ -181,7 +181,7 @@ def _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed, wsign="abs"):
 
 @pytest.mark.parametrize("mode", list(INDEXER_MODES))
 @pytest.mark.parametrize("case", INDEXER_CASES, ids=[c[0] for c in INDEXER_CASES])
-def test_indexer_topk_parity(case, mode, monkeypatch):
+def test_indexer_topk_parity(case, mode, tuning):
     lca = _lca()
     name, B, lens, n_q, H_I, k, needles = case[:7]
     wsign = case[7] if len(case) > 7 else "abs"
@@ -189,7 +189,7 @@ def test_indexer_topk_parity(case, mode, monkeypatch):
     say("indexer", name, "B", B, "lens", lens, "n_q", n_q, "H_I", H_I, "k", k, "seed", seed, "mode", mode,
         "weights", wsign)
     for var, val in INDEXER_MODES[mode].items():
-        monkeypatch.setenv(var, val)
+        tuning(var, val)
     ref, lay, Q = _indexer_case(lca, name, B, lens, n_q, H_I, k, needles, seed, wsign)
     got = lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
     torch.cuda.synchronize()
@@ -203,8 +203,8 @@ def test_indexer_topk_parity(case, mode, monkeypatch):
     # of every block that can reach the top k (candidate lists)
     ws = lay.indexer_workspace(n_q)
     layout = lca.indexer_layout(lay, n_q, H_I, k)
-    hist_words = B * n_q * 4096
-    assert not ws[:hist_words * 4].view(torch.int32).any().item()   # histograms left zeroed for the next call
+    assert layout["zero"] >= B * n_q * 4096 * 4
+    assert not ws[:layout["zero"]].view(torch.int32).any().item()   # counters, histograms zeroed for the next call
     for b in range(B):
         for qi in range(n_q):
             sc = scores[b][qi]
@@ -237,16 +237,16 @@ def test_indexer_prefill_decode_prefill_one_layer():
                 check_topk(got[b, qi], want[b, qi], oracle.indexer_scores(ref, b, qi, n_q, Q["iq"], Q["iw"]), k)
 
 
-TIE_MODES = ["auto", "sliced", "tile_cand", "fused"]
+TIE_MODES = ["auto", "sliced", "tile_cand", "separate"]
 
 
 @pytest.mark.parametrize("mode", TIE_MODES)
 @pytest.mark.parametrize("B,L", [(1, 4000), (2, 140000)], ids=["short", "long"])
-def test_indexer_equal_scores_take_lowest_indices(B, L, mode, monkeypatch):
+def test_indexer_equal_scores_take_lowest_indices(B, L, mode, tuning):
     lca = _lca()
     say("indexer equal scores", B, L, "mode", mode)
     for var, val in INDEXER_MODES[mode].items():
-        monkeypatch.setenv(var, val)
+        tuning(var, val)
     m, k = 4, 50
     ref = SL.make_layer(77, "eq", B, m, 128, 256, 1, L // m + 4, [L] * B)
     ref["idx_code"][:] = 0x22          # every key identical
@@ -262,13 +262,13 @@ def test_indexer_equal_scores_take_lowest_indices(B, L, mode, monkeypatch):
 
 @pytest.mark.parametrize("mode", TIE_MODES)
 @pytest.mark.parametrize("L", [48000, 140000], ids=["one_round", "two_rounds"])
-def test_indexer_near_equal_scores(L, mode, monkeypatch):
+def test_indexer_near_equal_scores(L, mode, tuning):
     """Most scores share their high bits (keys differ in one byte): exercises
     the second-level candidate selection."""
     lca = _lca()
     say("indexer near-equal scores", L, "mode", mode)
     for var, val in INDEXER_MODES[mode].items():
-        monkeypatch.setenv(var, val)
+        tuning(var, val)
     B, m, k = 2, 4, 512
     ref = SL.make_layer(78, "neq", B, m, 128, 256, 1, L // m + 4, [L, L - 7])
     rng = np.random.default_rng(78)
@@ -285,7 +285,7 @@ def test_indexer_near_equal_scores(L, mode, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", ["tile", "tile_full", "no_tile"])
-def test_indexer_exponent_extremes(mode, monkeypatch):
+def test_indexer_exponent_extremes(mode, tuning):
     """Key halves with E8M0 scales up to 12 apart and query halves scaled by
     2^20 or 2^-12: the products of the two MX halves can no longer be added
     inside one matrix-core product without rounding, so the per-half path
@@ -294,7 +294,7 @@ def test_indexer_exponent_extremes(mode, monkeypatch):
     lca = _lca()
     say("indexer exponent extremes", mode)
     for var, val in INDEXER_MODES[mode].items():
-        monkeypatch.setenv(var, val)
+        tuning(var, val)
     B, m, L, n_q, H_I, k = 2, 4, 6000, 24, 16, 100
     ref = SL.make_layer(79, "ext", B, m, 128, 256, 1, L // m + 4, [L, L - 3])
     rng = np.random.default_rng(79)
@@ -316,18 +316,18 @@ def test_indexer_exponent_extremes(mode, monkeypatch):
 _MAX_CASE = {}
 
 
-@pytest.mark.parametrize("mode", ["auto", "single", "fused"])
-def test_indexer_max_blocks(mode, monkeypatch):
+@pytest.mark.parametrize("mode", ["auto", "single", "sliced"])
+def test_indexer_max_blocks(mode, tuning):
     """The longest row the indexer takes: 524 288 blocks (2^21 tokens at
-    m = 4), which fills the whole selection bitmap: 16 rounds of the single
-    workgroup, 32 part workgroups of the sliced selection (taken by default
-    for one such row), or the selection inside the scoring launch."""
+    m = 4), which fills the whole selection bitmap: the selection inside the
+    scoring launch (the default: 256 candidate segments), 16 rounds of the
+    single selection workgroup, or 32 part workgroups of the sliced one."""
     lca = _lca()
     say("indexer max blocks", mode)
-    env = {"auto": {}, "single": {"LCA_TOPK_SLICED": "0"},
-           "fused": {"LCA_TOPK_SLICED": "0", "LCA_TOPK_FUSED": "1"}}[mode]
+    env = {"auto": {}, "single": {"LCA_TOPK_SLICED": "0", "LCA_TOPK_FUSED": "0"},
+           "sliced": {"LCA_TOPK_SLICED": "1"}}[mode]
     for var, val in env.items():
-        monkeypatch.setenv(var, val)
+        tuning(var, val)
     B, m, k, H_I, MB = 1, 4, 256, 8, 524288
     if not _MAX_CASE:
         ref = SL.make_layer(80, "max", B, m, 128, 256, 1, MB, [MB * m])
@@ -364,14 +364,14 @@ ATTEND_CASES = [
 
 
 @pytest.mark.parametrize("case", ATTEND_CASES, ids=[c[0] for c in ATTEND_CASES])
-def test_attend_parity(case, monkeypatch):
+def test_attend_parity(case, tuning):
     lca = _lca()
     name, csa, B, lens, n_q, H, k, splits = case
     seed = 4000 + len(name) * 7 + csa
     say("attend", name, "csa", csa, "B", B, "lens", lens, "n_q", n_q, "H", H, "k", k,
         "splits", splits, "seed", seed)
     if splits:
-        monkeypatch.setenv("LCA_ATTEND_SPLITS", str(splits))
+        tuning("LCA_ATTEND_SPLITS", splits)
     m = 4 if csa else 128
     W = 128
     MB = max(lens) // m + 8
