@@ -61,6 +61,37 @@ enum {
   LCA_EHIP = -5           /* a HIP runtime call failed                        */
 };
 
+/*
+ * Status bits of layer.sync[1], set by the device when a call could not do
+ * its work exactly (the call itself returned LCA_OK: the condition depends
+ * on device data, e.g. lengths that grew inside a replayed graph):
+ *   LCA_STATUS_COMPRESS_CAPACITY  a block to finalise lay at or past
+ *                                 max_blocks; it was not written
+ *   LCA_STATUS_INDEXER_CAPACITY   a query saw more blocks than the call's
+ *                                 plan holds (planned from len_max); the
+ *                                 newest ones were not scored
+ *   LCA_STATUS_ATTEND_CAPACITY    a query's key list was longer than the
+ *                                 call's plan (from len_max); its last keys
+ *                                 (the newest window tokens) were dropped
+ *   LCA_STATUS_FP16_RANGE         attention met an input its fp16 images
+ *                                 may not hold to 2^-11 of the vector's
+ *                                 largest magnitude: a query head, RoPE
+ *                                 group or 64-channel window group whose
+ *                                 largest magnitude is 65536 or more (also
+ *                                 inf, NaN) or nonzero and below 2^-14; or
+ *                                 an FP8 group scale outside [2^-14, 2^8),
+ *                                 where the scaled probabilities leave
+ *                                 fp16's normal range.  The result may miss
+ *                                 the 2e-3 bound
+ * Calls captured in a graph must be planned with len_max set to the longest
+ * length they will reach (set the host mirror before capture); the capacity
+ * bits report replays that went beyond it.
+ */
+#define LCA_STATUS_COMPRESS_CAPACITY 1u
+#define LCA_STATUS_INDEXER_CAPACITY 2u
+#define LCA_STATUS_ATTEND_CAPACITY 4u
+#define LCA_STATUS_FP16_RANGE 8u
+
 #define LCA_KV_DIM 512
 #define LCA_NOPE_DIM 448
 #define LCA_ROPE_DIM 64
@@ -74,8 +105,12 @@ enum {
  *
  * Planes (B = batch rows, MB = max_blocks, R = ring, m = ratio):
  *   seq_len    int32   [B]            tokens appended so far, per row (device)
- *   sync       uint32  [1]            zero when created; the library keeps it 0
- *                                     between calls (a completion counter)
+ *   sync       uint32  [2]            zero when created.  sync[0]: a completion
+ *                                     counter the library keeps 0 between
+ *                                     calls.  sync[1]: status bits (LCA_STATUS_*)
+ *                                     that kernels set and never clear; the
+ *                                     caller reads (and may reset) them after
+ *                                     its work has run
  *   nope       uint8   [B][MB][448]   e4m3fn codes of entry dims 0..447
  *   rope       uint16  [B][MB][64]    bf16 entry dims 448..511
  *   kv_scale   float   [B][MB][8]     fp32 scale of each 64-dim FP8 group

@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "liblca.so")
 KV, NOPE, ROPE, IDX = 512, 448, 64, 64
 ERRORS = {0: "LCA_OK", -1: "LCA_EINVAL", -2: "LCA_EUNSUPPORTED", -3: "LCA_ECAPACITY",
           -4: "LCA_EWORKSPACE", -5: "LCA_EHIP"}
+STATUS_COMPRESS_CAPACITY, STATUS_INDEXER_CAPACITY, STATUS_ATTEND_CAPACITY, STATUS_FP16_RANGE = 1, 2, 4, 8
 
 
 class LcaError(RuntimeError):
@@ -182,6 +183,15 @@ class Layer:
         out["pos_bias"] = self.pos_bias.cpu().numpy()
         out["ipos_bias"] = self.ipos_bias.cpu().numpy() if self.ipos_bias is not None else None
         return out
+
+    def status(self):
+        """The layer's status bits (LCA_STATUS_*: 1 compressor capacity,
+        2 indexer capacity, 4 attention capacity, 8 fp16 range), as left by
+        the work the stream has run so far."""
+        return int(self.sync[1].item()) & 0xFFFFFFFF
+
+    def clear_status(self):
+        self.sync[1].zero_()
 
     def set_lengths(self, lengths):
         lengths = torch.as_tensor(lengths, dtype=torch.int32)

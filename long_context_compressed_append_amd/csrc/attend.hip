@@ -17,8 +17,14 @@
 // other, so the loads and conversions leave the critical path.
 // A staged key is one fp16 image serving as K and as V: the exact value of
 // each e4m3 code (e4m3 values are fp16 numbers), or the bf16 RoPE / window
-// value (exact within fp16's normal range).  The query is converted to fp16
-// the same way.  Every product is computed transposed, keys x heads, so that
+// value (exact in fp16's normal range [2^-14, 65504], below it rounded to
+// fp16's subnormal spacing 2^-24).  The query is converted to fp16 the same
+// way, so each image is within 2^-11 of its vector's largest magnitude when
+// that lies in [2^-14, 65504].  LCA_STATUS_FP16_RANGE in the layer's status
+// word reports an input where this may fail: a query head or a 64-channel
+// key group (RoPE, or window channels) whose largest magnitude is 65536 or
+// more (also inf, NaN) or nonzero and below 2^-14, or an FP8 group scale
+// outside [2^-14, 2^8) (where P * scale leaves fp16's normal range).  Every product is computed transposed, keys x heads, so that
 // a lane owns one head throughout: lane l holds head l % 16 and key / channel
 // quarter l / 16.
 //   S^T = K Q^T   fp16 matrix cores over the 512 channels; the per-64-dim
@@ -70,6 +76,7 @@ struct AttendArgs {
   float* out;
   float* ws_ml;
   _Float16* ws_o;
+  uint32_t* status;      // the layer's status word (LCA_STATUS_* bits)
 };
 
 constexpr int kComputeWaves = 4;   // 4 head wavefronts of 16 heads, all channels
@@ -103,15 +110,27 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int g = lane >> 4;                    // this lane's key / channel quarter
   const int kq = 8 * g;                       // K offset of this lane inside a 32-K step
 
+  // range_ok turns false on an input the fp16 images may not hold to 2^-11
+  // of their vector's largest magnitude (reported through the status word):
+  // a query head or a 64-channel key group whose largest magnitude is 65536
+  // or more (also inf, NaN), or nonzero and below 2^-14; an FP8 scale
+  // outside [2^-14, 2^8)
+  bool range_ok = true;
   v8h qf[16];  // q of this lane's head (fp16 image of the bf16 input), channels 32 ks + 8 g .. +7
   {
     const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv;
+    uint32_t qmx = 0;
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (active && hq < a.H) v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + kq);
       qf[ks] = bf16x8_to_f16(v);
+      qmx = bf16x8_absmax(v, qmx);
     }
+    // over the head's four lanes l, l ^ 16, l ^ 32, l ^ 48
+    qmx = max(qmx, __float_as_uint(swap_rows(__uint_as_float(qmx))));
+    qmx = max(qmx, __float_as_uint(swap_halves(__uint_as_float(qmx))));
+    range_ok = qmx == 0 || (qmx >= kBf16MinNormalF16 && qmx < kBf16F16Overflow);
   }
 
   const int p = a.seq_len[brow] - a.n_q + qi;
@@ -125,6 +144,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int n_keys = n_c + nw;
   const int kb = split * a.chunk;
   const int ke = min(n_keys, kb + a.chunk);
+  if (split == a.splits - 1 && n_keys > ke && tid == 0)   // more keys than the plan holds
+    atomicOr(a.status, LCA_STATUS_ATTEND_CAPACITY);
   if (a.csa) {
     for (int j = tid; j < a.chunk; j += kThreads) {
       const int kk = kb + j;
@@ -187,7 +208,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // normal range; then the group scale and the key mask.
   auto stage_store = [&](const StageRegs& st, int sg, int buf) {
     uint4* tdst = reinterpret_cast<uint4*>(Ts[buf] + sj * kVst + sg * 64 + sp * 32);
+    uint32_t gmx = 0;
     if (st.kind == 1) {
+      range_ok &= st.s == 0.0f || (st.s >= 6.103515625e-05f && st.s < 256.0f);   // [2^-14, 2^8)
 #pragma unroll
       for (int v = 0; v < 2; v++) {
         const uint32_t w4[4] = {st.d[v].x, st.d[v].y, st.d[v].z, st.d[v].w};
@@ -207,10 +230,23 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       }
     } else if (st.kind >= 2) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) tdst[v] = __builtin_bit_cast(uint4, bf16x8_to_f16(st.d[v]));
+      for (int v = 0; v < 4; v++) {
+        const v8h h = bf16x8_to_f16(st.d[v]);
+        gmx = bf16x8_absmax(st.d[v], gmx);
+        tdst[v] = __builtin_bit_cast(uint4, h);
+      }
     } else {
 #pragma unroll
       for (int v = 0; v < 4; v++) tdst[v] = make_uint4(0, 0, 0, 0);
+    }
+    // this lane holds half of a 64-channel group, lane l ^ 32 the other half;
+    // a small group is reported by a lane whose half is nonzero (every lane
+    // of the wavefront is here, and rarely any lane's half is small)
+    range_ok &= gmx < kBf16F16Overflow;
+    const bool small = gmx != 0 && gmx < kBf16MinNormalF16;
+    if (__builtin_amdgcn_ballot_w64(small)) {
+      const uint32_t other = __float_as_uint(swap_halves(__uint_as_float(gmx)));
+      range_ok &= !(small && other < kBf16MinNormalF16);
     }
     if (sp == 0) sK[buf][sg * kTile + sj] = st.kind == 1 ? st.s : (st.kind ? 1.0f : 0.0f);
     // a key is valid when its first group is (every group of a key shares it)
@@ -257,6 +293,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       }
       __syncthreads();                     // tile t + 1 staged, tile t consumed
     }
+    if (__any(!range_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_FP16_RANGE);
     return;
   }
   __syncthreads();                         // tile 0 staged
@@ -368,6 +405,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     __syncthreads();                       // tile t + 1 staged, tile t consumed
   }
 
+  if (__any(!range_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_FP16_RANGE);
   if (!active) return;
   lrow += swap_rows(lrow);
   lrow += swap_halves(lrow);
@@ -520,6 +558,7 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   a.out = out;
   a.ws_ml = static_cast<float*>(ws);
   a.ws_o = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + ((pl.ml_bytes + 255) & ~(size_t)255));
+  a.status = L->sync + 1;
   const int rows = L->batch * n_q;
   {
     TimedLaunch t(kKernelAttend, stream);

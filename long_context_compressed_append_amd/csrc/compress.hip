@@ -197,7 +197,10 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     const int row = (int)(f / a.nfin);
     const int L0 = a.seq_len[row];
     const int64_t bk = (int64_t)(L0 / a.m) + s;
-    if ((bk + 1) * a.m <= (int64_t)L0 + a.n) {      // block completes in this call
+    const bool completes = (bk + 1) * a.m <= (int64_t)L0 + a.n;
+    if (completes && bk >= a.max_blocks) {           // past the cache (a replay beyond its plan)
+      if (lane == 0) atomicOr(a.sync + 1, LCA_STATUS_COMPRESS_CAPACITY);
+    } else if (completes) {                          // block completes in this call
       const int64_t e = (int64_t)row * a.max_blocks + bk;
       if (g < 8) {
         const int c = g * 64 + lane;

@@ -89,6 +89,7 @@ struct ScoreArgs {
   uint32_t* cand_count;
   uint32_t* row_done;    // fused selection: workgroups of a row done, [rows], zero between calls
   int fused_span;        // fused selection: blocks per scoring workgroup (its candidate segment)
+  uint32_t* status;      // the layer's status word (LCA_STATUS_* bits)
 };
 
 // max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
@@ -232,6 +233,7 @@ struct SelectArgs {
   const uint32_t* keys;
   uint32_t* hist;
   int32_t* topk;
+  uint32_t* status;      // the layer's status word
   // sliced path: per (query, round) bitmap words [rows][slices][1024], listed
   // key counts [rows][slices] and lists [rows][slices][2][kCandCap]
   int slices;
@@ -329,7 +331,10 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   typedef const int32_t __attribute__((address_space(4)))* const_i32p;
   const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
   int nv = (p + 1) / a.m;
-  if (nv > cap) nv = cap;                      // defensive: never past the key row
+  if (nv > cap) {                              // more blocks than the plan holds
+    if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
+    nv = cap;
+  }
 
   for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
   // MXFP4 quantisation of the query, one 32-lane half-wave per MX block
@@ -723,7 +728,10 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
     const int q = q0 + set * kQw + u;
     const int p = len - a.n_q + q;
     int nv = q < a.n_q ? (p + 1) / a.m : 0;
-    if (nv > cap) nv = cap;
+    if (nv > cap) {                            // more blocks than the plan holds
+      if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
+      nv = cap;
+    }
     nvq[u] = nv;
     nv_hi = nv > nv_hi ? nv : nv_hi;
   }
@@ -1304,7 +1312,10 @@ __device__ __forceinline__ int visible_blocks(const SelectArgs& a, int srow) {
   typedef const int32_t __attribute__((address_space(4)))* const_i32p;
   const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
   int nv = (p + 1) / a.m;
-  if (nv > a.stride) nv = (int)a.stride;       // defensive: never past the key row
+  if (nv > a.stride) {                         // more blocks than the plan holds
+    if (threadIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
+    nv = (int)a.stride;
+  }
   return nv;
 }
 
@@ -2244,6 +2255,7 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.cand_count = (pl.cand || pl.fused) ? reinterpret_cast<uint32_t*>(base + pl.off_cand_count) : nullptr;
   s.row_done = pl.fused ? reinterpret_cast<uint32_t*>(base + pl.off_done) : nullptr;
   s.fused_span = pl.fused_span;
+  s.status = L->sync + 1;
   SelectArgs sa;
   sa.n_q = n_q;
   sa.m = L->ratio;
@@ -2253,6 +2265,7 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   sa.keys = s.keys;
   sa.hist = s.hist;
   sa.topk = topk;
+  sa.status = s.status;
   sa.slices = pl.slices;
   sa.part_count = reinterpret_cast<uint32_t*>(base + pl.off_part_count);
   sa.part_bits = reinterpret_cast<uint32_t*>(base + pl.off_part_bits);

@@ -171,6 +171,21 @@ __device__ __forceinline__ v8h_t bf16x8_to_f16(uint4 w) {
   return r;
 }
 
+// Largest magnitude of eight bf16 values w folded into mx, as bf16
+// magnitude bits (ordered like the magnitudes; inf and NaN above every
+// finite value).  fp16 holds a vector of bf16 values to 2^-11 of its largest
+// magnitude when that lies in [2^-14, 65504]: values in fp16's normal range
+// convert exactly, smaller ones lose at most 2^-25 to fp16's subnormal
+// spacing 2^-24.
+__device__ __forceinline__ uint32_t bf16x8_absmax(uint4 w, uint32_t mx) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) mx = max(mx, max(ww[i] & 0x7FFFu, (ww[i] >> 16) & 0x7FFFu));
+  return mx;
+}
+constexpr uint32_t kBf16F16Overflow = 0x4780u;    // 65536: the first bf16 magnitude above 65504
+constexpr uint32_t kBf16MinNormalF16 = 0x3880u;   // 2^-14
+
 __device__ __forceinline__ uint32_t ord_key(float s) {
   // negative: every bit flipped; otherwise the sign bit set (one xor with
   // the sign spread over the word, sign bit forced)

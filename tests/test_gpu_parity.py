@@ -216,6 +216,7 @@ def test_indexer_topk_parity(case, mode, tuning):
             nd = SL.plant_needles(ref, seed, name, b, needles, Q["iq"][b, -1], Q["iw"][b, -1],
                                   Q["q"][b, -1])
             assert set(nd) <= set(got[b, -1].tolist())
+    assert lay.status() == 0
 
 
 def test_indexer_prefill_decode_prefill_one_layer():
@@ -402,6 +403,7 @@ def test_attend_parity(case, tuning):
     err = attn_rel_err(got.cpu().numpy(), want)
     print("max rel err", err)
     assert err <= ATTN_TOL
+    assert lay.status() == 0
     # the same call twice gives bitwise-identical output (no races in LDS)
     again = (lca.csa_attend(lay, q, _dev(topk), float(SCALE)) if csa
              else lca.hca_attend(lay, q, float(SCALE)))
@@ -586,3 +588,135 @@ def test_ratio1_csa_and_window_only(n_q):
     got = lca.csa_attend(lay, _dev(Q["q"]), _dev(none), float(SCALE))
     torch.cuda.synchronize()
     assert attn_rel_err(got.cpu().numpy(), oracle.csa_attend(ref, Q["q"], none, SCALE)) <= ATTN_TOL
+
+
+# ------------------------------------------------------------------ status word
+
+def _range_layer(lca, csa, seed):
+    B, L, W = 2, 3000, 128
+    m = 4 if csa else 128
+    ref = SL.make_layer(seed, "rng", B, m, W, 256, int(csa), L // m + 8, [L, L - 5])
+    return ref
+
+
+FP16_RANGE_CASES = {   # case -> whether it sets LCA_STATUS_FP16_RANGE
+    "none": False, "edges": False, "q_subnormal": False, "window_subnormal": False, "q_zero_head": False,
+    "q_big": True, "q_tiny_head": True, "window_big": True, "window_tiny_group": True,
+    "rope_big": True, "rope_tiny_group": True, "scale_big": True, "scale_small": True}
+
+
+def _tiny_bits(seed, n):
+    """bf16 bits of n values ~N(0,1) * 2^-20, all below 2^-14, some of which
+    fp16 rounds (bits below its subnormal spacing 2^-24)."""
+    v = synth.bf16_to_f32(synth.bf16_normal(seed, "tiny", (n,), "rng")) * np.float32(2.0 ** -20)
+    bits = synth.bf16_bits(v)
+    f = synth.bf16_to_f32(bits)
+    assert np.abs(f).max() < 2.0 ** -14
+    assert (f.astype(np.float16).astype(np.float32) != f).any()
+    return bits
+
+
+@pytest.mark.parametrize("what", list(FP16_RANGE_CASES))
+@pytest.mark.parametrize("csa", [0, 1], ids=["hca", "csa"])
+def test_attend_fp16_range_reported(what, csa):
+    """Inputs the fp16 images may not hold to 2^-11 of their vector's largest
+    magnitude set LCA_STATUS_FP16_RANGE: a query head or a 64-channel key
+    group whose largest magnitude is above 65504 or nonzero and below 2^-14,
+    FP8 scales outside [2^-14, 2^8).  In-range inputs leave the word clear:
+    fp16's exact edges (65280, 2^-24, scales 2^-14 and just below 2^8), a
+    value below fp16's subnormal spacing inside a vector of ordinary
+    magnitude, an all-zero query head."""
+    lca = _lca()
+    say("attend fp16 range", what, "csa", csa)
+    ref = _range_layer(lca, csa, 6200 + csa)
+    Q = SL.queries(6200, "rng", 2, 1, 16)
+    q = Q["q"].copy()
+    m = ref["ratio"]
+    p = int(ref["seq_len"][0]) - 1
+    slot = p % ref["ring"]
+    slot1 = (int(ref["seq_len"][1]) - 4) % ref["ring"]     # inside row 1's window
+    b_last = (p + 1) // m - 1
+    f32 = lambda v: synth.bf16_bits(np.array([v], np.float32))[0]
+    if what == "q_big":
+        q[0, 0, 3, 17] = f32(70144.0)
+    elif what == "q_subnormal":
+        q[1, 0, 0, 5] = f32(3e-8)              # below fp16's smallest subnormal 2^-24
+    elif what == "q_zero_head":
+        q[0, 0, 5, :] = 0
+    elif what == "q_tiny_head":
+        q[1, 0, 2, :] = _tiny_bits(1, 512)
+    elif what == "window_big":
+        ref["ring_kv"][0, slot, 100] = f32(-1.0e5)
+    elif what == "window_subnormal":
+        ref["ring_kv"][1, slot1, 480] = f32(1.5 * 2.0 ** -25)
+    elif what == "window_tiny_group":
+        ref["ring_kv"][1, slot1, 128:192] = _tiny_bits(2, 64)
+    elif what == "rope_big":
+        ref["rope"][0, b_last, 7] = f32(2.0 ** 17)
+    elif what == "rope_tiny_group":
+        ref["rope"][0, b_last, :] = _tiny_bits(3, 64)
+    elif what == "scale_big":
+        ref["kv_scale"][0, b_last, 2] = np.float32(300.0)
+    elif what == "scale_small":
+        ref["kv_scale"][1, 3, 0] = np.float32(1e-5)
+    elif what == "edges":
+        q[0, 0, 1, 2] = f32(65280.0)
+        q[0, 0, 1, 3] = f32(2.0 ** -24)
+        ref["ring_kv"][0, slot, 9] = f32(-65280.0)
+        ref["kv_scale"][0, b_last, 1] = np.float32(2.0 ** -14)
+        ref["kv_scale"][0, b_last, 3] = np.float32(255.0)
+    lay = lca.Layer.from_host(ref)
+    if csa:
+        # blocks 0..62 and row 0's last block (not yet visible to row 1)
+        sel = np.append(np.arange(63, dtype=np.int32), np.int32(b_last))
+        topk = np.ascontiguousarray(np.broadcast_to(sel, (2, 1, 64)))
+        lca.csa_attend(lay, _dev(q), _dev(topk), float(SCALE))
+    else:
+        lca.hca_attend(lay, _dev(q), float(SCALE))
+    torch.cuda.synchronize()
+    expect = FP16_RANGE_CASES[what]
+    assert lay.status() == (lca.STATUS_FP16_RANGE if expect else 0), (what, lay.status())
+
+
+def test_capacity_beyond_the_plan_is_reported():
+    """Host mirrors below the device lengths stand for a graph replayed past
+    its plan: each kernel keeps to its plan and sets its status bit; the
+    compressor skips a block past max_blocks."""
+    lca = _lca()
+    say("capacity status")
+    B, L, H, H_I, k = 2, 20000, 16, 4, 64
+    ref = SL.make_layer(6300, "cap", B, 4, 128, 256, 1, L // 4 + 8, [L, L - 3])
+    Q = SL.queries(6300, "cap", B, 1, H, H_I)
+    for fused in (1, 0):
+        lay = lca.Layer.from_host(ref)
+        lay.len_min, lay.len_max = 9000, 10000          # plans for 2500 blocks
+        lca.set_tuning("LCA_TOPK_FUSED", fused)
+        try:
+            lca.indexer_topk(lay, _dev(Q["iq"]), _dev(Q["iw"]), k)
+        finally:
+            lca.set_tuning("LCA_TOPK_FUSED", None)
+        torch.cuda.synchronize()
+        assert lay.status() == lca.STATUS_INDEXER_CAPACITY, (fused, lay.status())
+    href = SL.make_layer(6301, "caph", B, 128, 128, 256, 0, L // 128 + 8, [L, L - 3])
+    lay = lca.Layer.from_host(href)
+    lay.len_min, lay.len_max = 9000, 10000
+    lca.set_tuning("LCA_ATTEND_SPLITS", 4)
+    try:
+        lca.hca_attend(lay, _dev(Q["q"]), float(SCALE))
+    finally:
+        lca.set_tuning("LCA_ATTEND_SPLITS", None)
+    torch.cuda.synchronize()
+    assert lay.status() == lca.STATUS_ATTEND_CAPACITY, lay.status()
+    # compressor: 10 blocks fit, the device rows already hold 40 tokens
+    cref = SL.make_layer(6302, "capc", 1, 4, 8, 32, 0, 10, [40])
+    lay = lca.Layer.from_host(cref)
+    before = lay.download()
+    lay.len_min = lay.len_max = 0
+    tok = SL.tokens(6302, "capc", 1, 4, 0)
+    lca.compress_append(lay, _dev(tok["kv"]), _dev(tok["gate"]))
+    torch.cuda.synchronize()
+    after = lay.download()
+    assert lay.status() == lca.STATUS_COMPRESS_CAPACITY, lay.status()
+    assert int(after["seq_len"][0]) == 44
+    for f in ("nope", "rope", "kv_scale"):
+        assert np.array_equal(after[f], before[f]), f
