@@ -46,10 +46,13 @@ WORKLOADS = {
 
 # Interleaved streaming decode: `pairs` x (CSA layer, HCA layer) at `ctx`,
 # each step appends one token per row to every layer and runs every layer.
-# name: (batch, context, pairs, CSA heads, CSA indexer heads, CSA k, HCA heads, window)
+# name: (batch, context, pairs, CSA heads, CSA indexer heads, CSA k, HCA heads,
+#        window, needles per row, outlier channels)
 INTERLEAVED = {
-    "interleaved_1m": (8, 1 << 20, 8, 16, 4, 64, 64, 128),          # CSA layers shaped as the tiny decode
-    "interleaved_1m_wide": (8, 1 << 20, 8, 64, 16, 512, 64, 128),   # CSA layers shaped as the 128K decode
+    # the tiny CPU-scale decode: one row at 4K, one CSA + one HCA layer of 16 heads
+    "tiny_decode_4k": (1, 4096, 1, 16, 4, 64, 16, 128, 4, 0),
+    "interleaved_1m": (8, 1 << 20, 8, 16, 4, 64, 64, 128, 0, 26),          # CSA layers shaped as the tiny decode
+    "interleaved_1m_wide": (8, 1 << 20, 8, 64, 16, 512, 64, 128, 0, 26),   # CSA layers shaped as the 128K decode
 }
 
 
@@ -69,6 +72,16 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0     # dense MXFP4 matrix peak
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def spread_us(durations_ms):
+    """mean / p10 / p50 / p90 of per-launch durations, in microseconds."""
+    d = np.asarray(durations_ms, np.float64) * 1e3
+    if d.size == 0:
+        return None
+    return {"mean": round(float(d.mean()), 3), "p10": round(float(np.percentile(d, 10)), 3),
+            "p50": round(float(np.percentile(d, 50)), 3), "p90": round(float(np.percentile(d, 90)), 3),
+            "launches": int(d.size)}
 
 
 def algorithmic_bytes(wl):
@@ -113,8 +126,8 @@ def cpu_baseline(wl, ref, Q, tokens):
     """The oracle, as it stands, on one step of the workload for a sample of rows."""
     import oracle
     csa, B, ctx, m, H, HI, k, _, W = wl
-    nthreads = min(16, len(os.sched_getaffinity(0)))
-    rows = B if csa else max(1, B // 4)
+    nthreads = oracle.nthreads_default()
+    rows = B                          # the oracle's work unit is one (row, query): one row per thread
     sub = dict(ref)
     sub["batch"] = rows
     for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
@@ -131,10 +144,11 @@ def cpu_baseline(wl, ref, Q, tokens):
     else:
         oracle.hca_attend(sub, Q["q"][:rows], scale, nthreads=nthreads)
     dt = time.perf_counter() - t0
-    return dict(value=rows / dt, unit="queries/s", cores=nthreads, kind="oracle",
+    return dict(value=rows / dt, unit="queries/s", cores=min(nthreads, rows), kind="oracle",
                 sample=f"one decode step (compress_append + "
-                       f"{'indexer_topk + csa_attend' if csa else 'hca_attend'}) for {rows} of "
-                       f"{B} rows at full context, {dt:.2f}s wall")
+                       f"{'indexer_topk + csa_attend' if csa else 'hca_attend'}) for all {rows} rows "
+                       f"at full context, {dt:.2f}s wall, {min(nthreads, rows)} threads (the job's "
+                       f"CPU share: affinity capped by OMP_NUM_THREADS)")
 
 
 def counter_traffic(dominant, workload):
@@ -163,8 +177,9 @@ def counter_traffic(dominant, workload):
 
 def interleaved_bytes(B, ctx, H_c, HI, k, H_h, W):
     """Algorithmic bytes of one layer pair (per the per-row figures above)."""
-    csa = B * ((ctx // 4) * 34 + HI * 260 + 2 * k * 4 + k * 604 + W * 1024 + H_c * 1024 + H_c * 2048)
-    hca = B * ((ctx // 128) * 604 + W * 1024 + H_h * 1024 + H_h * 2048)
+    nc, nh = ctx // 4, ctx // 128
+    csa = B * (nc * 34 + HI * 260 + 2 * k * 4 + min(k, nc) * 604 + W * 1024 + H_c * 1024 + H_c * 2048)
+    hca = B * (nh * 604 + W * 1024 + H_h * 1024 + H_h * 2048)
     return csa, hca
 
 
@@ -244,15 +259,16 @@ def run_prefill(args):
         e1.synchronize()
         times.append(e0.elapsed_time(e1))
     ms_per_step = float(np.median(times))
-    kernels = {}
+    kernels, spreads = {}, {}
     for name in ("compress", "indexer_score", "topk_select", "attend", "attend_combine"):
         with lca.KernelTimer(name) as kt:
-            for _ in range(max(1, args.steps // 4)):
+            for _ in range(max(1, args.steps // 2)):
                 reset()
                 step()
             torch.cuda.synchronize()
         if kt.launches:
             kernels[name] = round(kt.total_ms * 1e3 / kt.launches, 1)
+            spreads[name] = spread_us(kt.durations_ms)
     flops, pairs = prefill_score_flops(prior, n, m, HI)
     score_us = kernels.get("indexer_score", 0.0)
     tflops = flops / (score_us * 1e-6) / 1e12 if score_us else 0.0
@@ -267,12 +283,14 @@ def run_prefill(args):
         roof = {"kernel": "indexer_score", "bound": "mfma", "achieved": round(tflops, 1),
                 "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel_avg_us": score_us, "flops_per_launch": flops}
+                "kernel_avg_us": score_us, "kernel_us": spreads.get("indexer_score"),
+                "flops_per_launch": flops}
     else:
         roof = {"kernel": "attend", "bound": "mfma", "achieved": round(att_tflops, 1),
                 "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(att_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel_avg_us": att_us, "flops_per_launch": att_flops}
+                "kernel_avg_us": att_us, "kernel_us": spreads.get("attend"),
+                "flops_per_launch": att_flops}
     cpu = None
     if not args.no_cpu_baseline:
         try:
@@ -317,7 +335,8 @@ def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k, csa=True):
     indexer_topk and csa_attend (HCA: hca_attend) for 4 of the chunk's queries
     (each on a view whose length ends at that query)."""
     import oracle
-    nthreads = min(16, len(os.sched_getaffinity(0)))
+    from concurrent.futures import ThreadPoolExecutor
+    nthreads = oracle.nthreads_default()
     scale = np.float32(1.0 / np.sqrt(512.0))
     V = oracle.row_view(ref, 0)
     t0 = time.perf_counter()
@@ -326,22 +345,30 @@ def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k, csa=True):
     else:
         oracle.compress_append(V, tok["kv"], tok["gate"])
     t_comp = time.perf_counter() - t0
-    sample = (0, n // 3, 2 * n // 3, n - 1)
-    t0 = time.perf_counter()
-    for qi in sample:
+    # one query per oracle call (each on a view whose length ends at that
+    # query), the calls spread over the job's threads
+    n_s = max(16, nthreads)
+    sample = [int(i * (n - 1) / (n_s - 1)) for i in range(n_s)]
+
+    def one(qi):
         Vq = dict(V)
         Vq["seq_len"] = np.array([prior + qi + 1], np.int32)
         if csa:
-            tk = oracle.indexer_topk(Vq, Q["iq"][:, qi:qi + 1], Q["iw"][:, qi:qi + 1], k, nthreads=nthreads)
-            oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], tk, scale, nthreads=nthreads)
+            tk = oracle.indexer_topk(Vq, Q["iq"][:, qi:qi + 1], Q["iw"][:, qi:qi + 1], k, nthreads=1)
+            oracle.csa_attend(Vq, Q["q"][:, qi:qi + 1], tk, scale, nthreads=1)
         else:
-            oracle.hca_attend(Vq, Q["q"][:, qi:qi + 1], scale, nthreads=nthreads)
-    t_q = (time.perf_counter() - t0) / len(sample)
+            oracle.hca_attend(Vq, Q["q"][:, qi:qi + 1], scale, nthreads=1)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthreads) as pool:
+        list(pool.map(one, sample))
+    t_q = (time.perf_counter() - t0) / len(sample)      # per query, all threads busy
     per_chunk = t_comp + t_q * n
     return dict(value=n / per_chunk, unit="queries/s", cores=nthreads, kind="oracle",
                 sample=f"compress_append of the {n}-token chunk ({t_comp:.2f}s) plus "
                        f"{'indexer_topk + csa_attend' if csa else 'hca_attend'} for {len(sample)} of its "
-                       f"queries ({t_q:.2f}s each), scaled to the chunk")
+                       f"queries spread over {nthreads} threads ({t_q:.3f}s per query), scaled to the "
+                       f"chunk")
 
 
 def run_interleaved(args):
@@ -349,17 +376,27 @@ def run_interleaved(args):
     import long_context_compressed_append_amd as lca
     from synth import layers as SL
 
-    B, ctx, P, H_c, HI, k, H_h, W = INTERLEAVED[args.workload]
+    B, ctx, P, H_c, HI, k, H_h, W, needles, n_out = INTERLEAVED[args.workload]
     seed = 1005
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t = time.time()
-    # one host image per layer kind (each with its outlier channels), copied to
+    n_set = 1 if needles else 4       # needles target one query set
+    # one host image per layer kind (with its outlier channels), copied to
     # every layer of that kind; from then on the layers diverge by their tokens
-    images = {}
+    images, chans = {}, {}
+    qc_host = [SL.queries(seed, "csaq", B, 1, H_c, HI, step=s) for s in range(n_set)]
+    # tokens appended after the image: warm-up, eager and graph timing, kernel timing
+    extra = args.warmup + 2 * min(args.steps, 128) + 64
     for kind, m, has_idx in (("csa", 4, 1), ("hca", 128, 0)):
-        ref = SL.make_layer(seed, kind, B, m, W, 256, has_idx, ctx // m + 64, [ctx - 1] * B)
-        SL.apply_outliers(ref, SL.outlier_channels(seed, kind, 0))
+        ref = SL.make_layer(seed, kind, B, m, W, 256, has_idx, (ctx + extra) // m + 64, [ctx - 1] * B)
+        chans[kind] = SL.outlier_channels(seed, kind, 0, n_out) if n_out else None
+        if n_out:
+            SL.apply_outliers(ref, chans[kind])
+        if needles and kind == "csa":
+            for b in range(B):
+                SL.plant_needles(ref, seed, kind, b, needles, qc_host[0]["iq"][b, 0], qc_host[0]["iw"][b, 0],
+                                 qc_host[0]["q"][b, 0])
         images[kind] = ref
     log(f"host images built in {time.time() - t:.1f}s")
 
@@ -383,57 +420,137 @@ def run_interleaved(args):
                     getattr(lay, f).copy_(src)
             lay.len_min, lay.len_max = base.len_min, base.len_max
             layers[kind].append(lay)
-    del images
+    all_layers = layers["csa"] + layers["hca"]
     torch.cuda.synchronize()
     log(f"{2 * P} device layers ready in {time.time() - t:.1f}s")
-    n_set = 4
-    toks = {kind: [[{kk: up(v) for kk, v in SL.outlier_tokens(
-        SL.tokens(seed, f"{kind}{l}", B, 1, kind == "csa", step=s),
-        SL.outlier_channels(seed, kind, 0)).items()} for s in range(n_set)] for l in range(P)]
-        for kind in ("csa", "hca")}
-    qs = {"csa": [up(SL.queries(seed, "csaq", B, 1, H_c, HI, step=s)["q"]) for s in range(n_set)],
+
+    def host_tokens(kind, l, s):
+        tk = SL.tokens(seed, f"{kind}{l}", B, 1, kind == "csa", step=s)
+        return SL.outlier_tokens(tk, chans[kind]) if n_out else tk
+
+    toks = {kind: [[{kk: up(v) for kk, v in host_tokens(kind, l, s).items()} for s in range(n_set)]
+                   for l in range(P)] for kind in ("csa", "hca")}
+    qs = {"csa": [up(x["q"]) for x in qc_host],
           "hca": [up(SL.queries(seed, "hcaq", B, 1, H_h, step=s)["q"]) for s in range(n_set)]}
-    iqs = [SL.queries(seed, "csaq", B, 1, H_c, HI, step=s) for s in range(n_set)]
-    iq = [(up(x["iq"]), up(x["iw"])) for x in iqs]
+    iq = [(up(x["iq"]), up(x["iw"])) for x in qc_host]
     topk = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
     out_c = torch.empty((B, 1, H_c, 512), dtype=torch.float32, device=dev)
     out_h = torch.empty((B, 1, H_h, 512), dtype=torch.float32, device=dev)
+    # the graph's inputs: fixed buffers, filled from the rotating sets
+    g_tok = {kind: [{kk: v.clone() for kk, v in toks[kind][l][0].items()} for l in range(P)]
+             for kind in ("csa", "hca")}
+    g_q = {"csa": qs["csa"][0].clone(), "hca": qs["hca"][0].clone()}
+    g_iq = (iq[0][0].clone(), iq[0][1].clone())
 
-    def step(s):
+    def step_with(tc_of, th_of, qc, qh, iqw, plan_len=None):
         for l in range(P):
             c, h = layers["csa"][l], layers["hca"][l]
-            tc, th = toks["csa"][l][s % n_set], toks["hca"][l][s % n_set]
+            tc, th = tc_of(l), th_of(l)
             lca.compress_append(c, tc["kv"], tc["gate"], tc["ikey"], tc["igate"])
-            lca.indexer_topk(c, iq[s % n_set][0], iq[s % n_set][1], k, out=topk)
-            lca.csa_attend(c, qs["csa"][s % n_set], topk, out=out_c)
+            if plan_len is not None:
+                c.len_max = plan_len
+            lca.indexer_topk(c, iqw[0], iqw[1], k, out=topk)
+            lca.csa_attend(c, qc, topk, out=out_c)
             lca.compress_append(h, th["kv"], th["gate"])
-            lca.hca_attend(h, qs["hca"][s % n_set], out=out_h)
+            if plan_len is not None:
+                h.len_max = plan_len
+            lca.hca_attend(h, qh, out=out_h)
+
+    def step(s):
+        j = s % n_set
+        step_with(lambda l: toks["csa"][l][j], lambda l: toks["hca"][l][j], qs["csa"][j], qs["hca"][j], iq[j])
+
+    def fill_graph_inputs(s):
+        j = s % n_set
+        for kind in ("csa", "hca"):
+            for l in range(P):
+                for kk, v in toks[kind][l][j].items():
+                    g_tok[kind][l][kk].copy_(v)
+        g_q["csa"].copy_(qs["csa"][j])
+        g_q["hca"].copy_(qs["hca"][j])
+        g_iq[0].copy_(iq[j][0])
+        g_iq[1].copy_(iq[j][1])
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    # timed, eager, one step at a time (per-step latency) over `steps` steps;
-    # the HCA layers finalise a block on the first step after every 128th token
+    done = args.warmup
+    stream = torch.cuda.current_stream()
+    # eager: one step at a time between HIP events (per-step latency); the HCA
+    # layers finalise a block on the first step after every 128th token
     nsteps = min(args.steps, 128)
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
-    t0 = time.perf_counter()
-    for i in range(nsteps):
-        ev0[i].record()
-        step(args.warmup + i)
-        ev1[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    times = np.array([ev0[i].elapsed_time(ev1[i]) for i in range(nsteps)])
+
+    def timed(run_one, first, prep=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+        t0 = time.perf_counter()
+        for i in range(nsteps):
+            if prep is not None:          # outside the events: input copies of a graph replay
+                prep(first + i)
+            ev[i][0].record(stream)
+            run_one(first + i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return np.array([a.elapsed_time(b) for a, b in ev]), wall
+
+    eager_times, eager_wall = timed(step, done)
+    done += nsteps
+    graph_times = None
+    if not args.eager:
+        final_len = max(x.len_max for x in all_layers) + nsteps + 2
+        saved = [(x.len_min, x.len_max) for x in all_layers]
+        for x in all_layers:                  # workspaces sized for the planned lengths before capture
+            x.len_max = final_len
+        for c in layers["csa"]:
+            c.indexer_workspace(1, lca.indexer_workspace_bytes(c, 1, HI, k))
+            c.workspace(lca.attend_workspace_bytes(c, 1, H_c, k), "attend")
+        for h in layers["hca"]:
+            h.workspace(lca.attend_workspace_bytes(h, 1, H_h, 0), "attend")
+        for x, (a, b) in zip(all_layers, saved):
+            x.len_min, x.len_max = a, b
+        fill_graph_inputs(done)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step_with(lambda l: g_tok["csa"][l], lambda l: g_tok["hca"][l], g_q["csa"], g_q["hca"], g_iq,
+                      plan_len=final_len)
+        torch.cuda.synchronize()
+        for x, (a, b) in zip(all_layers, saved):      # capture ran nothing on the device
+            x.len_min, x.len_max = a, b
+
+        graph_times, graph_wall = timed(lambda s: g.replay(), done, prep=fill_graph_inputs)
+        for x in all_layers:
+            x.len_min += nsteps
+            x.len_max += nsteps
+        done += nsteps
+        del g
     # the dominant kernel (CSA indexer score) alone, HIP events around its launches
     with lca.KernelTimer("indexer_score") as kt:
-        step(args.warmup + nsteps)
+        for i in range(max(1, 32 // P)):
+            step(done + i)
         torch.cuda.synchronize()
     kernel_ms = kt.total_ms / max(1, kt.launches)
     csa_b, hca_b = interleaved_bytes(B, ctx, H_c, HI, k, H_h, W)
+    times = graph_times if graph_times is not None else eager_times
     step_ms = float(times.mean())
     dom_bytes = B * ((ctx // 4) * 34 + HI * 260)
     achieved = dom_bytes / (kernel_ms / 1e3) / 1e9 if kernel_ms > 0 else 0.0
+
+    def lat(ts):
+        if ts is None:
+            return None
+        return {"step_ms_mean": round(float(ts.mean()), 4), "step_ms_p50": round(float(np.median(ts)), 4),
+                "step_ms_p90": round(float(np.percentile(ts, 90)), 4), "step_ms_max": round(float(ts.max()), 4),
+                "pair_us_mean": round(float(ts.mean()) * 1e3 / P, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = interleaved_cpu_baseline(images, qc_host[0], SL.queries(seed, "hcaq", B, 1, H_h, step=0),
+                                           {kind: host_tokens(kind, 0, 0) for kind in ("csa", "hca")}, k, P)
+        except Exception as e:  # report, never hide
+            cpu = dict(error=repr(e))
     res = {
         "metric": METRIC,
         "value": round(B / (step_ms / 1e3), 1),
@@ -442,28 +559,60 @@ def run_interleaved(args):
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4/fp8 storage; fp32 scores; bf16/fp16 MFMA with fp32 accumulate",
-        "data": "synthetic (seeded cache images, 26 outlier channels x20 per layer kind)",
+        "data": ("synthetic (seeded cache images"
+                 + (f", {n_out} outlier channels x20 per layer kind" if n_out else "")
+                 + (f", {needles} needle blocks per row" if needles else "") + ")"),
         "config": {
             "workload": args.workload, "batch": B, "context": ctx, "layer_pairs": P,
             "csa": {"heads": H_c, "indexer_heads": HI, "topk": k, "ratio": 4},
-            "hca": {"heads": H_h, "ratio": 128}, "window": W, "launch": "eager",
-            "pair_latency_us": {"mean": round(step_ms * 1e3 / P, 2),
-                                "p50": round(float(np.median(times)) * 1e3 / P, 2),
-                                "max": round(float(times.max()) * 1e3 / P, 2)},
-            "step_ms": {"mean": round(step_ms, 4), "p50": round(float(np.median(times)), 4),
-                        "max": round(float(times.max()), 4)},
+            "hca": {"heads": H_h, "ratio": 128}, "window": W,
+            "launch": "hip_graph" if graph_times is not None else "eager",
+            "eager": lat(eager_times), "graph": lat(graph_times),
             "step_algorithmic_bytes": P * (csa_b + hca_b),
             "step_hbm_gbs": round(P * (csa_b + hca_b) / (step_ms / 1e3) / 1e9, 1),
-            "wall_ms_per_step": round(wall * 1e3 / nsteps, 4),
+            "eager_wall_ms_per_step": round(eager_wall * 1e3 / nsteps, 4),
         },
         "roofline": {
             "kernel": "indexer_score", "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "kernel_avg_us": round(kernel_ms * 1e3, 3), "bytes_per_launch": dom_bytes,
+            "traffic": None, "kernel_avg_us": round(kernel_ms * 1e3, 3),
+            "kernel_us": spread_us(kt.durations_ms), "bytes_per_launch": dom_bytes,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+def interleaved_cpu_baseline(images, qc, qh, tok, k, P):
+    """The oracle on one layer pair of one step for every row (a CSA layer:
+    compress_append, indexer_topk, csa_attend; an HCA layer: compress_append,
+    hca_attend), scaled to the P pairs a token goes through."""
+    import oracle
+    nthreads = oracle.nthreads_default()
+    scale = np.float32(1.0 / np.sqrt(512.0))
+    views = {}
+    for kind, ref in images.items():
+        v = dict(ref)
+        for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv", "ring_gate",
+                  "ring_ikey", "ring_igate"):
+            v[f] = ref[f].copy()                       # the oracle appends in place
+        views[kind] = v
+    B = int(views["csa"]["batch"])
+    tc, th = tok["csa"], tok["hca"]
+    reps = 0
+    t0 = time.perf_counter()
+    # repeated steps (one more token each) until about 2 s of work, for short ones
+    while reps < 64 and (reps == 0 or time.perf_counter() - t0 < 2.0):
+        oracle.compress_append(views["csa"], tc["kv"], tc["gate"], tc["ikey"], tc["igate"])
+        tk = oracle.indexer_topk(views["csa"], qc["iq"], qc["iw"], k, nthreads=nthreads)
+        oracle.csa_attend(views["csa"], qc["q"], tk, scale, nthreads=nthreads)
+        oracle.compress_append(views["hca"], th["kv"], th["gate"])
+        oracle.hca_attend(views["hca"], qh["q"], scale, nthreads=nthreads)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    return dict(value=B / (dt * P), unit="tokens/s", cores=min(nthreads, B), kind="oracle",
+                sample=f"one layer pair of one step for all {B} rows ({dt:.4f}s wall per step over "
+                       f"{reps} steps, {min(nthreads, B)} threads), scaled to {P} pairs per token")
 
 
 def calibrate_copy(mib):
@@ -518,7 +667,8 @@ def main():
     csa, B, ctx, m, H, HI, k, needles, W = wl
     seed = 1001 if csa else 1002
     NL = args.layers
-    total_steps = args.warmup + args.steps + NL          # + eager timing pass
+    n_eager = 4 * NL                                     # eager pass timing the dominant kernel
+    total_steps = args.warmup + args.steps + n_eager
     ref, Q = build_host_layer(wl, seed)
     # tokens: a few distinct sets, rotated
     n_tok = 8
@@ -584,12 +734,13 @@ def main():
     # eager pass with the dominant kernel bracketed by HIP events
     t0 = time.perf_counter()
     with lca.KernelTimer(dominant) as kt:
-        for i in range(done, done + NL):
+        for i in range(done, done + n_eager):
             step(i)
         torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / NL
-    done += NL
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
+    done += n_eager
     kernel_ms = kt.total_ms / max(1, kt.launches)
+    kernel_spread = spread_us(kt.durations_ms)
 
     # graph of NL steps (one per layer), replayed; plans sized for the final lengths
     graph_ms = None
@@ -684,6 +835,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counter_traffic(dominant, args.workload),
             "kernel_avg_us": round(kernel_ms * 1e3, 3),
+            "kernel_us": kernel_spread,
             "bytes_per_launch": dom_bytes,
         },
         "cpu_baseline": cpu,

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 2
+#define LCA_ABI_VERSION 3
 
 enum {
   LCA_OK = 0,
@@ -83,6 +83,11 @@ enum {
  *                                 where the scaled probabilities leave
  *                                 fp16's normal range.  The result may miss
  *                                 the 2e-3 bound
+ *   LCA_STATUS_PAGE               a paged layer's block lay on an unmapped
+ *                                 page (page-table entry < 0 or not below
+ *                                 pool_pages): the compressor did not write
+ *                                 it; a visible one read by the indexer or
+ *                                 attention gave an unspecified score or key
  * Calls captured in a graph must be planned with len_max set to the longest
  * length they will reach (set the host mirror before capture); the capacity
  * bits report replays that went beyond it.
@@ -91,6 +96,7 @@ enum {
 #define LCA_STATUS_INDEXER_CAPACITY 2u
 #define LCA_STATUS_ATTEND_CAPACITY 4u
 #define LCA_STATUS_FP16_RANGE 8u
+#define LCA_STATUS_PAGE 16u
 
 #define LCA_KV_DIM 512
 #define LCA_NOPE_DIM 448
@@ -130,6 +136,22 @@ enum {
  * position p sees entries b < floor((p+1)/m) and the raw tokens
  * max(0, p-W+1) .. p.  Rows may hold different lengths; every call appends
  * the same number of tokens to every row.
+ *
+ * Paged entries (page_blocks = PB > 0).  Agent traces differ in length and
+ * run to about a million tokens ([AGENT] on why agents break down on long
+ * tasks), so rows of one batch may draw their compressed entries from one
+ * shared pool of pages instead of owning max_blocks each.  The five entry
+ * planes (nope, rope, kv_scale, idx_code, idx_scale) then hold pool_pages *
+ * PB entries, [pool_pages * PB][...], and
+ *   page_table int32   [B][MB / PB]   physical page of each logical page of a
+ *                                     row, or -1 (unmapped)
+ * places entry b of row r at physical entry
+ * page_table[r][b / PB] * PB + b % PB.  PB is a power of two in 64..65536
+ * and divides MB; the ring planes stay per row.  The caller maps the pages
+ * of every entry a compress_append call completes before the call (device
+ * data: a block on an unmapped page is not written and sets
+ * LCA_STATUS_PAGE) and may change the table between calls (unmapping pages
+ * of entries no query will read again, mapping new ones).
  */
 typedef struct lca_layer {
   int32_t batch;        /* B >= 1                                              */
@@ -137,7 +159,7 @@ typedef struct lca_layer {
   int32_t window;       /* W >= 1                                              */
   int32_t ring;         /* R >= W                                              */
   int32_t has_indexer;  /* 1: CSA layer (indexer planes present); 0: HCA       */
-  int32_t reserved;     /* 0                                                   */
+  int32_t page_blocks;  /* 0: entry planes [B][MB][...]; PB: paged (above)     */
   int64_t max_blocks;   /* MB >= 1                                             */
   int64_t len_min;      /* host mirror: min over rows of seq_len               */
   int64_t len_max;      /* host mirror: max over rows of seq_len               */
@@ -154,6 +176,8 @@ typedef struct lca_layer {
   float *ring_igate;
   const float *pos_bias;
   const float *ipos_bias;
+  const int32_t *page_table;  /* [B][MB / PB] when page_blocks > 0, else NULL  */
+  int64_t pool_pages;         /* pages in the entry planes when paged, else 0  */
 } lca_layer;
 
 /*
@@ -335,6 +359,12 @@ const char *lca_last_error(void);
  */
 int lca_timing_begin(const char *kernel);
 int lca_timing_end(double *total_ms, int64_t *launches);
+/*
+ * The per-launch durations (ms, launch order) of the session the last
+ * lca_timing_end closed: copies min(cap, launches) of them into ms and sets
+ * *launches to their number (ms may be NULL when cap is 0).  Errors: EINVAL.
+ */
+int lca_timing_durations(float *ms, int64_t cap, int64_t *launches);
 
 #ifdef __cplusplus
 }

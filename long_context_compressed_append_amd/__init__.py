@@ -29,6 +29,7 @@ KV, NOPE, ROPE, IDX = 512, 448, 64, 64
 ERRORS = {0: "LCA_OK", -1: "LCA_EINVAL", -2: "LCA_EUNSUPPORTED", -3: "LCA_ECAPACITY",
           -4: "LCA_EWORKSPACE", -5: "LCA_EHIP"}
 STATUS_COMPRESS_CAPACITY, STATUS_INDEXER_CAPACITY, STATUS_ATTEND_CAPACITY, STATUS_FP16_RANGE = 1, 2, 4, 8
+STATUS_PAGE = 16
 
 
 class LcaError(RuntimeError):
@@ -42,11 +43,12 @@ P = C.c_void_p
 
 class LcaLayerStruct(C.Structure):
     _fields_ = [("batch", C.c_int32), ("ratio", C.c_int32), ("window", C.c_int32),
-                ("ring", C.c_int32), ("has_indexer", C.c_int32), ("reserved", C.c_int32),
+                ("ring", C.c_int32), ("has_indexer", C.c_int32), ("page_blocks", C.c_int32),
                 ("max_blocks", C.c_int64), ("len_min", C.c_int64), ("len_max", C.c_int64),
                 ("seq_len", P), ("sync", P), ("nope", P), ("rope", P), ("kv_scale", P),
                 ("idx_code", P), ("idx_scale", P), ("ring_kv", P), ("ring_gate", P),
-                ("ring_ikey", P), ("ring_igate", P), ("pos_bias", P), ("ipos_bias", P)]
+                ("ring_ikey", P), ("ring_igate", P), ("pos_bias", P), ("ipos_bias", P),
+                ("page_table", P), ("pool_pages", C.c_int64)]
 
 
 _lib = None
@@ -77,6 +79,7 @@ def lib():
         L.lca_set_tuning.argtypes = [C.c_char_p, C.c_int32]
         L.lca_timing_begin.argtypes = [C.c_char_p]
         L.lca_timing_end.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        L.lca_timing_durations.argtypes = [C.POINTER(C.c_float), C.c_int64, C.POINTER(C.c_int64)]
         _lib = L
     return _lib
 
@@ -112,25 +115,36 @@ class Layer:
     """One layer's cache in device memory (plane layout of include/lca.h).
 
     Planes are torch tensors on `device`; `from_host` uploads numpy planes of
-    the same layout (the dict built by synth.layers)."""
+    the same layout (the dict built by synth.layers).  With page_blocks > 0
+    the entry planes are a pool of pool_pages pages, [pool_pages *
+    page_blocks][...], and page_table [B][max_blocks / page_blocks] (int32,
+    -1 = unmapped) places each row's entries in it."""
 
     PLANES = ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
               "ring_gate", "ring_ikey", "ring_igate")
 
     def __init__(self, batch, ratio, window, ring, has_indexer, max_blocks, device="cuda",
-                 pos_bias=None, ipos_bias=None, lengths=None):
+                 pos_bias=None, ipos_bias=None, lengths=None, page_blocks=0, pool_pages=0):
         self.batch, self.ratio, self.window, self.ring = int(batch), int(ratio), int(window), int(ring)
         self.has_indexer, self.max_blocks = int(bool(has_indexer)), int(max_blocks)
+        self.page_blocks, self.pool_pages = int(page_blocks), int(pool_pages)
         B, MB, R = self.batch, self.max_blocks, self.ring
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
         self.seq_len = z((B,), torch.int32)
         self.sync = z((4,), torch.int32)
-        self.nope = z((B, MB, NOPE), torch.uint8)
-        self.rope = z((B, MB, ROPE), torch.int16)
-        self.kv_scale = z((B, MB, 8), torch.float32)
+        ent = (B, MB)                         # entry planes: per row, or one pool
+        self.page_table = None
+        self.planes = self.PLANES
+        if self.page_blocks:
+            ent = (self.pool_pages * self.page_blocks,)
+            self.page_table = torch.full((B, MB // self.page_blocks), -1, dtype=torch.int32, device=device)
+            self.planes = self.PLANES + ("page_table",)
+        self.nope = z(ent + (NOPE,), torch.uint8)
+        self.rope = z(ent + (ROPE,), torch.int16)
+        self.kv_scale = z(ent + (8,), torch.float32)
         hi = self.has_indexer
-        self.idx_code = z((B, MB, 32), torch.uint8) if hi else None
-        self.idx_scale = z((B, MB, 2), torch.uint8) if hi else None
+        self.idx_code = z(ent + (32,), torch.uint8) if hi else None
+        self.idx_scale = z(ent + (2,), torch.uint8) if hi else None
         self.ring_kv = z((B, R, KV), torch.int16)
         self.ring_gate = z((B, R, KV), torch.float32)
         self.ring_ikey = z((B, R, IDX), torch.float32) if hi else None
@@ -150,13 +164,14 @@ class Layer:
     def from_host(cls, L, device="cuda"):
         """Upload a numpy plane dict (synth.layers layout)."""
         lay = cls(L["batch"], L["ratio"], L["window"], L["ring"], L["has_indexer"], L["max_blocks"],
-                  device=device, pos_bias=L["pos_bias"], ipos_bias=L.get("ipos_bias"))
+                  device=device, pos_bias=L["pos_bias"], ipos_bias=L.get("ipos_bias"),
+                  page_blocks=L.get("page_blocks", 0), pool_pages=L.get("pool_pages", 0))
         lay.upload(L)
         return lay
 
     def upload(self, L):
         import numpy as np
-        for f in self.PLANES:
+        for f in self.planes:
             t = getattr(self, f)
             if t is None:
                 continue
@@ -172,7 +187,9 @@ class Layer:
         import numpy as np
         out = dict(batch=self.batch, ratio=self.ratio, window=self.window, ring=self.ring,
                    has_indexer=self.has_indexer, max_blocks=self.max_blocks)
-        for f in self.PLANES:
+        if self.page_blocks:
+            out.update(page_blocks=self.page_blocks, pool_pages=self.pool_pages)
+        for f in self.planes:
             t = getattr(self, f)
             if t is None:
                 continue
@@ -186,8 +203,8 @@ class Layer:
 
     def status(self):
         """The layer's status bits (LCA_STATUS_*: 1 compressor capacity,
-        2 indexer capacity, 4 attention capacity, 8 fp16 range), as left by
-        the work the stream has run so far."""
+        2 indexer capacity, 4 attention capacity, 8 fp16 range, 16 unmapped
+        page), as left by the work the stream has run so far."""
         return int(self.sync[1].item()) & 0xFFFFFFFF
 
     def clear_status(self):
@@ -201,10 +218,11 @@ class Layer:
     def struct(self):
         s = LcaLayerStruct()
         s.batch, s.ratio, s.window, s.ring = self.batch, self.ratio, self.window, self.ring
-        s.has_indexer, s.reserved, s.max_blocks = self.has_indexer, 0, self.max_blocks
+        s.has_indexer, s.page_blocks, s.max_blocks = self.has_indexer, self.page_blocks, self.max_blocks
         s.len_min, s.len_max = self.len_min, self.len_max
+        s.pool_pages = self.pool_pages
         for f in ("seq_len", "sync", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
-                  "ring_gate", "ring_ikey", "ring_igate", "pos_bias", "ipos_bias"):
+                  "ring_gate", "ring_ikey", "ring_igate", "pos_bias", "ipos_bias", "page_table"):
             t = getattr(self, f)
             setattr(s, f, t.data_ptr() if t is not None else None)
         return s
@@ -363,7 +381,7 @@ class KernelTimer:
     """Sum of HIP-event durations of one library kernel over a code region:
 
         with KernelTimer("indexer_score") as t: ...
-        t.total_ms, t.launches
+        t.total_ms, t.launches, t.durations_ms (one per launch)
     """
 
     def __init__(self, kernel):
@@ -378,4 +396,7 @@ class KernelTimer:
         ms, n = C.c_double(0.0), C.c_int64(0)
         _check(lib().lca_timing_end(C.byref(ms), C.byref(n)))
         self.total_ms, self.launches = ms.value, n.value
+        each = (C.c_float * max(1, n.value))()
+        _check(lib().lca_timing_durations(each, n.value, C.byref(n)))
+        self.durations_ms = [float(x) for x in each[:self.launches]]
         return False

@@ -51,6 +51,7 @@ struct Timing {
   int kernel = kKernelNone;
   int used = 0;
   std::vector<hipEvent_t> start, stop;
+  std::vector<float> last;    // per-launch durations of the last closed session
 };
 Timing g_timing;
 constexpr int kMaxTimed = 4096;
@@ -116,6 +117,22 @@ static int check_layer(const lca_layer* L) {
       if (!im[i]) return set_error(LCA_EINVAL, "layer.%s is NULL on an indexer layer", in[i]);
       if (!aligned16(im[i])) return set_error(LCA_EINVAL, "layer.%s is not 16-byte aligned", in[i]);
     }
+  }
+  const int32_t pb = L->page_blocks;
+  if (pb == 0) {
+    if (L->page_table || L->pool_pages)
+      return set_error(LCA_EINVAL, "page_table / pool_pages set on a layer with page_blocks 0");
+  } else {
+    if (pb < 64 || pb > 65536 || (pb & (pb - 1)))
+      return set_error(LCA_EUNSUPPORTED, "page_blocks must be 0 or a power of two in 64..65536 (got %d)", pb);
+    if (L->max_blocks % pb)
+      return set_error(LCA_EINVAL, "max_blocks (%lld) is not a multiple of page_blocks (%d)",
+                       (long long)L->max_blocks, pb);
+    if (!L->page_table) return set_error(LCA_EINVAL, "layer.page_table is NULL on a paged layer");
+    if ((uintptr_t)L->page_table & 3u) return set_error(LCA_EINVAL, "layer.page_table is not 4-byte aligned");
+    if (L->pool_pages < 1) return set_error(LCA_EINVAL, "pool_pages must be >= 1 on a paged layer");
+    if (L->pool_pages > (((int64_t)1 << 31) - 1) / pb)
+      return set_error(LCA_EUNSUPPORTED, "pool_pages * page_blocks must stay below 2^31");
   }
   return LCA_OK;
 }
@@ -275,6 +292,7 @@ int lca_timing_end(double* total_ms, int64_t* launches) {
   std::lock_guard<std::mutex> g(g_timing.mu);
   if (g_timing.kernel == kKernelNone) return set_error(LCA_EINVAL, "no timing session is open");
   double tot = 0.0;
+  g_timing.last.clear();
   for (int i = 0; i < g_timing.used; i++) {
     if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess)
       return set_error(LCA_EHIP, "hipEventSynchronize failed");
@@ -282,12 +300,22 @@ int lca_timing_end(double* total_ms, int64_t* launches) {
     if (hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]) != hipSuccess)
       return set_error(LCA_EHIP, "hipEventElapsedTime failed");
     tot += ms;
+    g_timing.last.push_back(ms);
   }
   if (total_ms) *total_ms = tot;
   if (launches) *launches = g_timing.used;
   g_timing.kernel = kKernelNone;
   g_timing.used = 0;
   g_timing.open.store(0, std::memory_order_release);
+  return LCA_OK;
+}
+
+int lca_timing_durations(float* ms, int64_t cap, int64_t* launches) {
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  const int64_t n = (int64_t)g_timing.last.size();
+  if (launches) *launches = n;
+  if (cap > 0 && !ms) return set_error(LCA_EINVAL, "durations buffer is NULL");
+  for (int64_t i = 0; i < n && i < cap; i++) ms[i] = g_timing.last[i];
   return LCA_OK;
 }
 

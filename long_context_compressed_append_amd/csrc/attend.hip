@@ -65,6 +65,7 @@ constexpr int kAttendTargetWGs = 256;
 struct AttendArgs {
   int n_q, H, m, W, R, k, splits, chunk, csa, hwaves;
   int64_t max_blocks;
+  PageMap pm;             // where each entry lives
   float scale_log2;
   const int32_t* seq_len;
   const uint8_t* nope;
@@ -116,6 +117,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // or more (also inf, NaN), or nonzero and below 2^-14; an FP8 scale
   // outside [2^-14, 2^8)
   bool range_ok = true;
+  bool page_ok = true;    // false: a visible entry lay on an unmapped page (staged as masked)
   v8h qf[16];  // q of this lane's head (fp16 image of the bf16 input), channels 32 ks + 8 g .. +7
   {
     const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv;
@@ -175,8 +177,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     if (kk < ke) {
       if (kk < n_c) {
         const int e = a.csa ? klist[kk - kb] : kk;
-        if (e >= 0 && e < nv) {
-          const int64_t ent = (int64_t)brow * a.max_blocks + e;
+        const int64_t ent = e >= 0 && e < nv ? entry_index(a.pm, brow, e) : -1;
+        page_ok &= !(e >= 0 && e < nv && ent < 0);   // a visible entry on an unmapped page
+        if (ent >= 0) {
           if (sg < 7) {
             src = a.nope + ent * kNope + sg * 64 + sp * 32;
             scp = a.kv_scale + ent * kScaleStride + sg;
@@ -294,6 +297,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       __syncthreads();                     // tile t + 1 staged, tile t consumed
     }
     if (__any(!range_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_FP16_RANGE);
+    if (__any(!page_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_PAGE);
     return;
   }
   __syncthreads();                         // tile 0 staged
@@ -547,6 +551,7 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   a.csa = topk != nullptr;
   a.hwaves = pl.head_groups * 4;
   a.max_blocks = L->max_blocks;
+  a.pm = page_map_of<PageMap>(L);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.seq_len = L->seq_len;
   a.nope = L->nope;

@@ -26,6 +26,7 @@ namespace lca {
 struct CompressArgs {
   int B, m, R, n, has_idx, groups, nfin;   // nfin: block slots per row
   int64_t max_blocks;
+  PageMap pm;                              // where each entry lives
   int32_t* seq_len;
   uint32_t* sync;
   uint8_t* nope;
@@ -198,10 +199,13 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     const int L0 = a.seq_len[row];
     const int64_t bk = (int64_t)(L0 / a.m) + s;
     const bool completes = (bk + 1) * a.m <= (int64_t)L0 + a.n;
+    // (row and block are uniform over the wavefront: so is every branch here)
+    const int64_t e = completes && bk < a.max_blocks ? entry_index(a.pm, row, bk) : -1;
     if (completes && bk >= a.max_blocks) {           // past the cache (a replay beyond its plan)
       if (lane == 0) atomicOr(a.sync + 1, LCA_STATUS_COMPRESS_CAPACITY);
+    } else if (completes && e < 0) {                 // its page is not mapped
+      if (lane == 0) atomicOr(a.sync + 1, LCA_STATUS_PAGE);
     } else if (completes) {                          // block completes in this call
-      const int64_t e = (int64_t)row * a.max_blocks + bk;
       if (g < 8) {
         const int c = g * 64 + lane;
         float y = pool_channel<true>(a, row, bk, L0, c, kKv, a.kv, a.gate, a.ring_kv, a.ring_gate,
@@ -265,6 +269,7 @@ int launch_compress(const lca_layer* L, const uint16_t* kv, const float* gate, c
   a.groups = L->has_indexer ? 9 : 8;
   a.nfin = (n - 1) / L->ratio + 1;
   a.max_blocks = L->max_blocks;
+  a.pm = page_map_of<PageMap>(L);
   a.seq_len = L->seq_len;
   a.sync = L->sync;
   a.nope = L->nope;

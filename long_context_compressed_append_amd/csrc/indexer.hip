@@ -75,6 +75,7 @@ constexpr uint32_t kDropOffset = 0x80000000u;   // past every range used here
 struct ScoreArgs {
   int n_q, H, m;
   int64_t max_blocks, stride;
+  PageMap pm;            // where each block's key lives
   const int32_t* seq_len;
   const uint8_t* idx_code;
   const uint8_t* idx_scale;
@@ -91,6 +92,32 @@ struct ScoreArgs {
   int fused_span;        // fused selection: blocks per scoring workgroup (its candidate segment)
   uint32_t* status;      // the layer's status word (LCA_STATUS_* bits)
 };
+
+// Paged layers: lane l of every wavefront holds the physical page of the
+// l-th page from the one holding the workgroup's first block b0 (at most 64
+// pages: the plans keep a workgroup's span of blocks within 64 pages), or -1
+// past the row's table.
+__device__ __forceinline__ int wg_pages(const PageMap& pm, int row, int b0, int lane) {
+  const int pg = (b0 >> pm.shift) + lane;
+  return pg < pm.pages_per_row ? pm.table[(int64_t)row * pm.pages_per_row + pg] : -1;
+}
+// The physical entry of block blk (in the workgroup's span) whose 32-block
+// group starts at the wavefront-uniform block g0 (a page holds whole
+// groups); entry 0 (a harmless in-bounds read) when its page is unmapped.
+__device__ __forceinline__ int64_t wg_entry(const PageMap& pm, int lane_pg, int b0, int g0, int blk) {
+  const int pg = __builtin_amdgcn_readlane(lane_pg, ((g0 >> pm.shift) - (b0 >> pm.shift)) & 63);
+  const int64_t e = phys_entry(pm, pg, blk);
+  return e < 0 ? 0 : e;
+}
+// LCA_STATUS_PAGE when a visible block (below nv) of the workgroup's span
+// [b0, b0 + span) lies on an unmapped page (one wavefront reports)
+__device__ __forceinline__ void wg_pages_check(const PageMap& pm, int lane_pg, int b0, int span, int nv,
+                                               int lane, uint32_t* status) {
+  const int first = ((b0 >> pm.shift) + lane) << pm.shift;    // first block of the lane's page
+  const int lo = first > b0 ? first : b0;
+  const bool bad = first < b0 + span && lo < nv && (uint32_t)lane_pg >= (uint32_t)pm.pool_pages;
+  if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) atomicOr(status, LCA_STATUS_PAGE);
+}
 
 // max(x, +0) as one integer max on the bit pattern: a negative x (sign bit
 // set, a negative int) gives +0, any other x itself.  (fmaxf on a matrix-core
@@ -289,8 +316,12 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   const int wg_b0 = (int)blockIdx.x * a.cpw * kScoreBlocksPerWG;   // kFused: first block of the workgroup
   const int r = lane & 31, kh = lane >> 5;
 
-  const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
-  const uint8_t* ks = a.idx_scale + (int64_t)brow * a.max_blocks * 2;
+  // key planes: the row's entries (contiguous), or the page pool (paged)
+  const bool paged = a.pm.shift >= 0;
+  const int64_t row_base = paged ? 0 : (int64_t)brow * a.max_blocks;
+  const uint8_t* kc = a.idx_code + row_base * 32;
+  const uint8_t* ks = a.idx_scale + row_base * 2;
+  const int lane_pg = paged ? wg_pages(a.pm, brow, wg_b0, lane) : -1;
   // The wave walks iterations i = 0 .. n_it-1 of 32 blocks each: iteration i
   // is group i % 8 of this wave's 256 blocks in chunk c0 + i / 8.  Keys are
   // loaded kDepth iterations ahead of their use.
@@ -300,11 +331,13 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
            wh * (kScoreItersPerWave * kScoreBlocksPerIter) +
            (i % kScoreItersPerWave) * kScoreBlocksPerIter + r;
   };
-  // Loads are unconditional (a block past the capacity reads block 0) so that
-  // no load waits on another; compute() masks what they return.
+  // Loads are unconditional (a block past the capacity, or on an unmapped
+  // page, reads entry 0) so that no load waits on another; compute() masks
+  // what they return.
   auto load = [&](int i, int4& kr, uint32_t& er) {
     const int blk = blk_of(i);
-    const int b = (i < n_it && blk < cap) ? blk : 0;
+    int64_t b = (i < n_it && blk < cap) ? blk : 0;
+    if (paged && i < n_it && blk < cap) b = wg_entry(a.pm, lane_pg, wg_b0, blk - r, blk);
     kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
     er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
   };
@@ -335,6 +368,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
     if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
     nv = cap;
   }
+  if (paged && wave == 0) wg_pages_check(a.pm, lane_pg, wg_b0, a.cpw * kScoreBlocksPerWG, nv, lane, a.status);
 
   for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
   // MXFP4 quantisation of the query, one 32-lane half-wave per MX block
@@ -648,8 +682,12 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   const int cap = (int)(a.stride < a.max_blocks ? a.stride : a.max_blocks);
   const int b_lo = blockIdx.x * a.cpw * kScoreBlocksPerWG;
   const int b_hi = b_lo + a.cpw * kScoreBlocksPerWG;
-  const uint8_t* kc = a.idx_code + (int64_t)brow * a.max_blocks * 32;
-  const uint8_t* ks = a.idx_scale + (int64_t)brow * a.max_blocks * 2;
+  // key planes: the row's entries (contiguous), or the page pool (paged)
+  const bool paged = a.pm.shift >= 0;
+  const int64_t row_base = paged ? 0 : (int64_t)brow * a.max_blocks;
+  const uint8_t* kc = a.idx_code + row_base * 32;
+  const uint8_t* ks = a.idx_scale + row_base * 2;
+  const int lane_pg = paged ? wg_pages(a.pm, brow, b_lo, lane) : -1;
 
   // queries: Qwg x H x 64 fp32 values, quantised one MX block per half-wave
   const int nqv = min(kQwg, a.n_q - q0);              // queries of this workgroup
@@ -736,6 +774,7 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
     nv_hi = nv > nv_hi ? nv : nv_hi;
   }
   const int b_end = b_hi < nv_hi ? b_hi : nv_hi;
+  if (paged && wave == 0) wg_pages_check(a.pm, lane_pg, b_lo, b_hi - b_lo, nv_hi, lane, a.status);
   // lane l < 32 stores query 2m (H <= 16) or m of the pair, lane l >= 32 the other
   uint32_t* outq[kNm];
   int nvl[kNm];
@@ -768,7 +807,8 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   uint32_t erw[kRing];
   auto load = [&](int t, int4& k4, uint32_t& e2) {
     const int blk = blk_of(t);
-    const int bl = (t < n_it && blk < cap) ? blk : 0;
+    int64_t bl = (t < n_it && blk < cap) ? blk : 0;
+    if (paged && t < n_it && blk < cap) bl = wg_entry(a.pm, lane_pg, b_lo, blk - col, blk);
     k4 = *reinterpret_cast<const int4*>(kc + bl * 32 + 16 * kh);
     e2 = *reinterpret_cast<const uint16_t*>(ks + bl * 2);
   };
@@ -2154,6 +2194,10 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   int64_t cpw = (rows * chunks + kScoreTargetWGs - 1) / kScoreTargetWGs;
   const int force_cpw = tuning(kTuneScoreCpw);
   if (force_cpw > 0) cpw = force_cpw;
+  // paged: a workgroup's blocks span at most 64 pages (its wavefronts hold
+  // one page-table entry per lane)
+  const int64_t max_cpw = L->page_blocks > 0 ? (int64_t)L->page_blocks * 64 / kScoreBlocksPerWG : chunks;
+  if (cpw > max_cpw) cpw = max_cpw;
   if (cpw < 1) cpw = 1;
   if (cpw > chunks) cpw = chunks;
   pl.cpw = (int)cpw;
@@ -2168,6 +2212,7 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
     pl.qgroups = (n_q + pl.tile * kTileSets - 1) / (pl.tile * kTileSets);
     int64_t tcpw = ((int64_t)L->batch * pl.qgroups * chunks + kTileTargetWGs - 1) / kTileTargetWGs;
     if (force_cpw > 0) tcpw = force_cpw;
+    if (tcpw > max_cpw) tcpw = max_cpw;
     if (tcpw < 1) tcpw = 1;
     if (tcpw > chunks) tcpw = chunks;
     pl.cpw = (int)tcpw;
@@ -2242,6 +2287,7 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.H = H_I;
   s.m = L->ratio;
   s.max_blocks = L->max_blocks;
+  s.pm = page_map_of<PageMap>(L);
   s.stride = pl.stride;
   s.seq_len = L->seq_len;
   s.idx_code = L->idx_code;

@@ -186,6 +186,28 @@ __device__ __forceinline__ uint32_t bf16x8_absmax(uint4 w, uint32_t mx) {
 constexpr uint32_t kBf16F16Overflow = 0x4780u;    // 65536: the first bf16 magnitude above 65504
 constexpr uint32_t kBf16MinNormalF16 = 0x3880u;   // 2^-14
 
+// Where entry b of a row lives in the entry planes (nope, rope, kv_scale,
+// idx_code, idx_scale).  Contiguous layers (shift < 0): row * max_blocks + b.
+// Paged layers: the row's page-table entry for page b >> shift, times the
+// page size, plus b's offset in its page; -1 when that page is unmapped
+// (entry negative or not below pool_pages).
+struct PageMap {
+  const int32_t* table;     // [B][pages_per_row], null when contiguous
+  int64_t max_blocks;
+  int32_t pages_per_row;
+  int32_t shift;            // log2(page_blocks), or -1
+  int32_t pool_pages;
+  int32_t pad;
+};
+__device__ __forceinline__ int64_t phys_entry(const PageMap& pm, int page, int64_t b) {
+  return (uint32_t)page < (uint32_t)pm.pool_pages ? ((int64_t)page << pm.shift) + (b & ((1 << pm.shift) - 1))
+                                                   : (int64_t)-1;
+}
+__device__ __forceinline__ int64_t entry_index(const PageMap& pm, int row, int64_t b) {
+  if (pm.shift < 0) return (int64_t)row * pm.max_blocks + b;
+  return phys_entry(pm, pm.table[(int64_t)row * pm.pages_per_row + (b >> pm.shift)], b);
+}
+
 __device__ __forceinline__ uint32_t ord_key(float s) {
   // negative: every bit flipped; otherwise the sign bit set (one xor with
   // the sign spread over the word, sign bit forced)

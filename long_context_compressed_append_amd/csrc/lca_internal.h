@@ -33,6 +33,24 @@ enum TuneId {
 };
 int tuning(TuneId id);
 
+// The layer's entry placement for the kernels (the PageMap of lca_device.h):
+// fills table, max_blocks, pages_per_row, shift, pool_pages.
+template <class PM>
+inline PM page_map_of(const lca_layer* L) {
+  PM pm{};
+  pm.table = L->page_table;
+  pm.max_blocks = L->max_blocks;
+  pm.shift = -1;
+  if (L->page_blocks > 0) {
+    int sh = 0;
+    while ((1 << sh) < L->page_blocks) sh++;
+    pm.shift = sh;
+    pm.pages_per_row = (int32_t)(L->max_blocks / L->page_blocks);
+    pm.pool_pages = (int32_t)L->pool_pages;
+  }
+  return pm;
+}
+
 // Records HIP events around one launch when a timing session for `id` is open.
 struct TimedLaunch {
   TimedLaunch(KernelId id, hipStream_t s);

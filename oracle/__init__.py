@@ -46,11 +46,12 @@ P = C.c_void_p
 
 class OrcLayer(C.Structure):
     _fields_ = [("batch", C.c_int32), ("ratio", C.c_int32), ("window", C.c_int32),
-                ("ring", C.c_int32), ("has_indexer", C.c_int32), ("pad0", C.c_int32),
+                ("ring", C.c_int32), ("has_indexer", C.c_int32), ("page_blocks", C.c_int32),
                 ("max_blocks", C.c_int64),
                 ("seq_len", P), ("nope", P), ("rope", P), ("kv_scale", P),
                 ("idx_code", P), ("idx_scale", P), ("ring_kv", P), ("ring_gate", P),
-                ("ring_ikey", P), ("ring_igate", P), ("pos_bias", P), ("ipos_bias", P)]
+                ("ring_ikey", P), ("ring_igate", P), ("pos_bias", P), ("ipos_bias", P),
+                ("page_table", P), ("pool_pages", C.c_int64)]
 
 
 def _setup(L):
@@ -75,6 +76,8 @@ def _setup(L):
     L.orc_make_entry.argtypes = [P, P, P, P]
     L.orc_make_idx.argtypes = [P, P, P]
     L.orc_compress_append.argtypes = [C.POINTER(OrcLayer), P, P, P, P, C.c_int]
+    L.orc_entry_index.restype = C.c_long
+    L.orc_entry_index.argtypes = [C.POINTER(OrcLayer), C.c_int, C.c_long]
     L.orc_index_score.restype = C.c_float
     L.orc_index_score.argtypes = [P, P, P, C.c_int, P, P, C.POINTER(C.c_int)]
     L.orc_topk_select.argtypes = [P, C.c_int, C.c_int, P]
@@ -99,7 +102,13 @@ def _f32(x):
 
 
 def nthreads_default():
-    return max(1, len(os.sched_getaffinity(0)))
+    """The threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (a job's share of a shared host)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 # ---------------------------------------------------------------- formats
@@ -186,10 +195,13 @@ def layer_struct(L):
     s = OrcLayer()
     s.batch, s.ratio, s.window, s.ring = L["batch"], L["ratio"], L["window"], L["ring"]
     s.has_indexer, s.max_blocks = L["has_indexer"], L["max_blocks"]
+    s.page_blocks, s.pool_pages = int(L.get("page_blocks", 0)), int(L.get("pool_pages", 0))
     for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
-              "ring_gate", "ring_ikey", "ring_igate", "pos_bias", "ipos_bias"):
+              "ring_gate", "ring_ikey", "ring_igate", "pos_bias", "ipos_bias", "page_table"):
         a = L.get(f)
         setattr(s, f, _p(a) if a is not None and a.size else None)
+    if s.page_blocks:
+        assert L["page_table"].dtype == np.int32 and L["page_table"].flags["C_CONTIGUOUS"]
     return s
 
 
@@ -290,12 +302,22 @@ def hca_attend(L, q, scale, nthreads=None):
 
 
 def row_view(L, row):
-    """A one-row layer dict sharing memory with row `row` of L."""
+    """A one-row layer dict sharing memory with row `row` of L (a paged
+    layer's view keeps the whole page pool and the row's page table)."""
     V = dict(L)
     V["batch"] = 1
-    for f in ("seq_len",):
-        V[f] = L[f][row:row + 1]
-    for f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv", "ring_gate",
-              "ring_ikey", "ring_igate"):
+    V["seq_len"] = L["seq_len"][row:row + 1]
+    planes = ["ring_kv", "ring_gate", "ring_ikey", "ring_igate"]
+    if L.get("page_blocks", 0):
+        V["page_table"] = L["page_table"][row:row + 1]
+    else:
+        planes += ["nope", "rope", "kv_scale", "idx_code", "idx_scale"]
+    for f in planes:
         V[f] = L[f][row:row + 1]
     return V
+
+
+def entry_index(L, row, b):
+    """Where entry b of row `row` lives in L's entry planes (-1: unmapped page)."""
+    s = layer_struct(L)
+    return int(lib().orc_entry_index(C.byref(s), int(row), int(b)))

@@ -243,6 +243,19 @@ void orc_make_idx(const float *y, uint8_t *code, uint8_t *e8m0) {
  * ring at slot position % R ([ARCH] 2.1: the window store holds a fixed number
  * of raw tokens and overwrites cyclically), then seq_len grows by n.  Old
  * tokens of a block that straddles calls come from the ring. */
+/* Entry placement.  Contiguous layers give each row max_blocks consecutive
+ * entries.  Paged layers split a row's entries into runs of page_blocks,
+ * run j of row r being pool page page_table[r][j] (the library's layout
+ * rule for variable-length batches; it is storage only, so every result
+ * equals the contiguous layer's with the same entries). */
+long orc_entry_index(const orc_layer *L, int row, long b) {
+  if (L->page_blocks == 0) return (long)row * L->max_blocks + b;
+  const long pages_per_row = L->max_blocks / L->page_blocks;
+  const long page = L->page_table[(long)row * pages_per_row + b / L->page_blocks];
+  if (page < 0 || page >= L->pool_pages) return -1;
+  return page * L->page_blocks + b % L->page_blocks;
+}
+
 int orc_compress_append(orc_layer *L, const uint16_t *kv, const float *gate,
                         const float *ikey, const float *igate, int n) {
   const int m = L->ratio, R = L->ring, C = ORC_KV_DIM, CI = ORC_IDX_DIM;
@@ -280,8 +293,9 @@ int orc_compress_append(orc_layer *L, const uint16_t *kv, const float *gate,
           memcpy(ig + (long)i * CI, src_ig, sizeof(float) * CI);
         }
       }
+      long e = orc_entry_index(L, b, bk);
+      if (e < 0) { rc = -8; break; }
       orc_pool_f32(m, C, xs, C, zs, C, L->pos_bias, y);
-      long e = (long)b * L->max_blocks + bk;
       orc_make_entry(y, L->nope + e * ORC_NOPE_DIM, L->rope + e * ORC_ROPE_DIM,
                      L->kv_scale + e * ORC_SCALE_STRIDE);
       if (L->has_indexer) {
@@ -397,7 +411,8 @@ int orc_indexer_scores(const orc_layer *L, int row, int qi, int n_q,
   for (int h = 0; h < H; h++) orc_make_idx(q + h * ORC_IDX_DIM, qcode + h * 32, qe + h * 2);
   int inexact = 0;
   for (long b = 0; b < nv; b++) {
-    long e = (long)row * L->max_blocks + b;
+    long e = orc_entry_index(L, row, b);
+    if (e < 0) return -8;
     scores[b] = orc_index_score(qcode, qe, w, H, L->idx_code + e * 32, L->idx_scale + e * 2,
                                 &inexact);
   }
@@ -502,13 +517,15 @@ void orc_attend_keys(const uint16_t *q, int H, int n_keys, const double *keys,
   free(lg);
 }
 
-static void orc_entry_vector(const orc_layer *L, int row, long b, double *k) {
-  long e = (long)row * L->max_blocks + b;
+static int orc_entry_vector(const orc_layer *L, int row, long b, double *k) {
+  long e = orc_entry_index(L, row, b);
+  if (e < 0) return -8;
   const uint8_t *nope = L->nope + e * ORC_NOPE_DIM;
   const float *sc = L->kv_scale + e * ORC_SCALE_STRIDE;
   const uint16_t *rope = L->rope + e * ORC_ROPE_DIM;
   for (int c = 0; c < ORC_NOPE_DIM; c++) k[c] = orc_e4m3_value(nope[c]) * (double)sc[c / ORC_GROUP];
   for (int c = 0; c < ORC_ROPE_DIM; c++) k[ORC_NOPE_DIM + c] = orc_bf16_value(rope[c]);
+  return 0;
 }
 
 static void orc_window_vector(const orc_layer *L, int row, long pos, double *k) {
@@ -529,9 +546,16 @@ static void *orc_attend_worker(void *arg) {
     if (J->mode == 0) {
       const int32_t *sel = J->topk + (long)t * J->k;
       for (int i = 0; i < J->k; i++)
-        if (sel[i] >= 0 && sel[i] < nv) orc_entry_vector(L, row, sel[i], keys + (nk++) * ORC_KV_DIM);
+        if (sel[i] >= 0 && sel[i] < nv && orc_entry_vector(L, row, sel[i], keys + (nk++) * ORC_KV_DIM)) {
+          orc_set_err(J, -8);
+          nk--;
+        }
     } else {
-      for (long b = 0; b < nv; b++) orc_entry_vector(L, row, b, keys + (nk++) * ORC_KV_DIM);
+      for (long b = 0; b < nv; b++)
+        if (orc_entry_vector(L, row, b, keys + (nk++) * ORC_KV_DIM)) {
+          orc_set_err(J, -8);
+          nk--;
+        }
     }
     long w0 = p - L->window + 1;
     if (w0 < 0) w0 = 0;

@@ -68,23 +68,33 @@ void orc_pool_f64(int m, int C, const float *x, long x_stride,
 void orc_make_entry(const float *y, uint8_t *nope, uint16_t *rope, float *scale);
 void orc_make_idx(const float *y, uint8_t *code, uint8_t *e8m0);
 
-/* One layer's cache, host memory, same plane layout as the library's. */
+/* One layer's cache, host memory, same plane layout as the library's.
+ * Entry planes: [B][max_blocks][...] when page_blocks is 0; otherwise a pool
+ * of pool_pages pages of page_blocks entries, [pool_pages * page_blocks][...],
+ * and page_table[B][max_blocks / page_blocks] names the pool page holding
+ * each run of page_blocks consecutive entries of a row (-1: none). */
 typedef struct orc_layer {
-  int32_t batch, ratio, window, ring, has_indexer, pad0;
+  int32_t batch, ratio, window, ring, has_indexer, page_blocks;
   int64_t max_blocks;
   int32_t *seq_len;     /* [B] */
-  uint8_t *nope;        /* [B][max_blocks][448] */
-  uint16_t *rope;       /* [B][max_blocks][64] */
-  float *kv_scale;      /* [B][max_blocks][8], slot 7 unused (0) */
-  uint8_t *idx_code;    /* [B][max_blocks][32] */
-  uint8_t *idx_scale;   /* [B][max_blocks][2] */
+  uint8_t *nope;        /* entry planes (above): 448 e4m3 codes per entry */
+  uint16_t *rope;       /* 64 bf16 per entry */
+  float *kv_scale;      /* 8 per entry, slot 7 unused (0) */
+  uint8_t *idx_code;    /* 32 per entry */
+  uint8_t *idx_scale;   /* 2 per entry */
   uint16_t *ring_kv;    /* [B][R][512] */
   float *ring_gate;     /* [B][R][512] */
   float *ring_ikey;     /* [B][R][64] */
   float *ring_igate;    /* [B][R][64] */
   const float *pos_bias;  /* [m][512] */
   const float *ipos_bias; /* [m][64] */
+  const int32_t *page_table;  /* [B][max_blocks / page_blocks] when paged */
+  int64_t pool_pages;
 } orc_layer;
+
+/* Where entry b of a row lives in the entry planes, or -1 when it lies on a
+ * page the table does not map (functions meeting one return -8). */
+long orc_entry_index(const orc_layer *L, int row, long b);
 
 int orc_compress_append(orc_layer *L, const uint16_t *kv, const float *gate,
                         const float *ikey, const float *igate, int n);

@@ -21,7 +21,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (bf16_bits, bf16_to_f32, abs_normal_f32, bf16_normal, distinct_choice, e2m1_code_image,
-               e4m3_code_image, e8m0_image, fp8_scale_image, key, normal_f32, randbytes)
+               e4m3_code_image, e8m0_image, fp8_scale_image, key, normal_f32, randbytes, u64)
 
 KV, NOPE, ROPE, IDX = 512, 448, 64, 64
 
@@ -157,3 +157,77 @@ def outlier_tokens(tok, ch, factor=20.0):
     """The same stress on a batch of raw tokens (in place)."""
     tok["kv"][:, :, ch] = bf16_bits(bf16_to_f32(tok["kv"][:, :, ch]) * np.float32(factor))
     return tok
+
+
+ENTRY_PLANES = ("nope", "rope", "kv_scale", "idx_code", "idx_scale")
+
+
+def paginate(L, seed, page_blocks, reserve_blocks=0, spare_pages=3):
+    """The same layer with paged entry planes: each row maps the pages its
+    entries need (its current blocks plus `reserve_blocks` more, up to
+    max_blocks), every row's pages drawn from one pool in a seeded random
+    order; the remaining logical pages are unmapped (-1).  `spare_pages`
+    extra pool pages hold random codes that no row maps (a wrong page read
+    shows up).  Entry planes become [pool_pages * page_blocks][...]; the
+    other planes are copies."""
+    PB, B, MB, m = int(page_blocks), L["batch"], L["max_blocks"], L["ratio"]
+    assert MB % PB == 0
+    ppr = MB // PB
+    need = [min(ppr, (int(L["seq_len"][r]) // m + reserve_blocks + PB - 1) // PB) for r in range(B)]
+    pool = sum(need) + spare_pages
+    order = np.argsort(u64(key(seed, "page_order", B, PB), pool), kind="stable").astype(np.int32)
+    P = dict(L)
+    for f in ("seq_len", "ring_kv", "ring_gate", "ring_ikey", "ring_igate"):
+        P[f] = L[f].copy()                       # appends mutate these in place
+    P["page_blocks"], P["pool_pages"] = PB, pool
+    table = np.full((B, ppr), -1, np.int32)
+    E = pool * PB
+    has_idx = bool(L["has_indexer"])
+    P["nope"] = e4m3_code_image(seed, "pool_nope", E * NOPE, PB).reshape(E, NOPE)
+    P["rope"] = bf16_normal(seed, "pool_rope", (E, ROPE), PB)
+    sc = np.zeros((E, 8), np.float32)
+    sc[:, :7] = fp8_scale_image(seed, "pool_scale", E * 7, PB).reshape(E, 7)
+    P["kv_scale"] = sc
+    if has_idx:
+        P["idx_code"] = e2m1_code_image(seed, "pool_idx", E * 32, PB).reshape(E, 32)
+        P["idx_scale"] = e8m0_image(seed, "pool_iscale", E * 2, PB).reshape(E, 2)
+    else:
+        P["idx_code"] = np.zeros((0, 32), np.uint8)
+        P["idx_scale"] = np.zeros((0, 2), np.uint8)
+    nxt = 0
+    for r in range(B):
+        for j in range(need[r]):
+            pg = int(order[nxt])
+            nxt += 1
+            table[r, j] = pg
+            src = slice(j * PB, (j + 1) * PB)
+            dst = slice(pg * PB, (pg + 1) * PB)
+            for f in ENTRY_PLANES:
+                if f.startswith("idx") and not has_idx:
+                    continue
+                P[f][dst] = L[f][r, src]
+    P["page_table"] = table
+    return P
+
+
+def unpaginate(P):
+    """The contiguous layer holding a paged layer's mapped entries (unmapped
+    pages read as zeros)."""
+    B, MB, PB = P["batch"], P["max_blocks"], P["page_blocks"]
+    L = dict(P)
+    for k in ("page_blocks", "pool_pages", "page_table"):
+        L.pop(k)
+    for f in ENTRY_PLANES:
+        src = P.get(f)
+        if src is None:
+            continue
+        if src.shape[0] == 0:
+            L[f] = np.zeros((B, 0) + src.shape[1:], src.dtype)
+            continue
+        out = np.zeros((B, MB) + src.shape[1:], src.dtype)
+        for r in range(B):
+            for j, pg in enumerate(P["page_table"][r]):
+                if pg >= 0:
+                    out[r, j * PB:(j + 1) * PB] = src[pg * PB:(pg + 1) * PB]
+        L[f] = out
+    return L

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version():
     L = _lib()
-    assert L.lca_abi_version() == 2
+    assert L.lca_abi_version() == 3
 
 
 def _layer(**kw):
@@ -59,6 +59,15 @@ def _layer(**kw):
     (dict(nope=0x10001), -1),       # misaligned
     (dict(has_indexer=1), -1),      # indexer planes missing
     (dict(len_min=5, len_max=2), -1),
+    # paged entry planes
+    (dict(page_table=0x10000), -1),                                           # table without pages
+    (dict(page_blocks=32, max_blocks=128, page_table=0x10000, pool_pages=4), -2),    # below 64
+    (dict(page_blocks=96, max_blocks=192, page_table=0x10000, pool_pages=4), -2),    # not a power of two
+    (dict(page_blocks=64, max_blocks=100, page_table=0x10000, pool_pages=4), -1),    # MB not a multiple
+    (dict(page_blocks=64, max_blocks=128, page_table=None, pool_pages=4), -1),
+    (dict(page_blocks=64, max_blocks=128, page_table=0x10002, pool_pages=4), -1),    # misaligned table
+    (dict(page_blocks=64, max_blocks=128, page_table=0x10000, pool_pages=0), -1),
+    (dict(page_blocks=65536, max_blocks=65536, page_table=0x10000, pool_pages=1 << 15), -2),  # pool >= 2^31
 ])
 def test_layer_validation(kw, code):
     L = _lib()
@@ -91,6 +100,9 @@ def test_call_validation():
                             None) == -2
     # n == 0 is a no-op
     assert L.lca_compress_append(C.byref(s), p, p, None, None, 0, None) == 0
+    # a valid paged layer passes validation
+    s4 = _layer(page_blocks=64, max_blocks=128, page_table=0x10000, pool_pages=3)
+    assert L.lca_compress_append(C.byref(s4), p, p, None, None, 0, None) == 0, L.lca_last_error()
 
 
 def test_workspace_queries_are_pure():

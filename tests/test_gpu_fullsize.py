@@ -239,77 +239,181 @@ def _device_row(lay, r):
     return out
 
 
-def test_interleaved_1m_fullsize():
-    """8 rows at a 1048575-token context, 8 CSA layers (16 heads, 4 indexer
-    heads, k = 64) interleaved with 8 HCA layers (64 heads), 26 outlier
-    channels x20; six decode steps (step 0 finalises CSA block 262143 and HCA
-    entry 8191, step 4 finalises CSA block 262144).  Two sampled rows of the
-    first CSA and the last HCA layer are followed by the oracle through every
-    step and checked at the end."""
-    lca = _lca()
-    B, ctx, P, H_c, HI, k, H_h, W = 8, 1 << 20, 8, 16, 4, 64, 64, 128
-    seed = 1005
-    say("interleaved_1m fullsize B", B, "pairs", P, "seed", seed)
+INTERLEAVED_B, INTERLEAVED_CTX, INTERLEAVED_P, INTERLEAVED_W, INTERLEAVED_SEED = 8, 1 << 20, 8, 128, 1005
+# CSA layer shapes: (heads, indexer heads, k); the HCA layers have 64 heads
+INTERLEAVED_SHAPES = {"narrow": (16, 4, 64), "wide": (64, 16, 512)}
+
+
+@pytest.fixture(scope="module")
+def interleaved_images():
+    """One host image per layer kind (8 rows at a 1048575-token context, 26
+    outlier channels x20), shared by the interleaved cases."""
+    B, ctx, W, seed = INTERLEAVED_B, INTERLEAVED_CTX, INTERLEAVED_W, INTERLEAVED_SEED
     images, ch = {}, {}
     for kind, m, has_idx in (("csa", 4, 1), ("hca", 128, 0)):
         ref = SL.make_layer(seed, kind, B, m, W, 256, has_idx, ctx // m + 64, [ctx - 1] * B)
         ch[kind] = SL.outlier_channels(seed, kind, 0)
         SL.apply_outliers(ref, ch[kind])
         images[kind] = ref
-    layers = {kind: [lca.Layer.from_host(images[kind]) for _ in range(P)] for kind in ("csa", "hca")}
+    return images, ch
+
+
+def _device_layers(lca, image, P):
+    """P device layers holding the same image (one upload, device copies)."""
+    base = lca.Layer.from_host(image)
+    out = [base]
+    for _ in range(P - 1):
+        lay = lca.Layer(base.batch, base.ratio, base.window, base.ring, base.has_indexer, base.max_blocks,
+                        pos_bias=image["pos_bias"], ipos_bias=image.get("ipos_bias"))
+        for f in lca.Layer.PLANES:
+            src = getattr(base, f)
+            if src is not None:
+                getattr(lay, f).copy_(src)
+        lay.len_min, lay.len_max = base.len_min, base.len_max
+        out.append(lay)
+    return out
+
+
+@pytest.mark.parametrize("shape,launch", [("narrow", "eager"), ("narrow", "graph"), ("wide", "graph")])
+def test_interleaved_1m_fullsize(interleaved_images, shape, launch):
+    """8 CSA layers interleaved with 8 HCA layers (64 heads) at a 1048575-token
+    context, 8 rows, six decode steps: step 0 finalises CSA block 262143 and
+    HCA entry 8191, step 4 CSA block 262144.  The steps run eagerly, or as
+    replays of one captured HIP graph of a whole step (tokens and queries
+    copied into the graph's input buffers between replays, plans sized for
+    the last step's length).  Two sampled rows of the first CSA and the last
+    HCA layer follow the oracle, and after every step their finalised
+    entries, the CSA top-k set and both attention outputs are checked."""
+    from concurrent.futures import ThreadPoolExecutor
+    lca = _lca()
+    images, ch = interleaved_images
+    B, ctx, P, W, seed = INTERLEAVED_B, INTERLEAVED_CTX, INTERLEAVED_P, INTERLEAVED_W, INTERLEAVED_SEED
+    H_c, HI, k = INTERLEAVED_SHAPES[shape]
+    H_h, steps = 64, 6
+    say("interleaved_1m fullsize", shape, launch, "B", B, "pairs", P, "seed", seed)
+    layers = {kind: _device_layers(lca, images[kind], P) for kind in ("csa", "hca")}
     rows = (2, 7)
     track = {("csa", 0): {r: _row_copy(images["csa"], r) for r in rows},
              ("hca", P - 1): {r: _row_copy(images["hca"], r) for r in rows}}
-    del images
-    steps = 6
-    for s in range(steps):
-        say("interleaved step", s)
+
+    def host_inputs(s):
         qc = SL.queries(seed, "csaq", B, 1, H_c, HI, step=s)
         qh = SL.queries(seed, "hcaq", B, 1, H_h, step=s)
+        tc = [SL.outlier_tokens(SL.tokens(seed, f"csa{l}", B, 1, 1, step=s), ch["csa"]) for l in range(P)]
+        th = [SL.outlier_tokens(SL.tokens(seed, f"hca{l}", B, 1, 0, step=s), ch["hca"]) for l in range(P)]
+        return qc, qh, tc, th
+
+    # device input buffers (the graph reads these), refilled before every step
+    qc0, qh0, tc0, th0 = host_inputs(0)
+    d_qc = {kk: _dev(v) for kk, v in qc0.items()}
+    d_qh = _dev(qh0["q"])
+    d_tc = [{kk: _dev(v) for kk, v in t.items()} for t in tc0]
+    d_th = [{kk: _dev(v) for kk, v in t.items()} for t in th0]
+    topk = [torch.empty((B, 1, k), dtype=torch.int32, device="cuda") for _ in range(P)]
+    out_c = [torch.empty((B, 1, H_c, 512), dtype=torch.float32, device="cuda") for _ in range(P)]
+    out_h = [torch.empty((B, 1, H_h, 512), dtype=torch.float32, device="cuda") for _ in range(P)]
+    all_layers = layers["csa"] + layers["hca"]
+
+    def launch_step(plan_len=None):
         for l in range(P):
-            tc = SL.outlier_tokens(SL.tokens(seed, f"csa{l}", B, 1, 1, step=s), ch["csa"])
-            th = SL.outlier_tokens(SL.tokens(seed, f"hca{l}", B, 1, 0, step=s), ch["hca"])
             c, h = layers["csa"][l], layers["hca"][l]
-            lca.compress_append(c, _dev(tc["kv"]), _dev(tc["gate"]), _dev(tc["ikey"]), _dev(tc["igate"]))
-            topk = lca.indexer_topk(c, _dev(qc["iq"]), _dev(qc["iw"]), k)
-            out_c = lca.csa_attend(c, _dev(qc["q"]), topk, float(SCALE))
-            lca.compress_append(h, _dev(th["kv"]), _dev(th["gate"]))
-            out_h = lca.hca_attend(h, _dev(qh["q"]), float(SCALE))
-            for (kind, tl), views in track.items():
-                if tl != l:
-                    continue
-                t = tc if kind == "csa" else th
-                for r, V in views.items():
-                    if kind == "csa":
-                        oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1], t["ikey"][r:r + 1],
-                                               t["igate"][r:r + 1])
-                    else:
-                        oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1])
-            if l == 0:
-                csa_topk, csa_out = topk, out_c
-            if l == P - 1:
-                hca_out = out_h
+            lca.compress_append(c, d_tc[l]["kv"], d_tc[l]["gate"], d_tc[l]["ikey"], d_tc[l]["igate"])
+            if plan_len is not None:
+                c.len_max = plan_len
+            lca.indexer_topk(c, d_qc["iq"], d_qc["iw"], k, out=topk[l])
+            lca.csa_attend(c, d_qc["q"], topk[l], float(SCALE), out=out_c[l])
+            lca.compress_append(h, d_th[l]["kv"], d_th[l]["gate"])
+            if plan_len is not None:
+                h.len_max = plan_len
+            lca.hca_attend(h, d_qh, float(SCALE), out=out_h[l])
+
+    graph = None
+    if launch == "graph":
+        final_len = ctx - 1 + steps
+        saved = [(x.len_min, x.len_max) for x in all_layers]
+        for x in all_layers:      # workspaces sized for the last step before capture
+            x.len_max = final_len
+        for c in layers["csa"]:
+            c.indexer_workspace(1, lca.indexer_workspace_bytes(c, 1, HI, k))
+            c.workspace(lca.attend_workspace_bytes(c, 1, H_c, k), "attend")
+        for h in layers["hca"]:
+            h.workspace(lca.attend_workspace_bytes(h, 1, H_h, 0), "attend")
+        for x, (a, b) in zip(all_layers, saved):
+            x.len_min, x.len_max = a, b
         torch.cuda.synchronize()
-    got_topk, got_c, got_h = csa_topk.cpu().numpy(), csa_out.cpu().numpy(), hca_out.cpu().numpy()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            launch_step(plan_len=final_len)
+        torch.cuda.synchronize()
+        for x, (a, b) in zip(all_layers, saved):      # capture ran nothing on the device
+            x.len_min, x.len_max = a, b
+
+    def oracle_append(kind, V, t, r):
+        if kind == "csa":
+            oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1], t["ikey"][r:r + 1],
+                                   t["igate"][r:r + 1])
+        else:
+            oracle.compress_append(V, t["kv"][r:r + 1], t["gate"][r:r + 1])
+
+    def check_csa(V, r, qc, got_topk, got_out, dev_row):
+        flips = 0
+        n = int(V["seq_len"][0])
+        if n % 4 == 0:
+            flips += _check_finalised(dev_row, V, 0, n // 4 - 1, 4, True)
+        scores = oracle.indexer_scores(V, 0, 0, 1, qc["iq"][r:r + 1], qc["iw"][r:r + 1])
+        check_topk(got_topk[r, 0], oracle.topk_select(scores, k), scores, k)
+        wo = oracle.csa_attend(V, qc["q"][r:r + 1], got_topk[r:r + 1], SCALE, nthreads=1)
+        return flips, attn_rel_err(got_out[r:r + 1], wo)
+
+    def check_hca(V, r, qh, got_out, dev_row):
+        flips = 0
+        n = int(V["seq_len"][0])
+        if n % 128 == 0:
+            flips += _check_finalised(dev_row, V, 0, n // 128 - 1, 128, False)
+        wo = oracle.hca_attend(V, qh["q"][r:r + 1], SCALE, nthreads=1)
+        return flips, attn_rel_err(got_out[r:r + 1], wo)
+
     flips = 0
-    for r, V in track[("csa", 0)].items():
-        say("interleaved csa layer 0 row", r)
-        dev_row = _device_row(layers["csa"][0], r)
-        for b in (ctx // 4 - 1, ctx // 4):
-            flips += _check_finalised(dev_row, V, 0, b, 4, True)
-        want = oracle.indexer_topk(V, qc["iq"][r:r + 1], qc["iw"][r:r + 1], k)
-        check_topk(got_topk[r, 0], want[0, 0],
-                   oracle.indexer_scores(V, 0, 0, 1, qc["iq"][r:r + 1], qc["iw"][r:r + 1]), k)
-        wo = oracle.csa_attend(V, qc["q"][r:r + 1], got_topk[r:r + 1], SCALE)
-        err = attn_rel_err(got_c[r:r + 1], wo)
-        print("csa row", r, "attention max rel err", err, flush=True)
-        assert err <= ATTN_TOL
-    for r, V in track[("hca", P - 1)].items():
-        say("interleaved hca layer", P - 1, "row", r)
-        dev_row = _device_row(layers["hca"][P - 1], r)
-        flips += _check_finalised(dev_row, V, 0, ctx // 128 - 1, 128, False)
-        wo = oracle.hca_attend(V, qh["q"][r:r + 1], SCALE)
-        err = attn_rel_err(got_h[r:r + 1], wo)
-        print("hca row", r, "attention max rel err", err, flush=True)
-        assert err <= ATTN_TOL
-    assert flips <= 4
+    pool = ThreadPoolExecutor(max_workers=2 * len(rows))
+    try:
+        for s in range(steps):
+            say("interleaved step", s, shape, launch)
+            qc, qh, tc, th = host_inputs(s)
+            for kk, v in qc.items():
+                d_qc[kk].copy_(_dev(v))
+            d_qh.copy_(_dev(qh["q"]))
+            for l in range(P):
+                for kk, v in tc[l].items():
+                    d_tc[l][kk].copy_(_dev(v))
+                for kk, v in th[l].items():
+                    d_th[l][kk].copy_(_dev(v))
+            if graph is None:
+                launch_step()
+            else:
+                graph.replay()
+                for x in all_layers:
+                    x.len_min += 1
+                    x.len_max += 1
+            torch.cuda.synchronize()
+            assert all(int(x.seq_len[0].item()) == ctx + s for x in (layers["csa"][0], layers["hca"][-1]))
+            got_topk, got_c = topk[0].cpu().numpy(), out_c[0].cpu().numpy()
+            got_h = out_h[P - 1].cpu().numpy()
+            dev_c = {r: _device_row(layers["csa"][0], r) for r in rows}
+            dev_h = {r: _device_row(layers["hca"][P - 1], r) for r in rows}
+            for r in rows:
+                oracle_append("csa", track[("csa", 0)][r], tc[0], r)
+                oracle_append("hca", track[("hca", P - 1)][r], th[P - 1], r)
+            jobs = [pool.submit(check_csa, track[("csa", 0)][r], r, qc, got_topk, got_c, dev_c[r]) for r in rows]
+            jobs += [pool.submit(check_hca, track[("hca", P - 1)][r], r, qh, got_h, dev_h[r]) for r in rows]
+            for j, r in zip(jobs, rows + rows):
+                f, err = j.result()
+                flips += f
+                print("step", s, "row", r, "attention max rel err", err, flush=True)
+                assert err <= ATTN_TOL, (s, r)
+            assert all(x.status() == 0 for x in all_layers)
+    finally:
+        pool.shutdown()
+        del graph
+    assert flips <= 8
