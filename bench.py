@@ -74,6 +74,81 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measure_peaks():
+    """The chip's ceilings measured here (libpeak.so): matrix-instruction
+    issue rates with register operands (fp16 32x32x16, fp8 and fp4
+    32x32x64), and HBM copy and read rates over 2 GiB buffers (far above the
+    256 MB Infinity Cache).  Best of 3 timed launches each, HIP events on the
+    launching stream."""
+    import ctypes as C
+    import torch
+    lib = C.CDLL(os.path.join(ROOT, "long_context_compressed_append_amd", "libpeak.so"))
+    P = C.c_void_p
+    lib.peak_mfma.argtypes = [C.c_int, C.c_int, C.c_int, P, P]
+    lib.peak_copy.argtypes = [P, P, C.c_int64, C.c_int, P]
+    lib.peak_read.argtypes = [P, C.c_int64, C.c_int, P, P]
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+
+    def best_ms(launch):
+        launch()                                          # warm
+        ts = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts)
+
+    out = {}
+    blocks, iters = 2048, 2000                      # 8 wavefronts per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for kind, name, flops in ((0, "mfma_fp16_tflops", 32768), (1, "mfma_fp8_tflops", 131072),
+                              (2, "mfma_fp4_tflops", 131072)):
+        def go(kind=kind):
+            if lib.peak_mfma(kind, blocks, iters, P(sink.data_ptr()), sp) != 0:
+                raise RuntimeError("peak_mfma launch failed")
+        ms = best_ms(go)
+        out[name] = round(blocks * 4 * iters * 4 * flops / (ms * 1e-3) / 1e12, 1)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    words = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
+
+    def cp():
+        if lib.peak_copy(P(src.data_ptr()), P(dst.data_ptr()), nbytes, 16384, sp) != 0:
+            raise RuntimeError("peak_copy launch failed")
+
+    def rd():
+        if lib.peak_read(P(src.data_ptr()), nbytes, 16384, P(words.data_ptr()), sp) != 0:
+            raise RuntimeError("peak_read launch failed")
+    out["hbm_copy_gbs"] = round(2 * nbytes / (best_ms(cp) * 1e-3) / 1e9, 1)
+    out["hbm_read_gbs"] = round(nbytes / (best_ms(rd) * 1e-3) / 1e9, 1)
+    del src, dst, words, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def emit(res, args):
+    """Print the JSON line, with the ceilings measured in this run beside the
+    published peak the roofline uses."""
+    peaks = getattr(args, "peaks", None)
+    if peaks:
+        roof = res["roofline"]
+        if roof["bound"] == "hbm":
+            roof["measured_peak"] = peaks["hbm_read_gbs"]
+        elif roof["kernel"] == "indexer_score":
+            roof["measured_peak"] = peaks["mfma_fp8_tflops"]
+        else:
+            roof["measured_peak"] = peaks["mfma_fp16_tflops"]
+        roof["frac_of_measured"] = round(roof["achieved"] / roof["measured_peak"], 4)
+        res["config"]["measured_peaks"] = peaks
+    print(json.dumps(res), flush=True)
+
+
 def spread_us(durations_ms):
     """mean / p10 / p50 / p90 of per-launch durations, in microseconds."""
     d = np.asarray(durations_ms, np.float64) * 1e3
@@ -173,6 +248,30 @@ def counter_traffic(dominant, workload):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != src_hash:
         return None
     return nbytes
+
+
+def valu_bound_us(workload):
+    """The scoring kernel's VALU issue bound (us) from the committed SQ
+    counter summary, or None when it is missing or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        bound = float(fields["valu_bound_us"])
+        src_name, src_hash = fields["valu_source"].split()
+    except (KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "long_context_compressed_append_amd", "csrc", src_name)
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != src_hash:
+        return None
+    return bound
 
 
 def interleaved_bytes(B, ctx, H_c, HI, k, H_h, W):
@@ -285,6 +384,9 @@ def run_prefill(args):
                 "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                 "kernel_avg_us": score_us, "kernel_us": spreads.get("indexer_score"),
                 "flops_per_launch": flops}
+        vb = valu_bound_us(args.workload)
+        roof["valu_bound_us"] = vb          # the exact epilogue's VALU issue time (SQ counters)
+        roof["frac_of_valu_bound"] = round(vb / score_us, 4) if vb and score_us else None
     else:
         roof = {"kernel": "attend", "bound": "mfma", "achieved": round(att_tflops, 1),
                 "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -327,7 +429,7 @@ def run_prefill(args):
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res), flush=True)
+    emit(res, args)
 
 
 def prefill_cpu_baseline(ref, tok, Q, prior, n, m, k, csa=True):
@@ -580,7 +682,7 @@ def run_interleaved(args):
         },
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res))
+    emit(res, args)
 
 
 def interleaved_cpu_baseline(images, qc, qh, tok, k, P):
@@ -639,6 +741,7 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(INTERLEAVED) + sorted(PREFILL))
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-ceiling microbenchmarks")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
@@ -651,6 +754,13 @@ def main():
         print("bench.py measures one GPU: there is no multi-GPU path (decode rows would shard "
               "across GPUs with no exchange).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    args.peaks = None
+    if not args.no_peaks:
+        import torch
+        torch.cuda.set_device(0)
+        args.peaks = measure_peaks()
+        log("measured ceilings", args.peaks)
 
     if args.workload in INTERLEAVED:
         return run_interleaved(args)
@@ -840,7 +950,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res))
+    emit(res, args)
 
 
 if __name__ == "__main__":
