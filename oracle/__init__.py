@@ -241,8 +241,12 @@ def topk_select(scores, k):
 
 
 def indexer_scores(L, row, qi, n_q, iq, iw):
+    """Scores of query qi of row `row`: iq [rows][n_q][H][64] and iw
+    [rows][n_q][H] hold that row (row < rows)."""
     iq, iw = _f32(iq), _f32(iw)
     H = iw.shape[-1]
+    if not (0 <= row < iq.shape[0] and iq.shape[:3] == iw.shape and iq.shape[1] == n_q and 0 <= qi < n_q):
+        raise ValueError(f"indexer_scores: row {row}, query {qi} not in iq {iq.shape} / iw {iw.shape}")
     s = layer_struct(L)
     out = np.zeros(L["max_blocks"] + 1, np.float32)
     nv = C.c_int(0)

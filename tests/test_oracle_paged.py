@@ -62,8 +62,8 @@ def test_paged_indexer_equals_contiguous():
         b = oracle.indexer_topk(P, Q["iq"], Q["iw"], k)
         assert (a == b).all()
     for r in range(len(lengths)):
-        sa = oracle.indexer_scores(L, r, 2, 3, Q["iq"][r:r + 1], Q["iw"][r:r + 1])
-        sb = oracle.indexer_scores(P, r, 2, 3, Q["iq"][r:r + 1], Q["iw"][r:r + 1])
+        sa = oracle.indexer_scores(L, r, 2, 3, Q["iq"], Q["iw"])
+        sb = oracle.indexer_scores(P, r, 2, 3, Q["iq"], Q["iw"])
         assert sa.view(np.uint32).tolist() == sb.view(np.uint32).tolist()
 
 
