@@ -198,11 +198,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // (from the top down) and a wave scan gives the keys above it.  Wave-uniform.
 // kCoherent: h is a histogram in global memory that other workgroups are
 // adding to; it is read with agent-scope loads (past this XCD's L2).
+// Only bins below `to` (a multiple of 4) are read: keys in higher bins are
+// then not counted, so the bin found can only be lower (still a valid bound).
 template <bool kCoherent = false>
-__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, int from) {
+__device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, int from, int to = kHistBins) {
   const int lane = threadIdx.x & 63;
   const int lo = from & ~3;                           // whole uint4 groups
-  const int n4 = (kHistBins - lo) >> 2;
+  const int n4 = (min(to, kHistBins) - lo) >> 2;
   const int per = (n4 + 63) >> 6;                     // groups per lane: <= 16
   const int mine = max(0, min(per, n4 - per * lane));
   const uint4* hv = reinterpret_cast<const uint4*>(h + lo) + per * lane;
@@ -1823,6 +1825,26 @@ constexpr int kFusedTies = 2048;      // bin-tb candidates the selecting workgro
 constexpr int kMaxFusedSegs = 256;    // scoring workgroups per row
 constexpr int kMaxFusedCpw = 4;       // chunks per scoring workgroup: <= 4096 keys in LDS
 constexpr int kFusedDirect = 2 * kFT; // bin-tb lists up to this long are ranked directly
+constexpr int kBoundWindow = 256;     // histogram bins a scoring workgroup reads for its row bound
+
+// The segments holding candidates i[0..N-1] (each < soff[nseg]): for each,
+// the largest s < nseg with soff[s] <= i (soff ascending, soff[0] = 0,
+// soff[nseg] = the candidate count), by binary searches run side by side:
+// every halving step issues the N LDS reads together, without branches.
+template <int N>
+__device__ __forceinline__ void segments_of(const uint32_t* soff, int nseg, const uint32_t (&i)[N], int (&s)[N]) {
+  static_assert(kMaxFusedSegs <= 256, "eight halving steps");
+#pragma unroll
+  for (int u = 0; u < N; u++) s[u] = 0;
+#pragma unroll
+  for (int step = 128; step > 0; step >>= 1) {
+#pragma unroll
+    for (int u = 0; u < N; u++) {
+      const int t = min(s[u] + step, nseg);          // soff[nseg] > i: never taken
+      s[u] = soff[t] <= i[u] ? t : s[u];
+    }
+  }
+}
 
 // Over the 1024-bin LDS histogram h (thread t holds bins P t .. P t + P - 1,
 // P = 1024 / kT): the bin where the count from the top reaches `need`:
@@ -2008,13 +2030,15 @@ __device__ __forceinline__ void fused_select(const ScoreArgs& a, const SelectArg
 #pragma unroll 1
   for (uint32_t c0 = 0; c0 < C; c0 += kPer * kT) {
     uint64_t e[kPer];
-    int sg = 0;                                       // segment of i: soff[sg] <= i < soff[sg + 1]
+    uint32_t ci[kPer];
+    int sg[kPer];                                     // soff[sg] <= i < soff[sg + 1]
+#pragma unroll
+    for (int u = 0; u < kPer; u++) ci[u] = min(c0 + (uint32_t)(u * kT + tid), C - 1);
+    segments_of<kPer>(soff, nseg, ci, sg);
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
       const uint32_t i = c0 + (uint32_t)(u * kT + tid);
-      if (i < C)
-        while (soff[sg + 1] <= i) sg++;
-      e[u] = i < C ? __hip_atomic_load(row_pairs + (int64_t)sg * span + (i - soff[sg]), __ATOMIC_RELAXED,
+      e[u] = i < C ? __hip_atomic_load(row_pairs + (int64_t)sg[u] * span + (i - soff[sg[u]]), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT)
                    : 0ull;
     }
@@ -2133,9 +2157,12 @@ __device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, 
     if (c && i > b_loc) atomicAdd(&gh[i], c);
   }
   // 3. a higher bound from the row's histogram as it stands (the flushes of
-  //    the workgroups that are done), if it has one
+  //    the workgroups that are done), if it has one, from the kBoundWindow
+  //    bins above b_loc (32 octaves of scores: in practice every key above
+  //    it; keys beyond the window would only make the bound lower)
   if (wave == 0) {
-    const int b = running_threshold<true>(gh, (uint32_t)a.k, b_loc + 1);
+    const int from = b_loc + 1;
+    const int b = running_threshold<true>(gh, (uint32_t)a.k, from, (from & ~3) + kBoundWindow);
     if (lane == 0) bnd = max(b, b_loc);
   }
   __syncthreads();
