@@ -205,9 +205,15 @@ def cpu_baseline(wl, ref, Q, tokens):
     rows = B                          # the oracle's work unit is one (row, query): one row per thread
     sub = dict(ref)
     sub["batch"] = rows
+    paged = bool(ref.get("page_blocks"))
     for f in ("seq_len", "nope", "rope", "kv_scale", "idx_code", "idx_scale", "ring_kv",
-              "ring_gate", "ring_ikey", "ring_igate"):
-        sub[f] = np.ascontiguousarray(ref[f][:rows]).copy()      # the oracle appends in place
+              "ring_gate", "ring_ikey", "ring_igate", "page_table"):
+        if f not in ref:
+            continue
+        if paged and f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale"):
+            sub[f] = ref[f].copy()                                  # the page pool, whole
+        else:
+            sub[f] = np.ascontiguousarray(ref[f][:rows]).copy()      # the oracle appends in place
     scale = np.float32(1.0 / np.sqrt(512.0))
     t0 = time.perf_counter()
     oracle.compress_append(sub, tokens["kv"][:rows], tokens["gate"][:rows],
@@ -743,6 +749,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-ceiling microbenchmarks")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--paged", type=int, default=0, metavar="PB",
+                    help="decode workloads: keep the compressed entries in a shared pool of pages of PB "
+                         "blocks (rows map their pages in a seeded random order)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -780,6 +789,15 @@ def main():
     n_eager = 4 * NL                                     # eager pass timing the dominant kernel
     total_steps = args.warmup + args.steps + n_eager
     ref, Q = build_host_layer(wl, seed)
+    if args.paged:                        # the same entries in a page pool; pages for every append to come
+        grow_blocks = (total_steps + NL - 1) // NL // m + 2
+        mb = (ref["max_blocks"] + args.paged - 1) // args.paged * args.paged
+        if mb != ref["max_blocks"]:
+            for f in ("nope", "rope", "kv_scale", "idx_code", "idx_scale"):
+                pad = np.zeros((B, mb - ref["max_blocks"]) + ref[f].shape[2:], ref[f].dtype)
+                ref[f] = np.concatenate([ref[f], pad], axis=1) if ref[f].shape[1] else ref[f][:, :0]
+            ref["max_blocks"] = mb
+        ref = SL.paginate(ref, seed, args.paged, reserve_blocks=grow_blocks)
     # tokens: a few distinct sets, rotated
     n_tok = 8
     toks = [SL.tokens(seed, "step", B, 1, int(csa), step=s) for s in range(n_tok)]
@@ -802,8 +820,9 @@ def main():
             lay = base
         else:
             lay = lca.Layer(B, m, W, ref["ring"], csa, ref["max_blocks"], device=dev,
-                            pos_bias=ref["pos_bias"], ipos_bias=ref.get("ipos_bias"))
-            for f in lca.Layer.PLANES:
+                            pos_bias=ref["pos_bias"], ipos_bias=ref.get("ipos_bias"),
+                            page_blocks=base.page_blocks, pool_pages=base.pool_pages)
+            for f in base.planes:
                 src = getattr(base, f)
                 if src is not None:
                     getattr(lay, f).copy_(src)
@@ -930,6 +949,7 @@ def main():
             "workload": args.workload,
             "batch": B, "context": ctx, "ratio": m, "heads": H, "indexer_heads": HI, "topk": k,
             "window": W, "layers_rotated": NL, "launch": "eager" if args.eager else "hip_graph",
+            "page_blocks": args.paged or None,
             "eager_ms_per_step": round(eager_ms, 4),
             "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
             "step_algorithmic_bytes": step_bytes,

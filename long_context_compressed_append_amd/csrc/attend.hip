@@ -61,6 +61,7 @@ constexpr int kTile = 32;          // keys per tile
 constexpr int kVst = 528;          // fp16 per staged key row (512 + 16 pad)
 constexpr int kMaxChunk = 1024;    // keys per split workgroup (list entries staged in LDS)
 constexpr int kAttendTargetWGs = 256;
+static_assert(kMaxChunk % (64 * 8) == 0, "whole list entries per thread");
 
 struct AttendArgs {
   int n_q, H, m, W, R, k, splits, chunk, csa, hwaves;
@@ -148,11 +149,41 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int ke = min(n_keys, kb + a.chunk);
   if (split == a.splits - 1 && n_keys > ke && tid == 0)   // more keys than the plan holds
     atomicOr(a.status, LCA_STATUS_ATTEND_CAPACITY);
+  const bool paged = a.pm.shift >= 0;
   if (a.csa) {
-    for (int j = tid; j < a.chunk; j += kThreads) {
-      const int kk = kb + j;
-      klist[j] = kk < n_c ? a.topk[(int64_t)srow * a.k + kk] : -1;
+    // the listed blocks; on a paged layer their physical entries, looked up
+    // here all at once (-1: padding or not visible, -2: visible on an
+    // unmapped page)
+    int e[kMaxChunk / kThreads];
+#pragma unroll
+    for (int u = 0; u < kMaxChunk / kThreads; u++) {
+      const int j = tid + u * kThreads, kk = kb + j;
+      e[u] = j < a.chunk && kk < n_c ? a.topk[(int64_t)srow * a.k + kk] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < kMaxChunk / kThreads; u++) {
+      const int j = tid + u * kThreads;
+      if (j < a.chunk) {
+        int v = e[u];
+        if (paged) {
+          const int64_t pe = e[u] >= 0 && e[u] < nv ? entry_index(a.pm, brow, e[u]) : (int64_t)-1;
+          v = pe >= 0 ? (int)pe : (e[u] >= 0 && e[u] < nv ? -2 : -1);
+        }
+        klist[j] = v;
+      }
+    }
+  }
+  // HCA on a paged layer: the split's entries kb .. min(ke, nv) - 1 are
+  // consecutive, so klist holds the page-table entries of their pages
+  // (pages pg0 ..) and the staging takes each entry's page from LDS; more
+  // pages than klist holds: every entry is looked up in the table
+  const int pg0 = paged ? kb >> a.pm.shift : 0;
+  const int cend = min(ke, n_c);
+  const int npg = paged && cend > kb ? ((cend - 1) >> a.pm.shift) - pg0 + 1 : 0;
+  const bool lds_pages = !a.csa && npg <= kMaxChunk;
+  if (!a.csa && paged && lds_pages) {
+    for (int j = tid; j < npg; j += kThreads)
+      klist[j] = a.pm.table[(int64_t)brow * a.pm.pages_per_row + pg0 + j];
   }
 
   v4f O[32];
@@ -177,8 +208,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     if (kk < ke) {
       if (kk < n_c) {
         const int e = a.csa ? klist[kk - kb] : kk;
-        const int64_t ent = e >= 0 && e < nv ? entry_index(a.pm, brow, e) : -1;
-        page_ok &= !(e >= 0 && e < nv && ent < 0);   // a visible entry on an unmapped page
+        int64_t ent = -1;
+        if (a.csa && paged) {                      // klist holds physical entries
+          ent = e >= 0 ? (int64_t)e : (int64_t)-1;
+          page_ok &= e != -2;
+        } else if (e >= 0 && e < nv) {
+          ent = paged && lds_pages ? phys_entry(a.pm, klist[(e >> a.pm.shift) - pg0], e)
+                                   : entry_index(a.pm, brow, e);
+          page_ok &= ent >= 0;                     // a visible entry on an unmapped page
+        }
         if (ent >= 0) {
           if (sg < 7) {
             src = a.nope + ent * kNope + sg * 64 + sp * 32;

@@ -250,3 +250,90 @@ def test_unmapped_pages_are_reported():
             lca.hca_attend(lay, _dev(Q["q"]), float(SCALE))
         torch.cuda.synchronize()
         assert lay.status() == lca.STATUS_PAGE, call
+
+
+# ------------------------------------------------------------------ graph replay, no-allocation entry point
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_paged_graph_replay_with_append(kind):
+    """A paged layer's decode step (append, then selection and attention for
+    CSA, or attention for HCA) captured once and replayed six times against
+    an eager twin: top-k lists, outputs, lengths and the page pool agree bit
+    for bit, across a finalised block (the table maps the pages to come)."""
+    lca = _lca()
+    csa = kind == "csa"
+    B, H, HI, k, steps, PB = 3, 64, 16, 256, 6, 64
+    m, lens = (4, [20001, 6003, 12999]) if csa else (128, [128 * 90 - 3, 128 * 40 - 1, 128 * 70 - 2])
+    say("paged graph replay", kind, B, lens, steps, "PB", PB)
+    MB = (max(lens) // m + 8 + PB - 1) // PB * PB
+    base = SL.make_layer(5700, "pgr" + kind, B, m, 128, 256, int(csa), MB, lens)
+    ref = SL.paginate(base, 5700, PB, reserve_blocks=steps // m + 2)
+    tok = SL.tokens(5700, "pgr" + kind, B, 1, int(csa))
+    Q = SL.queries(5700, "pgr" + kind, B, 1, H, HI if csa else 0)
+    lg, le = lca.Layer.from_host(ref), lca.Layer.from_host(ref)
+    d = {kk: _dev(v) for kk, v in tok.items()}
+    q = _dev(Q["q"])
+    iq, iw = (_dev(Q["iq"]), _dev(Q["iw"])) if csa else (None, None)
+    bufs = {id(lay): (torch.empty((B, 1, k), dtype=torch.int32, device="cuda"),
+                      torch.empty((B, 1, H, 512), dtype=torch.float32, device="cuda")) for lay in (lg, le)}
+
+    def step(lay, plan_len=None):
+        lca.compress_append(lay, d["kv"], d["gate"], d.get("ikey"), d.get("igate"))
+        if plan_len is not None:
+            lay.len_max = plan_len
+        t, o = bufs[id(lay)]
+        if csa:
+            lca.indexer_topk(lay, iq, iw, k, out=t)
+            lca.csa_attend(lay, q, t, float(SCALE), out=o)
+        else:
+            lca.hca_attend(lay, q, float(SCALE), out=o)
+
+    final = max(lens) + steps + 2
+    before = (lg.len_min, lg.len_max)
+    lg.len_max = final
+    if csa:
+        lg.indexer_workspace(1, lca.indexer_workspace_bytes(lg, 1, HI, k))
+    lg.workspace(lca.attend_workspace_bytes(lg, 1, H, k if csa else 0), "attend")
+    lg.len_min, lg.len_max = before
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(lg, plan_len=final)
+    torch.cuda.synchronize()
+    lg.len_min, lg.len_max = before
+    for r in range(steps):
+        g.replay()
+        step(le)
+        torch.cuda.synchronize()
+        (tg, og), (te, oe) = bufs[id(lg)], bufs[id(le)]
+        assert torch.equal(lg.seq_len, le.seq_len), r
+        assert not csa or torch.equal(tg, te), r
+        assert torch.equal(og, oe), r
+    a, b = lg.download(), le.download()
+    for f in SL.ENTRY_PLANES + ("ring_kv",):
+        if f in a:
+            assert np.array_equal(a[f], b[f]), f
+    assert lg.status() == 0 and le.status() == 0
+    assert any(int(b["seq_len"][r]) // m > lens[r] // m for r in range(B))   # a block was finalised
+
+
+def test_paged_noalloc_matches_workspace_call():
+    """The no-allocation indexer entry point on a paged layer: the same
+    selection as the call with a caller workspace, twice in a row."""
+    lca = _lca()
+    say("paged noalloc")
+    B, lens, H_I, k, PB = 3, [70000, 9000, 33333], 16, 512, 128
+    MB = (max(lens) // 4 + 8 + PB - 1) // PB * PB
+    base = SL.make_layer(5800, "pna", B, 4, 128, 256, 1, MB, lens)
+    ref = SL.paginate(base, 5800, PB)
+    Q = SL.queries(5800, "pna", B, 1, 16, H_I)
+    lay = lca.Layer.from_host(ref)
+    iq, iw = _dev(Q["iq"]), _dev(Q["iw"])
+    want = lca.indexer_topk(lay, iq, iw, k)
+    for _ in range(2):
+        got = lca.indexer_topk_noalloc(lay, iq, iw, k)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
+    assert lay.status() == 0
