@@ -175,13 +175,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   }
   // HCA on a paged layer: the split's entries kb .. min(ke, nv) - 1 are
   // consecutive, so klist holds the page-table entries of their pages
-  // (pages pg0 ..) and the staging takes each entry's page from LDS; more
-  // pages than klist holds: every entry is looked up in the table
+  // (pages pg0 ..) and the staging takes each entry's page from LDS
   const int pg0 = paged ? kb >> a.pm.shift : 0;
   const int cend = min(ke, n_c);
   const int npg = paged && cend > kb ? ((cend - 1) >> a.pm.shift) - pg0 + 1 : 0;
-  const bool lds_pages = !a.csa && npg <= kMaxChunk;
-  if (!a.csa && paged && lds_pages) {
+  if (!a.csa && paged) {                       // npg <= kMaxChunk: the plan sizes the splits for it
     for (int j = tid; j < npg; j += kThreads)
       klist[j] = a.pm.table[(int64_t)brow * a.pm.pages_per_row + pg0 + j];
   }
@@ -207,14 +205,17 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     const float* scp = a.kv_scale;
     if (kk < ke) {
       if (kk < n_c) {
+        // the entry's place from registers and LDS only: a global load here
+        // would make every later data load wait for it (loads complete in
+        // order), draining the loads of the tiles in flight
         const int e = a.csa ? klist[kk - kb] : kk;
         int64_t ent = -1;
         if (a.csa && paged) {                      // klist holds physical entries
           ent = e >= 0 ? (int64_t)e : (int64_t)-1;
           page_ok &= e != -2;
         } else if (e >= 0 && e < nv) {
-          ent = paged && lds_pages ? phys_entry(a.pm, klist[(e >> a.pm.shift) - pg0], e)
-                                   : entry_index(a.pm, brow, e);
+          ent = paged ? phys_entry(a.pm, klist[(e >> a.pm.shift) - pg0], e)   // HCA: the pages in LDS
+                      : (int64_t)brow * a.max_blocks + e;
           page_ok &= ent >= 0;                     // a visible entry on an unmapped page
         }
         if (ent >= 0) {
@@ -563,6 +564,9 @@ AttendPlan plan_attend(const lca_layer* L, int n_q, int H, int k, bool csa) {
   if (s < 1) s = 1;
   int64_t per = (pl.max_keys + s - 1) / s;
   if (csa && per > kMaxChunk) per = kMaxChunk;
+  // paged HCA: a split's pages (at most per / PB + 2) fit the LDS list
+  if (!csa && L->page_blocks > 0 && per > (int64_t)(kMaxChunk - 2) * L->page_blocks)
+    per = (int64_t)(kMaxChunk - 2) * L->page_blocks;
   pl.chunk = (int)(((per + kTile - 1) / kTile) * kTile);
   pl.splits = (int)((pl.max_keys + pl.chunk - 1) / pl.chunk);
   if (pl.splits > 1) {
