@@ -200,6 +200,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // adding to; it is read with agent-scope loads (past this XCD's L2).
 // Only bins below `to` (a multiple of 4) are read: keys in higher bins are
 // then not counted, so the bin found can only be lower (still a valid bound).
+// A range of at most 256 bins (one group per lane) is read once: lane F's
+// four counts come from its registers, so the coherent case takes a single
+// round trip.
 template <bool kCoherent = false>
 __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, int from, int to = kHistBins) {
   const int lane = threadIdx.x & 63;
@@ -209,6 +212,7 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
   const int mine = max(0, min(per, n4 - per * lane));
   const uint4* hv = reinterpret_cast<const uint4*>(h + lo) + per * lane;
   uint32_t s = 0;
+  uint4 x1 = make_uint4(0u, 0u, 0u, 0u);            // this lane's group when per == 1
   if (kCoherent) {
     // 16-byte loads that read past this XCD's L2 (buffer cache policy sc1)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(h), (short)0,
@@ -216,12 +220,19 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
     for (int i = 0; i < mine; i++) {
       const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * lo + 16 * (per * lane + i), 0, 16);
       s += x.x + x.y + x.z + x.w;
+      x1 = make_uint4(x.x, x.y, x.z, x.w);
     }
   } else {
-    for (int i = 0; i < mine; i++) {
-      const uint4 x = hv[i];
-      s += x.x + x.y + x.z + x.w;
+    // every LDS read issued before the first is used
+    uint4 xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      xs[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < mine) xs[i] = hv[i];
     }
+#pragma unroll
+    for (int i = 0; i < 16; i++) s += xs[i].x + xs[i].y + xs[i].z + xs[i].w;
+    x1 = xs[0];
   }
   const uint32_t incl = wave_inclusive_scan(s);
   const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys of higher lanes' bins
@@ -231,10 +242,19 @@ __device__ __forceinline__ int running_threshold(const uint32_t* h, uint32_t k, 
   const uint32_t aF = (uint32_t)__builtin_amdgcn_readlane((int)above, F);
   const int base = lo + 4 * per * F;
   const int cnt = 4 * __builtin_amdgcn_readlane(mine, F);   // lane F's bins: base .. base + cnt - 1
-  const uint32_t c = lane < cnt ? (kCoherent ? __hip_atomic_load(h + base + cnt - 1 - lane, __ATOMIC_RELAXED,
-                                                                  __HIP_MEMORY_SCOPE_AGENT)
-                                              : h[base + cnt - 1 - lane])
-                                 : 0u;   // the lane-th from the top
+  uint32_t c;                                      // the lane-th from the top
+  if (per == 1) {                                  // cnt == 4: lane F's registers
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)x1.x, F);
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)x1.y, F);
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_readlane((int)x1.z, F);
+    const uint32_t b3 = (uint32_t)__builtin_amdgcn_readlane((int)x1.w, F);
+    c = lane == 0 ? b3 : lane == 1 ? b2 : lane == 2 ? b1 : lane == 3 ? b0 : 0u;
+  } else {
+    c = lane < cnt ? (kCoherent ? __hip_atomic_load(h + base + cnt - 1 - lane, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : h[base + cnt - 1 - lane])
+                   : 0u;
+  }
   const uint32_t ci = wave_inclusive_scan(c);
   const uint64_t q = __ballot(lane < cnt && aF + ci - c >= k);   // keys above that bin reach k
   return base + __popcll(q) - 1;
@@ -343,13 +363,16 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
     kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
     er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
   };
-  // query values and weights: all loads in flight before any is used
+  // query values and weights: all loads in flight before any is used; four
+  // consecutive values per thread (16-byte loads), so the 32 values of an MX
+  // block are 8 neighbouring lanes
   const float* qsrc = a.iq + (int64_t)srow * a.H * kIdx;
-  float qv[8];
+  constexpr int kQv = 2;                          // H_I * 64 <= 2048 values
+  float4 qv[kQv];
 #pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const int e = tid + 256 * u;
-    qv[u] = (e < a.H * kIdx && tid < 256) ? qsrc[e] : 0.0f;
+  for (int u = 0; u < kQv; u++) {
+    const int e = 4 * (tid + kT * u);
+    qv[u] = e < a.H * kIdx ? *reinterpret_cast<const float4*>(qsrc + e) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const float wq = tid < a.H ? a.iw[(int64_t)srow * a.H + tid] : 0.0f;
   // Key loads go out after the query's: the loads complete in issue order, so
@@ -373,24 +396,24 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   if (paged && wave == 0) wg_pages_check(a.pm, lane_pg, wg_b0, a.cpw * kScoreBlocksPerWG, nv, lane, a.status);
 
   for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
-  // MXFP4 quantisation of the query, one 32-lane half-wave per MX block
-  // (the first 256 threads)
+  // MXFP4 quantisation of the query: an MX block's largest magnitude over
+  // its 8 lanes, then four codes per thread (two bytes of q_code)
 #pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const int e = tid + 256 * u;
-    if (e >= a.H * kIdx || tid >= 256) break;
-    const float x = qv[u];
-    float amax = half_wave_max(fabsf(x));
-    uint32_t code = 0;
+  for (int u = 0; u < kQv; u++) {
+    const int e = 4 * (tid + kT * u);
+    if (e >= a.H * kIdx) break;                   // uniform per wavefront (H_I * 64: whole 256s)
+    const float4 x = qv[u];
+    const float amax = octet_max(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    uint32_t c4 = 0;
     int X = -127;
     if (amax > 0.0f) {
       X = floor_log2(amax) - 2;
       X = X < -127 ? -127 : (X > 127 ? 127 : X);
-      code = f32_e2m1(ldexpf(x, -X));
+      c4 = f32_e2m1(ldexpf(x.x, -X)) | (f32_e2m1(ldexpf(x.y, -X)) << 4) | (f32_e2m1(ldexpf(x.z, -X)) << 8) |
+           (f32_e2m1(ldexpf(x.w, -X)) << 12);
     }
-    uint32_t hi = lane_xor1(code);
     const int h = e >> 6, el = e & 63;
-    if ((el & 1) == 0) q_code[h][el >> 1] = (uint8_t)(code | (hi << 4));
+    *reinterpret_cast<uint16_t*>(&q_code[h][el >> 1]) = (uint16_t)c4;   // values el .. el + 3
     if ((el & 31) == 0) q_exp[h][el >> 5] = X;
   }
   if (tid < a.H) q_w[tid] = wq;
@@ -691,30 +714,41 @@ __global__ void __launch_bounds__(64 * kTileWaves) indexer_score_tile_kernel(Sco
   const uint8_t* ks = a.idx_scale + row_base * 2;
   const int lane_pg = paged ? wg_pages(a.pm, brow, b_lo, lane) : -1;
 
-  // queries: Qwg x H x 64 fp32 values, quantised one MX block per half-wave
+  // queries: Qwg x H x 64 fp32 values, four consecutive ones per thread and
+  // step (16-byte loads, all issued before the first is used), so the 32
+  // values of an MX block are 8 neighbouring lanes
+  constexpr int kQSteps = kQwg * (kQw == 8 ? 16 : 32) * kIdx / (4 * 64 * kTileWaves);
+  static_assert(kQSteps * 4 * 64 * kTileWaves == kQwg * (kQw == 8 ? 16 : 32) * kIdx, "whole steps");
   const int nqv = min(kQwg, a.n_q - q0);              // queries of this workgroup
   const float* qsrc = a.iq + ((int64_t)brow * a.n_q + q0) * a.H * kIdx;
   const int qvals = kQwg * a.H * kIdx;
+  float4 qv4[kQSteps];
+#pragma unroll
+  for (int u = 0; u < kQSteps; u++) {
+    const int e = 4 * (tid + 64 * kTileWaves * u);
+    const bool ok = e < qvals && e / (a.H * kIdx) < nqv;
+    qv4[u] = ok ? *reinterpret_cast<const float4*>(qsrc + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int i = tid; i < kQwg * kHistBins / 4; i += 64 * kTileWaves)
     reinterpret_cast<uint4*>(&lh[0][0])[i] = make_uint4(0, 0, 0, 0);
-  for (int e0 = 0; e0 < qvals; e0 += 64 * kTileWaves) {
-    const int e = e0 + tid;                           // whole MX blocks per half-wave
+#pragma unroll
+  for (int u = 0; u < kQSteps; u++) {
+    const int e = 4 * (tid + 64 * kTileWaves * u);
+    if (e >= qvals) break;                            // whole MX blocks: octets stay whole
     const int q = e / (a.H * kIdx), rem = e % (a.H * kIdx);
-    const float x = (e < qvals && q < nqv) ? qsrc[e] : 0.0f;
-    const float amax = half_wave_max(fabsf(x));
-    uint32_t code = 0;
+    const float4 x = qv4[u];
+    const float amax = octet_max(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    uint32_t c4 = 0;
     int X = -127;
     if (amax > 0.0f) {
       X = floor_log2(amax) - 2;
       X = X < -127 ? -127 : (X > 127 ? 127 : X);
-      code = f32_e2m1(ldexpf(x, -X));
+      c4 = f32_e2m1(ldexpf(x.x, -X)) | (f32_e2m1(ldexpf(x.y, -X)) << 4) | (f32_e2m1(ldexpf(x.z, -X)) << 8) |
+           (f32_e2m1(ldexpf(x.w, -X)) << 12);
     }
-    const uint32_t hi = lane_xor1(code);
     const int h = rem >> 6, el = rem & 63;
-    if (e < qvals) {
-      if ((el & 1) == 0) q_code[q][h][el >> 1] = (uint8_t)(code | (hi << 4));
-      if ((el & 31) == 0) q_exp[q][h][el >> 5] = X;
-    }
+    *reinterpret_cast<uint16_t*>(&q_code[q][h][el >> 1]) = (uint16_t)c4;   // values el .. el + 3
+    if ((el & 31) == 0) q_exp[q][h][el >> 5] = X;
   }
   if (kCand && tid < kQwg) thr_s[tid] = -1;
   for (int i = tid; i < kQwg * 32; i += 64 * kTileWaves) {

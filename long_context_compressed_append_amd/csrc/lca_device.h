@@ -122,6 +122,17 @@ __device__ __forceinline__ float half_wave_max(float v) {
   return (threadIdx.x & 32) ? hi : lo;
 }
 
+// max over the caller's aligned group of 8 lanes, in every lane of it: two
+// quad permutations (lanes 1, 0, 3, 2, then 2, 3, 0, 1) give each lane its
+// quad's maximum, the half-row mirror (lane i with lane 7 - i) joins the two
+// quads
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141;
+__device__ __forceinline__ float octet_max(float v) {
+  v = dpp_max<kDppQuadXor1, 0xf>(v);
+  v = dpp_max<kDppQuadXor2, 0xf>(v);
+  return dpp_max<kDppRowHalfMirror, 0xf>(v);
+}
+
 // min (kOp 0) or max (kOp 1) over the wave, in every lane
 template <int kOp>
 __device__ __forceinline__ int wave_minmax(int v) {
