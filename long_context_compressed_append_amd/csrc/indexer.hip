@@ -332,7 +332,7 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   __shared__ __attribute__((aligned(16))) uint8_t q_code[32][32];
   __shared__ int q_exp[32][2];
   __shared__ float q_w[32];
-  __shared__ uint32_t lhist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lhist[kHistBins];   // read as uint4
   // kFused: the workgroup's keys by block offset (later the selection bitmap)
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
   const int wg_b0 = (int)blockIdx.x * a.cpw * kScoreBlocksPerWG;   // kFused: first block of the workgroup
