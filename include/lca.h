@@ -297,6 +297,27 @@ int lca_indexer_topk_noalloc(const lca_layer *layer, const float *iq, const floa
                              int32_t H_I, int32_t k, int32_t *topk, hipStream_t stream);
 
 /*
+ * lca_decode_append_topk -- one decode step of a CSA layer up to the top-k:
+ * the compressor takes the new token and the lightning index selects among
+ * the compressed blocks (pnsm.cn "DeepSeek V4 架构深度解析" page, section
+ * 2.1: the compressor updates the compressed cache, the index keeps the
+ * top-k; vibecoco.ai "DeepSeek V4 agent architecture" page, section
+ * 混合注意力).  Exactly lca_compress_append(layer, kv, gate, ikey, igate, 1)
+ * followed by lca_indexer_topk(layer, iq, iw, 1, H_I, k, topk, ws, ...),
+ * with the same results, arguments, layouts and status bits; in one launch
+ * when the decode selection runs inside the scoring launch (H_I <= 16, the
+ * automatic choice) and the layer's blocks hold at most 8 tokens (ratio <=
+ * 8), else as those two launches.  Needs a CSA layer (has_indexer).  ws
+ * holds lca_decode_append_workspace(layer, H_I, k) bytes (the indexer's
+ * workspace for the layer one token longer, under the same rules).  Updates
+ * len_min / len_max like lca_compress_append.
+ */
+size_t lca_decode_append_workspace(const lca_layer *layer, int32_t H_I, int32_t k);
+int lca_decode_append_topk(lca_layer *layer, const uint16_t *kv, const float *gate, const float *ikey,
+                           const float *igate, const float *iq, const float *iw, int32_t H_I, int32_t k,
+                           int32_t *topk, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * lca_csa_attend -- [ARCH] 2.1 (one attention over the sliding-window KV and
  * the top-k selected compressed KV); [AGENT] hybrid-attention section (recent
  * tokens at raw precision).

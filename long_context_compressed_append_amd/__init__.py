@@ -71,6 +71,9 @@ def lib():
         L.lca_indexer_layout.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
         L.lca_indexer_topk.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_size_t, P]
         L.lca_indexer_topk_noalloc.argtypes = [LP, P, P, C.c_int32, C.c_int32, C.c_int32, P, P]
+        L.lca_decode_append_workspace.restype = C.c_size_t
+        L.lca_decode_append_workspace.argtypes = [LP, C.c_int32, C.c_int32]
+        L.lca_decode_append_topk.argtypes = [LP, P, P, P, P, P, P, C.c_int32, C.c_int32, P, P, C.c_size_t, P]
         L.lca_attend_workspace.restype = C.c_size_t
         L.lca_attend_workspace.argtypes = [LP, C.c_int32, C.c_int32, C.c_int32]
         L.lca_csa_attend.argtypes = [LP, P, C.c_int32, C.c_int32, P, C.c_int32, C.c_float, P, P,
@@ -313,6 +316,34 @@ def indexer_topk(layer: Layer, iq, iw, k, out=None):
     ws = layer.indexer_workspace(n_q, nbytes)
     _check(lib().lca_indexer_topk(C.byref(s), _ptr(iq), _ptr(iw), n_q, H_I, k, _ptr(out), _ptr(ws),
                                   nbytes, _stream()))
+    return out
+
+
+def decode_append_topk(layer: Layer, kv, gate, ikey, igate, iq, iw, k, out=None):
+    """One decode step of a CSA layer up to the top-k (lca_decode_append_topk):
+    the same as compress_append(layer, kv, gate, ikey, igate) with one token
+    per row followed by indexer_topk(layer, iq, iw, k).  kv [B][1][512]
+    bf16 bits, gate [B][1][512], ikey/igate [B][1][64], iq [B][1][H_I][64],
+    iw [B][1][H_I] -> int32 [B][1][k]."""
+    B = layer.batch
+    if kv.dtype == torch.bfloat16:
+        kv = kv.view(torch.int16)
+    _dev(kv, torch.int16, (B, 1, KV), "kv")
+    _dev(gate, torch.float32, (B, 1, KV), "gate")
+    _dev(ikey, torch.float32, (B, 1, IDX), "ikey")
+    _dev(igate, torch.float32, (B, 1, IDX), "igate")
+    H_I = iw.shape[2]
+    _dev(iq, torch.float32, (B, 1, H_I, IDX), "iq")
+    _dev(iw, torch.float32, (B, 1, H_I), "iw")
+    if out is None:
+        out = torch.empty((B, 1, k), dtype=torch.int32, device=iq.device)
+    _dev(out, torch.int32, (B, 1, k), "topk")
+    s = layer.struct()
+    nbytes = lib().lca_decode_append_workspace(C.byref(s), H_I, k)
+    ws = layer.indexer_workspace(1, nbytes)
+    _check(lib().lca_decode_append_topk(C.byref(s), _ptr(kv), _ptr(gate), _ptr(ikey), _ptr(igate), _ptr(iq),
+                                        _ptr(iw), H_I, k, _ptr(out), _ptr(ws), nbytes, _stream()))
+    layer.len_min, layer.len_max = s.len_min, s.len_max
     return out
 
 

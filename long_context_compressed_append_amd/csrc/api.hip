@@ -171,12 +171,10 @@ int lca_abi_version(void) { return LCA_ABI_VERSION; }
 
 const char* lca_last_error(void) { return g_err; }
 
-int lca_compress_append(lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
-                        const float* igate, int32_t n, hipStream_t stream) {
-  int rc = check_layer(L);
-  if (rc) return rc;
-  if (n < 0) return set_error(LCA_EINVAL, "n must be >= 0 (got %d)", n);
-  if (n == 0) return LCA_OK;
+// argument checks of an append of n >= 1 tokens per row
+static int append_validate(const lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
+                           const float* igate, int32_t n) {
+  int rc;
   if ((rc = check_ptr(kv, "kv")) || (rc = check_ptr(gate, "gate"))) return rc;
   if (L->has_indexer) {
     if ((rc = check_ptr(ikey, "ikey")) || (rc = check_ptr(igate, "igate"))) return rc;
@@ -188,6 +186,16 @@ int lca_compress_append(lca_layer* L, const uint16_t* kv, const float* gate, con
   if ((L->len_max + n) / L->ratio > L->max_blocks)
     return set_error(LCA_ECAPACITY, "max_blocks (%lld) too small for %lld tokens at ratio %d",
                      (long long)L->max_blocks, (long long)(L->len_max + n), L->ratio);
+  return LCA_OK;
+}
+
+int lca_compress_append(lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
+                        const float* igate, int32_t n, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (n < 0) return set_error(LCA_EINVAL, "n must be >= 0 (got %d)", n);
+  if (n == 0) return LCA_OK;
+  if ((rc = append_validate(L, kv, gate, ikey, igate, n))) return rc;
   rc = launch_compress(L, kv, gate, ikey, igate, n, stream);
   if (rc) return rc;
   L->len_min += n;
@@ -226,6 +234,41 @@ int lca_indexer_topk(const lca_layer* L, const float* iq, const float* iw, int32
     return set_error(LCA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   if (!aligned16(ws)) return set_error(LCA_EINVAL, "workspace is not 16-byte aligned");
   return launch_indexer(L, iq, iw, n_q, H_I, k, topk, ws, pl, stream);
+}
+
+// the layer as the selection of lca_decode_append_topk sees it: one token longer
+static lca_layer one_longer(const lca_layer* L) {
+  lca_layer a = *L;
+  a.len_min += 1;
+  a.len_max += 1;
+  return a;
+}
+
+size_t lca_decode_append_workspace(const lca_layer* L, int32_t H_I, int32_t k) {
+  if (!L || L->ratio < 1 || L->batch < 1) return 0;
+  const lca_layer after = one_longer(L);
+  return plan_indexer(&after, 1, H_I, k).total();
+}
+
+int lca_decode_append_topk(lca_layer* L, const uint16_t* kv, const float* gate, const float* ikey,
+                           const float* igate, const float* iq, const float* iw, int32_t H_I, int32_t k,
+                           int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!L->has_indexer) return set_error(LCA_EINVAL, "the layer has no indexer (an HCA layer)");
+  if ((rc = append_validate(L, kv, gate, ikey, igate, 1))) return rc;
+  const lca_layer after = one_longer(L);
+  if ((rc = indexer_validate(&after, iq, iw, 1, H_I, k, topk))) return rc;
+  IndexerPlan pl = plan_indexer(&after, 1, H_I, k);
+  const size_t need = pl.total();
+  if (!ws || ws_bytes < need)
+    return set_error(LCA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned16(ws)) return set_error(LCA_EINVAL, "workspace is not 16-byte aligned");
+  rc = launch_decode_append(L, &after, kv, gate, ikey, igate, iq, iw, H_I, k, topk, ws, pl, stream);
+  if (rc) return rc;
+  L->len_min += 1;
+  L->len_max += 1;
+  return LCA_OK;
 }
 
 size_t lca_attend_workspace(const lca_layer* L, int32_t n_q, int32_t H, int32_t k) {

@@ -47,8 +47,7 @@
 // the same launch), indexer_score_tile_kernel (many queries per row),
 // topk_select_kernel / topk_slice_kernel + topk_finish_kernel (selection over
 // full key rows), topk_cand_kernel (selection over candidate lists).
-#include "lca_device.h"
-#include "lca_internal.h"
+#include "compress_ops.h"
 
 namespace lca {
 
@@ -90,6 +89,11 @@ struct ScoreArgs {
   uint32_t* cand_count;
   uint32_t* row_done;    // fused selection: workgroups of a row done, [rows], zero between calls
   int fused_span;        // fused selection: blocks per scoring workgroup (its candidate segment)
+  // fused selection with the decode append (one token per row, blocks of at
+  // most 8 tokens): seq_len is the length before the token; the launch
+  // appends it (ring, and the block it completes) and advances seq_len
+  int append;
+  CompressArgs ca;
   uint32_t* status;      // the layer's status word (LCA_STATUS_* bits)
 };
 
@@ -301,7 +305,7 @@ __device__ void select_row(const SelectArgs& a, int srow, uint32_t* hist, uint32
 
 // The decode scoring with the selection in the same launch (kFused).
 __device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, int nv, uint32_t* lhist,
-                           uint32_t* dyn, int wg_b0);
+                           uint32_t* dyn, int wg_b0, int len, int64_t fin_bk, int64_t fin_e);
 
 // kFused: the keys stay in LDS; from its own histogram and the row's
 // histogram as it stands the workgroup derives a bin below the row's
@@ -387,7 +391,8 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   }
   // the row length through the scalar cache, once every vector load is out
   typedef const int32_t __attribute__((address_space(4)))* const_i32p;
-  const int p = *(const_i32p)(a.seq_len + brow) - a.n_q + qi;
+  const int len = *(const_i32p)(a.seq_len + brow);
+  const int p = (kFused && a.append ? len : len - a.n_q) + qi;   // append: the new token is at len
   int nv = (p + 1) / a.m;
   if (nv > cap) {                              // more blocks than the plan holds
     if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
@@ -418,6 +423,52 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   }
   if (tid < a.H) q_w[tid] = wq;
   __syncthreads();
+
+  // Append: the block this token completes (bk, entry e) is finalised by the
+  // scoring wavefront whose keys hold it, before that key is scored: its
+  // indexer key (group 8) goes to the entry planes and to LDS, and the lane
+  // that loaded the block's old bytes takes the new ones (iteration pi, lane
+  // pr).  The other groups and the ring copy run after the arrival.
+  __shared__ __attribute__((aligned(16))) uint8_t patch[48];
+  int pi = -1, pr = 0;
+  int4 pk = make_int4(0, 0, 0, 0);
+  uint32_t pe = 0;
+  int64_t fin_bk = -1, fin_e = -1;
+  if constexpr (kFused) {
+    if (a.append) {
+      const int64_t bk = (int64_t)(len / a.m);
+      if ((bk + 1) * a.m == (int64_t)len + 1) {      // this token completes block bk
+        if (bk >= a.ca.max_blocks) {
+          if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_COMPRESS_CAPACITY);
+        } else {
+          const int64_t e = entry_index(a.pm, brow, bk);
+          if (e < 0) {
+            if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_PAGE);
+          } else {
+            fin_bk = bk;
+            fin_e = e;
+          }
+        }
+      }
+      const int64_t off = fin_bk - wg_b0;
+      if (fin_bk >= 0 && off >= 0 && off < (int64_t)a.cpw * kScoreBlocksPerWG && fin_bk < cap) {
+        const int o = (int)off;
+        if (wh == (o % kScoreBlocksPerWG) / (kScoreItersPerWave * kScoreBlocksPerIter)) {
+          finalize_group(a.ca, brow, fin_bk, len, 8, fin_e, nullptr, lane, patch);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          pi = (o / kScoreBlocksPerWG) * kScoreItersPerWave +
+               (o % (kScoreItersPerWave * kScoreBlocksPerIter)) / kScoreBlocksPerIter;
+          pr = o % kScoreBlocksPerIter;
+          pk = *reinterpret_cast<const int4*>(patch + 16 * kh);
+          pe = (uint32_t)patch[32] | ((uint32_t)patch[33] << 8);
+        }
+      } else if (fin_bk >= cap && wg_b0 == 0 && wh == 0) {
+        // past the key row the scoring covers: only the entry (capacity reported above)
+        finalize_group(a.ca, brow, fin_bk, len, 8, fin_e, nullptr, lane, nullptr);
+      }
+    }
+  }
 
   // A operands for the per-half products of the exact fallback (no scales):
   // lane l feeds row l%32 with K-half l/32, row (head, half) holding only that
@@ -597,18 +648,31 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
     }
   };
 
+  // the appended block's new key replaces what the owning lane loaded
+  auto patch_keys = [&](int i0, int4 (&kk)[kDepth], uint32_t (&ee)[kDepth]) {
+    if (pi >= i0 && pi < i0 + kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; u++)
+        if (i0 + u == pi && r == pr) {
+          kk[u] = pk;
+          ee[u] = pe;
+        }
+    }
+  };
 #pragma unroll 1
   for (int i0 = 0; i0 < n_it; i0 += 2 * kDepth) {
+    if (kFused) patch_keys(i0, kA, eA);
     compute(i0, kA, eA);
 #pragma unroll
     for (int u = 0; u < kDepth; u++) load(i0 + 2 * kDepth + u, kA[u], eA[u]);
+    if (kFused) patch_keys(i0 + kDepth, kB, eB);
     compute(i0 + kDepth, kB, eB);
 #pragma unroll
     for (int u = 0; u < kDepth; u++) load(i0 + 3 * kDepth + u, kB[u], eB[u]);
   }
   __syncthreads();
   if constexpr (kFused) {
-    fused_tail(a, sel, srow, nv, lhist, dyn_lds, wg_b0);
+    fused_tail(a, sel, srow, nv, lhist, dyn_lds, wg_b0, len, fin_bk, fin_e);
   } else {
     uint32_t* gh = a.hist + (int64_t)srow * kHistBins;
     // every count is read before any atomic goes out
@@ -2170,7 +2234,7 @@ __device__ __forceinline__ void fused_select(const ScoreArgs& a, const SelectArg
 }
 
 __device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, int nv, uint32_t* lhist,
-                           uint32_t* dyn, int wg_b0) {
+                           uint32_t* dyn, int wg_b0, int len, int64_t fin_bk, int64_t fin_e) {
   constexpr int kT = kFT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int span = a.fused_span;
@@ -2233,13 +2297,37 @@ __device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, 
   // 5. arrival: this thread's stores and atomics have completed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0)
-    last = __hip_atomic_fetch_add(&a.row_done[srow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           gridDim.x - 1;
+  __shared__ uint32_t arrival;
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.row_done[srow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrival = old;
+    last = old == gridDim.x - 1;
+  }
   __syncthreads();
-  if (!last) return;
+  // 6. append: task t < 8 finalises group t of the completed block (if any),
+  //    task 8 copies the token into the ring (the indexer key, group 8, was
+  //    finalised before it was scored); the workgroup that arrived j-th
+  //    takes tasks 4 j .. 4 j + 3 (wavefront w: task 4 j + w), the row's last
+  //    one, after its selection, also every task past that (rows of fewer
+  //    than three workgroups).  Every task uses the length read at the start.
+  const int brow = srow / a.n_q;
+  auto task = [&](int t) {
+    if (t == 8)
+      ring_copy(a.ca, brow, 0, len, lane);
+    else if (fin_bk >= 0)
+      finalize_group(a.ca, brow, fin_bk, len, t, fin_e, nullptr, lane, nullptr);
+  };
+  if (!last) {
+    if (a.append && 4 * (int)arrival + wave < 9) task(4 * (int)arrival + wave);
+    return;
+  }
   if (tid == 0) __hip_atomic_store(&a.row_done[srow], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   fused_select(a, sel, srow, nv, lhist, dyn, tmp, found);
+  if (a.append) {
+    // every workgroup of the row has read the old length
+    if (tid == 0) a.ca.seq_len[brow] = len + 1;
+    for (int t = 4 * (int)arrival + wave; t < 9; t += 4) task(t);
+  }
 }
 
 IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
@@ -2340,7 +2428,7 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
 }
 
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
-                   int32_t* topk, void* ws, const IndexerPlan& pl, hipStream_t stream) {
+                   int32_t* topk, void* ws, const IndexerPlan& pl, hipStream_t stream, const CompressArgs* append) {
   const int rows = L->batch * n_q;
   char* base = static_cast<char*>(ws);
   ScoreArgs s;
@@ -2362,6 +2450,8 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
   s.cand_count = (pl.cand || pl.fused) ? reinterpret_cast<uint32_t*>(base + pl.off_cand_count) : nullptr;
   s.row_done = pl.fused ? reinterpret_cast<uint32_t*>(base + pl.off_done) : nullptr;
   s.fused_span = pl.fused_span;
+  s.append = append != nullptr;
+  s.ca = append ? *append : CompressArgs{};
   s.status = L->sync + 1;
   SelectArgs sa;
   sa.n_q = n_q;
@@ -2421,6 +2511,18 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, sa);
   }
   return t.done();
+}
+
+int launch_decode_append(const lca_layer* L, const lca_layer* after, const uint16_t* kv, const float* gate,
+                         const float* ikey, const float* igate, const float* iq, const float* iw, int H_I,
+                         int k, int32_t* topk, void* ws, const IndexerPlan& pl, hipStream_t stream) {
+  if (pl.fused && L->has_indexer && L->ratio <= 8) {
+    const CompressArgs ca = compress_args(L, kv, gate, ikey, igate, 1);
+    return launch_indexer(after, iq, iw, 1, H_I, k, topk, ws, pl, stream, &ca);
+  }
+  const int rc = launch_compress(L, kv, gate, ikey, igate, 1, stream);
+  if (rc) return rc;
+  return launch_indexer(after, iq, iw, 1, H_I, k, topk, ws, pl, stream);
 }
 
 }  // namespace lca

@@ -95,8 +95,19 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k);
 // argument checks of lca_indexer_topk (everything but the workspace)
 int indexer_validate(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
                      const int32_t* topk);
+struct CompressArgs;
+// append (fused plans only): the launch also appends one token per row with
+// these arguments (seq_len then holds the length before the token)
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
-                   int32_t* topk, void* ws, const IndexerPlan& plan, hipStream_t stream);
+                   int32_t* topk, void* ws, const IndexerPlan& plan, hipStream_t stream,
+                   const CompressArgs* append = nullptr);
+// lca_decode_append_topk: the append of one token per row to L and the
+// selection on `after` (L's host mirrors one token longer), in one launch
+// when the plan selects inside the scoring launch and blocks hold at most 8
+// tokens, else as the two launches
+int launch_decode_append(const lca_layer* L, const lca_layer* after, const uint16_t* kv, const float* gate,
+                         const float* ikey, const float* igate, const float* iq, const float* iw, int H_I,
+                         int k, int32_t* topk, void* ws, const IndexerPlan& plan, hipStream_t stream);
 
 // Attention: split-K partials (m, l) and unnormalised o per (row, split, head).
 struct AttendPlan {
