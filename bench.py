@@ -5,9 +5,10 @@ Default workload (csa_decode_128k): CSA decode at 128K context, batch 32,
 64 query heads over one shared 512-d KV entry (448 FP8 + 64 BF16), 4x
 compression (32768 entries per row), indexer 16 heads x 64 dims FP4,
 top-k 512, window 128, 16 planted needle blocks per row.  One step = one
-decode token per row through the whole CSA path: compress_append (ring
-append; a block is pooled and quantised every 4th step), indexer_topk and
-csa_attend (with its split-K combine).  Steps rotate over --layers copies of
+decode token per row through the whole CSA path: decode_append_topk (the
+ring append, the pooling and quantisation of the block every 4th token
+completes, and the top-k selection, in one launch) and csa_attend (with its
+split-K combine).  Steps rotate over --layers copies of
 the cache (distinct HBM addresses) so that every step reads its cache cold
 from HBM rather than from the 256 MB Infinity Cache, as a multi-layer decode
 does.  hca_decode_1m (HCA at 1M context, batch 16: compress_append +
@@ -339,8 +340,8 @@ def run_prefill(args):
 
     def step():
         if csa:
-            lca.compress_append(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"])
-            lca.indexer_topk(lay, iq, iw, k, out=topk)
+            lca.decode_append_topk(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"], iq, iw, k,
+                                   out=topk)
             lca.csa_attend(lay, q, topk, scale, out=out)
         else:
             lca.compress_append(lay, d_tok["kv"], d_tok["gate"])
@@ -554,10 +555,9 @@ def run_interleaved(args):
         for l in range(P):
             c, h = layers["csa"][l], layers["hca"][l]
             tc, th = tc_of(l), th_of(l)
-            lca.compress_append(c, tc["kv"], tc["gate"], tc["ikey"], tc["igate"])
-            if plan_len is not None:
-                c.len_max = plan_len
-            lca.indexer_topk(c, iqw[0], iqw[1], k, out=topk)
+            if plan_len is not None:          # the selection plans for the length after the token
+                c.len_max = plan_len - 1
+            lca.decode_append_topk(c, tc["kv"], tc["gate"], tc["ikey"], tc["igate"], iqw[0], iqw[1], k, out=topk)
             lca.csa_attend(c, qc, topk, out=out_c)
             lca.compress_append(h, th["kv"], th["gate"])
             if plan_len is not None:
@@ -844,13 +844,18 @@ def main():
     def step(i, plan_len=None):
         lay = layers[i % NL]
         tk, qq = d_tok[i % n_tok], d_q[i % n_tok]
-        lca.compress_append(lay, tk["kv"], tk["gate"], tk.get("ikey"), tk.get("igate"))
-        if plan_len is not None:          # graph capture: plan for the largest length reached
-            lay.len_max = plan_len
         if csa:
-            lca.indexer_topk(lay, qq["iq"], qq["iw"], k, out=topk_buf)
+            # the append and the selection in one launch; under graph capture
+            # the selection plans for the largest length reached
+            if plan_len is not None:
+                lay.len_max = plan_len - 1
+            lca.decode_append_topk(lay, tk["kv"], tk["gate"], tk["ikey"], tk["igate"], qq["iq"], qq["iw"], k,
+                                   out=topk_buf)
             lca.csa_attend(lay, qq["q"], topk_buf, out=out_buf)
         else:
+            lca.compress_append(lay, tk["kv"], tk["gate"])
+            if plan_len is not None:          # graph capture: plan for the largest length reached
+                lay.len_max = plan_len
             lca.hca_attend(lay, qq["q"], out=out_buf)
 
     # warm-up (eager): allocates workspaces, loads code objects
