@@ -340,8 +340,8 @@ def run_prefill(args):
 
     def step():
         if csa:
-            lca.decode_append_topk(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"], iq, iw, k,
-                                   out=topk)
+            lca.compress_append(lay, d_tok["kv"], d_tok["gate"], d_tok["ikey"], d_tok["igate"])
+            lca.indexer_topk(lay, iq, iw, k, out=topk)
             lca.csa_attend(lay, q, topk, scale, out=out)
         else:
             lca.compress_append(lay, d_tok["kv"], d_tok["gate"])
