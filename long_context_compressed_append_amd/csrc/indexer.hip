@@ -316,8 +316,10 @@ __device__ void fused_tail(const ScoreArgs& a, const SelectArgs& sel, int srow, 
 // candidates, reading them with agent-scope loads.  No device-scope fence is
 // needed: nothing it reads sits only in another XCD's L2.
 // kHQ: heads per chain slot (8, 16 or 32 >= H); kTPA key tiles share one
-// matrix-core output (4, 2 or 1).
-template <bool kFused, int kHQ>
+// matrix-core output (4, 2 or 1).  kPaged: the key planes are a page pool
+// (a separate instantiation, so that a contiguous layer's workgroups run no
+// page lookups and fetch less code).
+template <bool kFused, int kHQ, bool kPaged>
 __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectArgs sel) {
   constexpr int kT = 256;
   constexpr int kTPA = kHQ == 32 ? 1 : 32 / kHQ;
@@ -343,11 +345,12 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   const int r = lane & 31, kh = lane >> 5;
 
   // key planes: the row's entries (contiguous), or the page pool (paged)
-  const bool paged = a.pm.shift >= 0;
+  constexpr bool paged = kPaged;                 // the launch checked a.pm.shift >= 0
   const int64_t row_base = paged ? 0 : (int64_t)brow * a.max_blocks;
   const uint8_t* kc = a.idx_code + row_base * 32;
   const uint8_t* ks = a.idx_scale + row_base * 2;
-  const int lane_pg = paged ? wg_pages(a.pm, brow, wg_b0, lane) : -1;
+  int lane_pg = -1;
+  if constexpr (paged) lane_pg = wg_pages(a.pm, brow, wg_b0, lane);
   // The wave walks iterations i = 0 .. n_it-1 of 32 blocks each: iteration i
   // is group i % 8 of this wave's 256 blocks in chunk c0 + i / 8.  Keys are
   // loaded kDepth iterations ahead of their use.
@@ -363,7 +366,9 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   auto load = [&](int i, int4& kr, uint32_t& er) {
     const int blk = blk_of(i);
     int64_t b = (i < n_it && blk < cap) ? blk : 0;
-    if (paged && i < n_it && blk < cap) b = wg_entry(a.pm, lane_pg, wg_b0, blk - r, blk);
+    if constexpr (paged) {
+      if (i < n_it && blk < cap) b = wg_entry(a.pm, lane_pg, wg_b0, blk - r, blk);
+    }
     kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
     er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
   };
@@ -398,7 +403,9 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
     if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, LCA_STATUS_INDEXER_CAPACITY);
     nv = cap;
   }
-  if (paged && wave == 0) wg_pages_check(a.pm, lane_pg, wg_b0, a.cpw * kScoreBlocksPerWG, nv, lane, a.status);
+  if constexpr (paged) {
+    if (wave == 0) wg_pages_check(a.pm, lane_pg, wg_b0, a.cpw * kScoreBlocksPerWG, nv, lane, a.status);
+  }
 
   for (int i = tid; i < kHistBins; i += kT) lhist[i] = 0;
   // MXFP4 quantisation of the query: an MX block's largest magnitude over
@@ -2124,7 +2131,9 @@ __device__ __forceinline__ void fused_select(const ScoreArgs& a, const SelectArg
   const uint32_t C = ctot;
   // 2. one pass over the candidates, kPer per thread in flight: above bin tb
   //    -> bit; inside it -> the LDS list and a histogram of key bits 19..10
-  constexpr int kPer = 16;
+  //    (2048 per pass: a decode row has a few thousand candidates at most,
+  //    and a wider unrolled pass costs more instruction fetch than it saves)
+  constexpr int kPer = 8;
 #pragma unroll 1
   for (uint32_t c0 = 0; c0 < C; c0 += kPer * kT) {
     uint64_t e[kPer];
@@ -2427,6 +2436,27 @@ IndexerPlan plan_indexer(const lca_layer* L, int n_q, int H_I, int k) {
   return pl;
 }
 
+// The decode scoring launch (one query per row), contiguous or paged planes.
+template <bool kPaged>
+static void launch_score(const IndexerPlan& pl, const ScoreArgs& s, const SelectArgs& sa, int H_I, int rows,
+                         hipStream_t stream) {
+  if (pl.fused) {   // the selection runs in the same launch
+    const dim3 g(pl.fused_wgs, rows), b(kFT);
+    if (H_I <= 8)
+      hipLaunchKernelGGL((indexer_score_kernel<true, 8, kPaged>), g, b, pl.fused_lds, stream, s, sa);
+    else
+      hipLaunchKernelGGL((indexer_score_kernel<true, 16, kPaged>), g, b, pl.fused_lds, stream, s, sa);
+  } else {
+    const dim3 g(pl.chunks, rows), b(256);
+    if (H_I <= 8)
+      hipLaunchKernelGGL((indexer_score_kernel<false, 8, kPaged>), g, b, 0, stream, s, sa);
+    else if (H_I <= 16)
+      hipLaunchKernelGGL((indexer_score_kernel<false, 16, kPaged>), g, b, 0, stream, s, sa);
+    else
+      hipLaunchKernelGGL((indexer_score_kernel<false, 32, kPaged>), g, b, 0, stream, s, sa);
+  }
+}
+
 int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q, int H_I, int k,
                    int32_t* topk, void* ws, const IndexerPlan& pl, hipStream_t stream, const CompressArgs* append) {
   const int rows = L->batch * n_q;
@@ -2481,21 +2511,10 @@ int launch_indexer(const lca_layer* L, const float* iq, const float* iw, int n_q
       hipLaunchKernelGGL((indexer_score_tile_kernel<4, true>), tg, tb, 0, stream, s);
     else if (pl.tile == 4)
       hipLaunchKernelGGL((indexer_score_tile_kernel<4, false>), tg, tb, 0, stream, s);
-    else if (pl.fused) {   // the selection runs in the same launch
-      const dim3 g(pl.fused_wgs, rows), b(kFT);
-      if (H_I <= 8)
-        hipLaunchKernelGGL((indexer_score_kernel<true, 8>), g, b, pl.fused_lds, stream, s, sa);
-      else
-        hipLaunchKernelGGL((indexer_score_kernel<true, 16>), g, b, pl.fused_lds, stream, s, sa);
-    } else {
-      const dim3 g(pl.chunks, rows), b(256);
-      if (H_I <= 8)
-        hipLaunchKernelGGL((indexer_score_kernel<false, 8>), g, b, 0, stream, s, sa);
-      else if (H_I <= 16)
-        hipLaunchKernelGGL((indexer_score_kernel<false, 16>), g, b, 0, stream, s, sa);
-      else
-        hipLaunchKernelGGL((indexer_score_kernel<false, 32>), g, b, 0, stream, s, sa);
-    }
+    else if (s.pm.shift >= 0)
+      launch_score<true>(pl, s, sa, H_I, rows, stream);
+    else
+      launch_score<false>(pl, s, sa, H_I, rows, stream);
     int rc = t.done();
     if (rc || pl.fused) return rc;
   }
