@@ -304,10 +304,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int voff = (4 * g + (Lq >> 2)) * kVst + 4 * (Lq & 3);
   const int koff = Lq * kVst + kq;
 
-  // Staging wavefronts: tile 0 into buffer 0 before the loop; during tile t
-  // they store tile t + 1 (loaded a tile earlier) into the other buffer and
-  // load tile t + 2, groups sw and sw + 4.  Every wavefront passes the same
-  // barrier once per tile.
+  // Staging wavefronts: while the compute wavefronts work on tile t they
+  // store tile t + 1 (loaded a tile earlier) into the other buffer and load
+  // tile t + 2, groups sw and sw + 4.  Every wavefront passes the same
+  // barrier before the first tile and once per tile.
   // (Two separate loops, so that the staging registers and the compute
   // registers are never live at once.)
   if (!computes) {
@@ -315,25 +315,23 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     if (kb < ke) {
       stage_load(kb, sw, stA);
       stage_load(kb, sw + 4, stB);
-      stage_store(stA, sw, 0);
-      stage_store(stB, sw + 4, 0);
-      if (kb + kTile < ke) {
-        stage_load(kb + kTile, sw, stA);
-        stage_load(kb + kTile, sw + 4, stB);
-      }
     }
-    __syncthreads();
-    int cur = 0;
-    for (int t0 = kb; t0 < ke; t0 += kTile, cur ^= 1) {
-      if (t0 + kTile < ke) {
-        stage_store(stA, sw, cur ^ 1);
-        stage_store(stB, sw + 4, cur ^ 1);
-        if (t0 + 2 * kTile < ke) {
-          stage_load(t0 + 2 * kTile, sw, stA);
-          stage_load(t0 + 2 * kTile, sw + 4, stB);
+    // Pass j stores tile j (loaded one pass earlier) into buffer j % 2, loads
+    // tile j + 1 and meets the compute wavefronts' barrier: the one before
+    // their first tile (j = 0), then the one after tile j - 1.  One copy of
+    // the staging code serves every tile (a launch fetches its code cold).
+    int buf = 0;
+    for (int t0 = kb;; t0 += kTile, buf ^= 1) {
+      if (t0 < ke) {
+        stage_store(stA, sw, buf);
+        stage_store(stB, sw + 4, buf);
+        if (t0 + kTile < ke) {
+          stage_load(t0 + kTile, sw, stA);
+          stage_load(t0 + kTile, sw + 4, stB);
         }
       }
-      __syncthreads();                     // tile t + 1 staged, tile t consumed
+      __syncthreads();                     // tile j staged, tile j - 1 consumed
+      if (t0 >= ke) break;
     }
     if (__any(!range_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_FP16_RANGE);
     if (__any(!page_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_PAGE);
