@@ -1935,13 +1935,14 @@ constexpr int kBoundWindow = 256;     // histogram bins a scoring workgroup read
 // The segments holding candidates i[0..N-1] (each < soff[nseg]): for each,
 // the largest s < nseg with soff[s] <= i (soff ascending, soff[0] = 0,
 // soff[nseg] = the candidate count), by binary searches run side by side:
-// every halving step issues the N LDS reads together, without branches.
+// every halving step issues the N LDS reads together, without branches.  The
+// steps depend on one another, so they stay a loop (less code to fetch).
 template <int N>
 __device__ __forceinline__ void segments_of(const uint32_t* soff, int nseg, const uint32_t (&i)[N], int (&s)[N]) {
   static_assert(kMaxFusedSegs <= 256, "eight halving steps");
 #pragma unroll
   for (int u = 0; u < N; u++) s[u] = 0;
-#pragma unroll
+#pragma unroll 1
   for (int step = 128; step > 0; step >>= 1) {
 #pragma unroll
     for (int u = 0; u < N; u++) {
