@@ -362,15 +362,19 @@ __global__ void __launch_bounds__(256) indexer_score_kernel(ScoreArgs a, SelectA
   };
   // Loads are unconditional (a block past the capacity, or on an unmapped
   // page, reads entry 0) so that no load waits on another; compute() masks
-  // what they return.
+  // what they return.  Each key is read once per launch: non-temporal loads
+  // keep the stream from evicting the cache lines that are reused (the
+  // kernel's code, the query, the histograms).
+  typedef int nt_v4i __attribute__((ext_vector_type(4)));
   auto load = [&](int i, int4& kr, uint32_t& er) {
     const int blk = blk_of(i);
     int64_t b = (i < n_it && blk < cap) ? blk : 0;
     if constexpr (paged) {
       if (i < n_it && blk < cap) b = wg_entry(a.pm, lane_pg, wg_b0, blk - r, blk);
     }
-    kr = *reinterpret_cast<const int4*>(kc + b * 32 + 16 * kh);
-    er = *reinterpret_cast<const uint16_t*>(ks + b * 2);
+    const nt_v4i v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4i*>(kc + b * 32 + 16 * kh));
+    kr = make_int4(v.x, v.y, v.z, v.w);
+    er = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(ks + b * 2));
   };
   // query values and weights: all loads in flight before any is used; four
   // consecutive values per thread (16-byte loads), so the 32 values of an MX
