@@ -93,6 +93,10 @@ struct StageRegs {
   int kind;         // 0 padding, 1 nope group, 2 rope group of an entry, 3 window group
 };
 
+// kCsa: the key list is the top-k list (else every visible entry); kPaged:
+// the entry planes are a page pool.  Separate instantiations, so that each
+// launch fetches only the code of its own case.
+template <bool kCsa, bool kPaged>
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // two tile buffers: the compute wavefronts read tile t from buffer t % 2
   // while the staging wavefronts convert tile t + 1 into the other
@@ -143,14 +147,14 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int w0 = p - nw + 1;
   // key list: CSA = the k listed blocks (entries that are -1 or not yet
   // visible are masked), HCA = the visible blocks; then the window tokens
-  const int n_c = a.csa ? a.k : nv;
+  const int n_c = kCsa ? a.k : nv;
   const int n_keys = n_c + nw;
   const int kb = split * a.chunk;
   const int ke = min(n_keys, kb + a.chunk);
   if (split == a.splits - 1 && n_keys > ke && tid == 0)   // more keys than the plan holds
     atomicOr(a.status, LCA_STATUS_ATTEND_CAPACITY);
-  const bool paged = a.pm.shift >= 0;
-  if (a.csa) {
+  constexpr bool paged = kPaged;               // the launch checked a.pm.shift >= 0
+  if (kCsa) {
     // the listed blocks; on a paged layer their physical entries, looked up
     // here all at once (-1: padding or not visible, -2: visible on an
     // unmapped page)
@@ -179,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   const int pg0 = paged ? kb >> a.pm.shift : 0;
   const int cend = min(ke, n_c);
   const int npg = paged && cend > kb ? ((cend - 1) >> a.pm.shift) - pg0 + 1 : 0;
-  if (!a.csa && paged) {                       // npg <= kMaxChunk: the plan sizes the splits for it
+  if (!kCsa && paged) {                       // npg <= kMaxChunk: the plan sizes the splits for it
     for (int j = tid; j < npg; j += kThreads)
       klist[j] = a.pm.table[(int64_t)brow * a.pm.pages_per_row + pg0 + j];
   }
@@ -208,9 +212,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
         // the entry's place from registers and LDS only: a global load here
         // would make every later data load wait for it (loads complete in
         // order), draining the loads of the tiles in flight
-        const int e = a.csa ? klist[kk - kb] : kk;
+        const int e = kCsa ? klist[kk - kb] : kk;
         int64_t ent = -1;
-        if (a.csa && paged) {                      // klist holds physical entries
+        if (kCsa && paged) {                      // klist holds physical entries
           ent = e >= 0 ? (int64_t)e : (int64_t)-1;
           page_ok &= e != -2;
         } else if (e >= 0 && e < nv) {
@@ -607,7 +611,16 @@ int launch_attend(const lca_layer* L, const uint16_t* q, int n_q, int H, const i
   const int rows = L->batch * n_q;
   {
     TimedLaunch t(kKernelAttend, stream);
-    hipLaunchKernelGGL(attend_kernel, dim3(pl.splits, rows, pl.head_groups), dim3(kThreads), 0, stream, a);
+    const dim3 g(pl.splits, rows, pl.head_groups), b(kThreads);
+    const bool paged = a.pm.shift >= 0;
+    if (a.csa && paged)
+      hipLaunchKernelGGL((attend_kernel<true, true>), g, b, 0, stream, a);
+    else if (a.csa)
+      hipLaunchKernelGGL((attend_kernel<true, false>), g, b, 0, stream, a);
+    else if (paged)
+      hipLaunchKernelGGL((attend_kernel<false, true>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attend_kernel<false, false>), g, b, 0, stream, a);
     int rc = t.done();
     if (rc) return rc;
   }
