@@ -81,6 +81,12 @@ struct AttendArgs {
   uint32_t* status;      // the layer's status word (LCA_STATUS_* bits)
 };
 
+// buffer resource word 3: raw 32-bit data (gfx9 layout); an access at or
+// past the range reads 0 (loads) or is dropped
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kDropOffset = 0x80000000u;
+typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
+
 constexpr int kComputeWaves = 4;   // 4 head wavefronts of 16 heads, all channels
 constexpr int kStageWaves = 4;     // wavefronts that load and convert the next tile
 constexpr int kThreads = 64 * (kComputeWaves + kStageWaves);
@@ -123,21 +129,37 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // outside [2^-14, 2^8)
   bool range_ok = true;
   bool page_ok = true;    // false: a visible entry lay on an unmapped page (staged as masked)
-  v8h qf[16];  // q of this lane's head (fp16 image of the bf16 input), channels 32 ks + 8 g .. +7
+  const int kb = split * a.chunk;
+  // Loads go out in the order their data is needed (loads complete in
+  // order): the CSA list (for the staging of tile 0), then the query (for
+  // the first product); the query is converted only after the list is in
+  // LDS, so the staging of tile 0 does not wait for it.
+  // Buffer loads, so that no branch separates the loads from their use (a
+  // masked lane's offset lies past the range and reads 0) and each wait
+  // covers only the loads issued before the ones it needs.
+  int e[kMaxChunk / kThreads];
+  if (kCsa) {
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.topk + (int64_t)srow * a.k), (short)0, a.k * 4, kRsrcWord3);
+#pragma unroll
+    for (int u = 0; u < kMaxChunk / kThreads; u++) {
+      const int j = tid + u * kThreads, kk = kb + j;
+      const bool ok = j < a.chunk && kk < a.k;
+      const int v = __builtin_amdgcn_raw_buffer_load_b32(lrs, ok ? 4 * kk : (int)kDropOffset, 0, 0);
+      e[u] = ok ? v : -1;
+    }
+  }
+  uint4 qraw[16];  // q of this lane's head (bf16), channels 32 ks + 8 g .. +7
   {
-    const uint16_t* qrow = a.q + ((int64_t)srow * a.H + hq) * kKv;
-    uint32_t qmx = 0;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.q + (int64_t)srow * a.H * kKv), (short)0, a.H * kKv * 2, kRsrcWord3);
+    const bool ok = active && hq < a.H;
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (active && hq < a.H) v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + kq);
-      qf[ks] = bf16x8_to_f16(v);
-      qmx = bf16x8_absmax(v, qmx);
+      const u32x4a v = __builtin_amdgcn_raw_buffer_load_b128(
+          qrs, ok ? (hq * kKv + ks * 32 + kq) * 2 : (int)kDropOffset, 0, 0);
+      qraw[ks] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    // over the head's four lanes l, l ^ 16, l ^ 32, l ^ 48
-    qmx = max(qmx, __float_as_uint(swap_rows(__uint_as_float(qmx))));
-    qmx = max(qmx, __float_as_uint(swap_halves(__uint_as_float(qmx))));
-    range_ok = qmx == 0 || (qmx >= kBf16MinNormalF16 && qmx < kBf16F16Overflow);
   }
 
   const int p = a.seq_len[brow] - a.n_q + qi;
@@ -149,7 +171,6 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
   // visible are masked), HCA = the visible blocks; then the window tokens
   const int n_c = kCsa ? a.k : nv;
   const int n_keys = n_c + nw;
-  const int kb = split * a.chunk;
   const int ke = min(n_keys, kb + a.chunk);
   if (split == a.splits - 1 && n_keys > ke && tid == 0)   // more keys than the plan holds
     atomicOr(a.status, LCA_STATUS_ATTEND_CAPACITY);
@@ -158,12 +179,6 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     // the listed blocks; on a paged layer their physical entries, looked up
     // here all at once (-1: padding or not visible, -2: visible on an
     // unmapped page)
-    int e[kMaxChunk / kThreads];
-#pragma unroll
-    for (int u = 0; u < kMaxChunk / kThreads; u++) {
-      const int j = tid + u * kThreads, kk = kb + j;
-      e[u] = j < a.chunk && kk < n_c ? a.topk[(int64_t)srow * a.k + kk] : -1;
-    }
 #pragma unroll
     for (int u = 0; u < kMaxChunk / kThreads; u++) {
       const int j = tid + u * kThreads;
@@ -340,6 +355,20 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     if (__any(!range_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_FP16_RANGE);
     if (__any(!page_ok) && lane == 0) atomicOr(a.status, LCA_STATUS_PAGE);
     return;
+  }
+  // the query's fp16 image, and its range over the head's four lanes l,
+  // l ^ 16, l ^ 32, l ^ 48
+  v8h qf[16];
+  {
+    uint32_t qmx = 0;
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++) {
+      qf[ks] = bf16x8_to_f16(qraw[ks]);
+      qmx = bf16x8_absmax(qraw[ks], qmx);
+    }
+    qmx = max(qmx, __float_as_uint(swap_rows(__uint_as_float(qmx))));
+    qmx = max(qmx, __float_as_uint(swap_halves(__uint_as_float(qmx))));
+    range_ok = qmx == 0 || (qmx >= kBf16MinNormalF16 && qmx < kBf16F16Overflow);
   }
   __syncthreads();                         // tile 0 staged
   int cur = 0;
