@@ -379,13 +379,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
 
     // S^T = K Q^T over the 512 channels, 32 keys x 16 heads, per 64-dim
     // group scaled in fp32
+    // (groups outer, the two key tiles inner: two independent product
+    // chains side by side)
     v4f S[2];
+    S[0] = S[1] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-      S[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-      const _Float16* krow = Kc + nt * 16 * kVst;
+    for (int gl = 0; gl < 8; gl++) {
 #pragma unroll
-      for (int gl = 0; gl < 8; gl++) {
+      for (int nt = 0; nt < 2; nt++) {
+        const _Float16* krow = Kc + nt * 16 * kVst;
         v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; s2++) {
@@ -435,10 +437,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
     // O^T += V^T P^T over the 32 channel tiles.  The tile holds code values,
     // so each 64-dim group's FP8 scale goes into P: B operand of group gl =
     // fp16(p_j * scale of key j's group), for the group's four channel tiles.
-    // Software-pipelined by hand: the transpose reads of tile c + 1 and the
+    // Software-pipelined by hand: the transpose reads of tile c + 2 and the
     // scales of the next group go out before the product of tile c, so each
-    // product waits only for reads issued a step earlier (LDS reads complete
-    // in order); scheduling barriers keep that order.
+    // product waits only for reads issued two steps earlier (LDS reads
+    // complete in order); scheduling barriers keep that order.
     typedef __attribute__((address_space(3))) v4s lds_v4s;
     auto tr_pair = [&](int c, v4s& lo, v4s& hi) {
       lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow0 + 16 * c));
@@ -449,10 +451,12 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       s0 = *reinterpret_cast<const v4f*>(sg0);
       s1 = *reinterpret_cast<const v4f*>(sg0 + 16);
     };
-    v4s lo_c, hi_c;
+    constexpr int kTrDepth = 2;        // channel tiles of transpose reads in flight
+    v4s lo_r[kTrDepth], hi_r[kTrDepth];
     v4f s0, s1;
     scales(0, s0, s1);
-    tr_pair(0, lo_c, hi_c);
+#pragma unroll
+    for (int d = 0; d < kTrDepth; d++) tr_pair(d, lo_r[d], hi_r[d]);
     v8h pb;
 #pragma unroll
     for (int c = 0; c < 32; c++) {
@@ -465,15 +469,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttendArgs a) {
       }
       if ((c & 3) == 2 && c + 2 < 32) scales((c + 2) >> 2, s0, s1);
       v4s lo_n, hi_n;
-      if (c + 1 < 32) tr_pair(c + 1, lo_n, hi_n);
+      if (c + kTrDepth < 32) tr_pair(c + kTrDepth, lo_n, hi_n);
       __builtin_amdgcn_sched_barrier(0);
-      const v4h lo_h = __builtin_bit_cast(v4h, lo_c), hi_h = __builtin_bit_cast(v4h, hi_c);
+      const v4h lo_h = __builtin_bit_cast(v4h, lo_r[c % kTrDepth]), hi_h = __builtin_bit_cast(v4h, hi_r[c % kTrDepth]);
       const v8h va = {lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
       O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[c], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (c + 1 < 32) {
-        lo_c = lo_n;
-        hi_c = hi_n;
+      if (c + kTrDepth < 32) {
+        lo_r[c % kTrDepth] = lo_n;
+        hi_r[c % kTrDepth] = hi_n;
       }
     }
     __syncthreads();                       // tile t + 1 staged, tile t consumed
